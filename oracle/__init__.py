@@ -1,0 +1,29 @@
+"""fp64 CPU oracle of Skiparse attention -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The product library never does, and
+the oracle imports nothing from the product package.
+"""
+
+from .skiparse_oracle import (  # noqa: F401
+    GROUP,
+    ROPE_BASE,
+    SINGLE,
+    attention,
+    group_skip_rearrange,
+    group_skip_reverse,
+    rearrange,
+    reverse,
+    reverse_rows,
+    rope_3d,
+    rope_3d_at,
+    rope_axis_sizes,
+    rope_rearrange,
+    scope_table,
+    single_skip_rearrange,
+    single_skip_reverse,
+    skiparse_attention,
+    skiparse_attention_rows,
+    skiparse_flops,
+    token_positions,
+)

@@ -1,0 +1,310 @@
+"""Plain fp64 CPU oracle for Skiparse attention.
+
+TEST INFRASTRUCTURE ONLY.  This module is imported by ``tests/``, by
+``__graft_entry__.smoke()`` and by the ``cpu_baseline`` leg of ``bench.py``;
+nothing on the product path may import or call it.  It shares no code with
+the HIP library (no headers, tables, helpers or constants): it is written
+directly from the pages so that a reader can check it by eye.
+
+What it computes, and where each step comes from
+-----------------------------------------------
+Open-Sora Plan documentation, section "Skiparse Attention":
+
+* The attention sequence of a Full-3D-attention block is split into ``k``
+  scopes; attention runs inside each scope only.  Only the attention part of
+  the transformer block changes.
+* "Single Skip Mode": token ``n`` joins scope ``n mod k``; each scope holds
+  every k-th token.  The page's code is the einops pattern
+  ``'b (g k) d -> (k b) g d'`` and its inverse ``'(k b) g d -> b (g k) d'``.
+* "Group Skip Mode": adjacent tokens are grouped in runs of ``k``; group
+  ``j`` joins scope ``j mod k``.  The page's code is
+  ``'b (n m k) d -> (m b) (n k) d'`` with ``m = k = sparse_k`` and its inverse
+  ``'(m b) (n k) d -> b (n m k) d'``.
+* Implementation note: RoPE is applied to q and k *before* the rearrange,
+  because the rearrange loses the original positions.
+* The forward snippet runs ``F.scaled_dot_product_attention(q, k, v)`` on the
+  rearranged tensors: non-causal softmax attention, no mask, no dropout.
+
+``add_rope`` is used but never defined on the pages (the vidax page notes
+that 3D-RoPE conventions differ per model family).  The reading taken here:
+base 10000; head_dim split over the t/h/w axes in the ratio 2:3:3
+(16/24/24 at d=64, 32/48/48 at d=128), in that order; inside each axis chunk
+the pairs are rotate-half pairs (j, j + d_a/2) with angle
+pos_a * base**(-2j/d_a); integer positions from 0.
+
+Multi-head reading: the rearrange acts on the token axis of (B, N, C) with
+C = heads*head_dim, so it is the same for every head; attention is per head
+with scale 1/sqrt(head_dim).
+
+Token flattening: n = (t*H + h)*W + w (Wan 2.1 report, section 4.2.1
+"Video Diffusion Transformer": the patchified latent is flattened into a
+(B, L, D) sequence).
+
+Every pin of this module lives in ``tests/test_oracle_pins.py``.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+ROPE_BASE = 10000.0
+
+
+# ---------------------------------------------------------------------------
+# Positions
+# ---------------------------------------------------------------------------
+
+def token_positions(T: int, H: int, W: int):
+    """(t, h, w) of every token n = (t*H + h)*W + w, as int64 arrays of length T*H*W.
+
+    Wan 2.1 report, section 4.2.1: the (T, H, W) latent grid is flattened
+    into one token sequence, frame-major.
+    """
+    n = np.arange(T * H * W, dtype=np.int64)
+    t = n // (H * W)
+    h = (n // W) % H
+    w = n % W
+    return t, h, w
+
+
+# ---------------------------------------------------------------------------
+# 3D RoPE
+# ---------------------------------------------------------------------------
+
+def rope_axis_sizes(head_dim: int):
+    """Chunk sizes (d_t, d_h, d_w) of head_dim for the t, h, w axes (ratio 2:3:3)."""
+    if head_dim % 16 != 0:
+        raise ValueError("3D RoPE split 2:3:3 into even chunks needs head_dim % 16 == 0")
+    return head_dim // 4, 3 * head_dim // 8, 3 * head_dim // 8
+
+
+def rope_3d_at(x, t, h, w, base: float = ROPE_BASE):
+    """Rotate the last axis of ``x`` (..., ntok, heads, d) by 3D RoPE.
+
+    ``t, h, w`` give the grid position of each of the ``ntok`` tokens.
+    For axis a with chunk offset o, size d_a and position pos, and for
+    j in [0, d_a/2):
+        theta = pos * base**(-2j/d_a)
+        x1 = x[o+j], x2 = x[o+j+d_a/2]
+        out[o+j]        = x1*cos(theta) - x2*sin(theta)
+        out[o+j+d_a/2]  = x2*cos(theta) + x1*sin(theta)
+    Computed in float64.  (Open-Sora Plan docs, "Skiparse Attention",
+    implementation note: RoPE goes on q and k in the original token order.)
+    """
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    sizes = rope_axis_sizes(d)
+    out = x.copy()
+    offset = 0
+    for pos, d_a in zip((t, h, w), sizes):
+        half = d_a // 2
+        j = np.arange(half, dtype=np.float64)
+        freq = base ** (-2.0 * j / d_a)                      # (half,)
+        theta = np.asarray(pos, dtype=np.float64)[:, None] * freq[None, :]   # (ntok, half)
+        cos = np.cos(theta)[:, None, :]                      # broadcast over heads
+        sin = np.sin(theta)[:, None, :]
+        x1 = x[..., offset:offset + half]
+        x2 = x[..., offset + half:offset + d_a]
+        out[..., offset:offset + half] = x1 * cos - x2 * sin
+        out[..., offset + half:offset + d_a] = x2 * cos + x1 * sin
+        offset += d_a
+    return out
+
+
+def rope_3d(x, T: int, H: int, W: int, base: float = ROPE_BASE):
+    """3D RoPE of a full (B, N, heads, d) tensor laid out on the T x H x W grid."""
+    t, h, w = token_positions(T, H, W)
+    return rope_3d_at(x, t, h, w, base)
+
+
+# ---------------------------------------------------------------------------
+# Skiparse rearrange / reverse (the pages' einops patterns, written out)
+# ---------------------------------------------------------------------------
+
+SINGLE = 0
+GROUP = 1
+
+
+def single_skip_rearrange(x, k: int):
+    """(B, N, C) -> (k*B, N/k, C): pattern 'b (g k) d -> (k b) g d'.
+
+    Split the token axis as (g, k) with k innermost, then move k in front of b.
+    """
+    B, N, C = x.shape
+    if N % k:
+        raise ValueError("single skip needs N % k == 0")
+    g = N // k
+    return x.reshape(B, g, k, C).transpose(2, 0, 1, 3).reshape(k * B, g, C)
+
+
+def single_skip_reverse(x, k: int):
+    """(k*B, N/k, C) -> (B, N, C): pattern '(k b) g d -> b (g k) d'."""
+    kB, g, C = x.shape
+    B = kB // k
+    return x.reshape(k, B, g, C).transpose(1, 2, 0, 3).reshape(B, g * k, C)
+
+
+def group_skip_rearrange(x, k: int):
+    """(B, N, C) -> (k*B, N/k, C): pattern 'b (n m k) d -> (m b) (n k) d', m = k.
+
+    Split the token axis as (n, m, k) with k innermost (position inside a
+    group of k adjacent tokens) and m the group index modulo k; m becomes
+    the scope and moves in front of b; (n, k) stays as the in-scope order.
+    """
+    B, N, C = x.shape
+    if N % (k * k):
+        raise ValueError("group skip needs N % k**2 == 0")
+    n = N // (k * k)
+    return x.reshape(B, n, k, k, C).transpose(2, 0, 1, 3, 4).reshape(k * B, n * k, C)
+
+
+def group_skip_reverse(x, k: int):
+    """(k*B, N/k, C) -> (B, N, C): pattern '(m b) (n k) d -> b (n m k) d', m = k."""
+    kB, L, C = x.shape
+    B = kB // k
+    n = L // k
+    return x.reshape(k, B, n, k, C).transpose(1, 2, 0, 3, 4).reshape(B, n * k * k, C)
+
+
+def rearrange(x, k: int, mode: int):
+    """Skiparse rearrange of (B, N, C) in the given mode (SINGLE or GROUP)."""
+    if mode == SINGLE:
+        return single_skip_rearrange(x, k)
+    if mode == GROUP:
+        return group_skip_rearrange(x, k)
+    raise ValueError("mode must be SINGLE (0) or GROUP (1)")
+
+
+def reverse(x, k: int, mode: int):
+    """Inverse of :func:`rearrange` for the same mode."""
+    if mode == SINGLE:
+        return single_skip_reverse(x, k)
+    if mode == GROUP:
+        return group_skip_reverse(x, k)
+    raise ValueError("mode must be SINGLE (0) or GROUP (1)")
+
+
+def scope_table(N: int, k: int, mode: int):
+    """int64 (k, N/k): entry [s, p] is the token index placed at position p of scope s.
+
+    Obtained by applying :func:`rearrange` to the token indices themselves,
+    so it is the same permutation the data goes through.
+    """
+    idx = np.arange(N, dtype=np.int64).reshape(1, N, 1)
+    return rearrange(idx, k, mode)[:, :, 0]
+
+
+# ---------------------------------------------------------------------------
+# Attention inside a scope
+# ---------------------------------------------------------------------------
+
+def attention(q, k, v):
+    """softmax(q k^T / sqrt(d)) v over the last two axes, one (L, d) problem per leading index.
+
+    ``q``: (..., Lq, d); ``k``, ``v``: (..., Lk, d).  float64, non-causal,
+    no mask, no dropout (the defaults of the scaled-dot-product attention
+    call on the Open-Sora Plan page).  The row maximum is subtracted before
+    the exponential.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    d = q.shape[-1]
+    s = np.matmul(q, np.swapaxes(k, -1, -2)) / math.sqrt(d)
+    s = s - s.max(axis=-1, keepdims=True)
+    p = np.exp(s)
+    p = p / p.sum(axis=-1, keepdims=True)
+    return np.matmul(p, v)
+
+
+# ---------------------------------------------------------------------------
+# The full Skiparse forward
+# ---------------------------------------------------------------------------
+
+def rope_rearrange(x, T, H, W, sparse_k, mode, apply_rope=True, base=ROPE_BASE):
+    """(B, N, heads, d) -> (k*B, N/k, heads, d): optional 3D RoPE, then the Skiparse rearrange.
+
+    Row s*B + b of the result holds scope s of batch b (the '(k b)' / '(m b)'
+    batch order of the page's patterns).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    B, N, heads, d = x.shape
+    if apply_rope:
+        x = rope_3d(x, T, H, W, base)
+    r = rearrange(x.reshape(B, N, heads * d), sparse_k, mode)
+    return r.reshape(r.shape[0], r.shape[1], heads, d)
+
+
+def reverse_rows(x, sparse_k, mode):
+    """(k*B, N/k, heads, d) -> (B, N, heads, d): the Skiparse reverse."""
+    kB, L, heads, d = x.shape
+    r = reverse(np.asarray(x).reshape(kB, L, heads * d), sparse_k, mode)
+    return r.reshape(r.shape[0], r.shape[1], heads, d)
+
+
+def skiparse_attention(q, k, v, T, H, W, sparse_k, mode, base=ROPE_BASE):
+    """Skiparse attention forward, float64.  q, k, v: (B, N, heads, d) with N = T*H*W.
+
+    Steps in the page's order: RoPE on q and k; rearrange q, k, v into
+    (k*B, N/k, ...); softmax attention per rearranged batch row and head;
+    reverse back to (B, N, heads, d).  With sparse_k == 1 this is dense
+    full-3D attention.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    B, N, heads, d = q.shape
+    if N != T * H * W:
+        raise ValueError("N must equal T*H*W")
+    rq = rope_rearrange(q, T, H, W, sparse_k, mode, True, base)
+    rk = rope_rearrange(k, T, H, W, sparse_k, mode, True, base)
+    rv = rope_rearrange(v, T, H, W, sparse_k, mode, False, base)
+    # (kB, L, heads, d) -> (kB, heads, L, d): one attention problem per (row, head)
+    o = attention(rq.transpose(0, 2, 1, 3), rk.transpose(0, 2, 1, 3), rv.transpose(0, 2, 1, 3))
+    return reverse_rows(o.transpose(0, 2, 1, 3), sparse_k, mode)
+
+
+def skiparse_attention_rows(q, k, v, T, H, W, sparse_k, mode, batch_idx, token_idx,
+                            base=ROPE_BASE):
+    """Skiparse attention output of selected (batch, token) rows only, float64.
+
+    Returns (len(token_idx), heads, d).  For each requested token n of batch
+    b: its scope is the row of :func:`scope_table` that contains n; its
+    query is RoPE(q[b, n]) at n's own grid position; its keys and values are
+    RoPE(k[b, m]) and v[b, m] for every member m of that scope; the output is
+    softmax attention over them.  This is the same definition as
+    :func:`skiparse_attention`, evaluated row by row so that very large
+    inputs can be checked on a sample.
+    """
+    batch_idx = np.asarray(batch_idx, dtype=np.int64)
+    token_idx = np.asarray(token_idx, dtype=np.int64)
+    B, N, heads, d = q.shape
+    table = scope_table(N, sparse_k, mode)
+    scope_of = np.empty(N, dtype=np.int64)
+    for s in range(sparse_k):
+        scope_of[table[s]] = s
+    t_all, h_all, w_all = token_positions(T, H, W)
+    out = np.empty((len(token_idx), heads, d), dtype=np.float64)
+    keys = sorted(set(zip(batch_idx.tolist(), scope_of[token_idx].tolist())))
+    for b, s in keys:
+        members = table[s]
+        sel = np.nonzero((batch_idx == b) & (scope_of[token_idx] == s))[0]
+        toks = token_idx[sel]
+        kk = rope_3d_at(np.asarray(k[b, members], dtype=np.float64),
+                        t_all[members], h_all[members], w_all[members], base)
+        vv = np.asarray(v[b, members], dtype=np.float64)
+        qq = rope_3d_at(np.asarray(q[b, toks], dtype=np.float64),
+                        t_all[toks], h_all[toks], w_all[toks], base)
+        o = attention(qq.transpose(1, 0, 2), kk.transpose(1, 0, 2), vv.transpose(1, 0, 2))
+        out[sel] = o.transpose(1, 0, 2)
+    return out
+
+
+def skiparse_flops(B, N, heads, head_dim, sparse_k):
+    """Forward attention FLOPs counted for a Skiparse call: 4 * B * heads * N * (N/k) * d.
+
+    Wan 2.1 report, section 4.3.1 "Workload Analysis": non-causal attention
+    costs beta*b*s^2*h with beta = 4 in the forward pass; Skiparse runs it
+    on k scopes of length N/k, i.e. k * 4 * (N/k)^2 * d per batch and head.
+    """
+    return 4.0 * B * heads * N * (N // sparse_k) * head_dim
