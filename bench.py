@@ -1,0 +1,230 @@
+"""Benchmark of the Skiparse attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one Skiparse attention forward of the 24x22x40-token (N = 21120)
+Open-Sora-Plan-like workload (B=1, 24 heads, head_dim 128, bf16, k = 4) in
+Single Skip mode followed by one in Group Skip mode, each a single launch of
+the fused kernel (RoPE, gather, attention, scatter).  Inputs are resident in
+HBM before timing starts.  Prints one JSON line with the throughput in
+TFLOP/s, the fused kernel's roofline figures, the standalone RoPE+remap pass
+in GB/s, and the fp64 oracle's throughput on the host cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_osp_24x22x40_traffic.md")
+ATTN_SOURCE = os.path.join(ROOT, "skiparse_sparse_attention_amd", "csrc", "attn_fwd.hip")
+
+
+def parse_args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
+    ap.add_argument("--no-remap", action="store_true", help="skip the standalone RoPE+remap pass")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB (counter calibration)")
+    return ap.parse_args()
+
+
+def source_digest():
+    with open(ATTN_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(per_launch_flops):
+    """HBM bytes per launch from the committed counter summary, if it matches this kernel."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    m_src = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not (m_src and m_b) or m_src.group(1) != source_digest():
+        return None
+    return float(m_b.group(1))
+
+
+def cpu_baseline(w, q, k, v, budget_s=15.0):
+    """Time the fp64 oracle on a bounded sample of the same workload (host cores)."""
+    import numpy as np
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    qn, kn, vn = (x.float().numpy() for x in (q, k, v))
+    table = oracle.scope_table(w.N, w.sparse_k, w.mode)
+    rng = np.random.default_rng(0)
+
+    def run(nrows):
+        toks = table[0, np.sort(rng.choice(w.L, size=nrows, replace=False))]
+        b = np.zeros_like(toks)
+        t0 = time.perf_counter()
+        oracle.skiparse_attention_rows(qn, kn, vn, w.T, w.H, w.W, w.sparse_k, w.mode, b, toks)
+        return time.perf_counter() - t0
+
+    # fixed cost (rotating the scope's keys) plus a per-row cost, from two short runs
+    t1, t2 = run(64), run(256)
+    per_row = max((t2 - t1) / 192.0, 1e-6)
+    fixed = max(t1 - 64 * per_row, 0.0)
+    nrows = int(min(w.L, max(256, (budget_s - fixed) / per_row)))
+    t = run(nrows)
+    flops = 4.0 * nrows * w.heads * w.L * w.head_dim
+    return {
+        "value": flops / t / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"{nrows} query tokens of scope 0 (all {w.heads} heads, all {w.L} keys of the scope) "
+                   f"of {w.name}, fp64 numpy, {t:.1f} s"),
+    }
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+
+    import skiparse_sparse_attention_amd as sk
+    from skiparse_sparse_attention_amd import workloads as wl
+
+    if not torch.cuda.is_available():
+        raise RuntimeError("bench.py needs a ROCm GPU")
+    torch.cuda.set_device(0)
+    sk.lib()
+
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_each_way": n * 4, "copies": 5}))
+        return
+
+    ws = wl.OSP_SINGLE
+    wg = wl.OSP_GROUP
+    q, k, v = wl.make_inputs(ws, seed=0, device="cpu")
+    qg, kg, vg = q.cuda(), k.cuda(), v.cuda()
+    out_s = torch.empty_like(qg)
+    out_g = torch.empty_like(qg)
+    stream = torch.cuda.current_stream()
+    flops_launch = sk.attn_flops(ws.B, ws.grid, ws.heads, ws.head_dim, ws.sparse_k)
+
+    def step():
+        sk.attn(qg, kg, vg, ws.grid, ws.sparse_k, ws.mode, out=out_s, stream=stream)
+        sk.attn(qg, kg, vg, wg.grid, wg.sparse_k, wg.mode, out=out_g, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # per-launch HIP events on the launch stream, inside the timed region
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(args.steps):
+        sk.attn(qg, kg, vg, ws.grid, ws.sparse_k, ws.mode, out=out_s, stream=stream)
+        ev[2 * i + 1].record(stream)
+        sk.attn(qg, kg, vg, wg.grid, wg.sparse_k, wg.mode, out=out_g, stream=stream)
+        ev[2 * i + 2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    durs = [ev[i].elapsed_time(ev[i + 1]) for i in range(2 * args.steps)]   # ms per launch
+    single_ms = sorted(durs[0::2])[len(durs[0::2]) // 2]
+    group_ms = sorted(durs[1::2])[len(durs[1::2]) // 2]
+    gpu_ms = sum(durs)
+    ms_per_step = wall * 1e3 / args.steps
+    value = 2 * flops_launch * args.steps / wall / 1e12
+    avg_launch_ms = gpu_ms / len(durs)
+    achieved = flops_launch / (avg_launch_ms * 1e-3) / 1e12
+    traffic = measured_traffic(flops_launch)
+
+    result = {
+        "metric": "Skiparse attention TFLOP/s (bf16) and % of MFMA peak at N~21k-46k, k=4",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "osp_24x22x40_h24_d128_k4: Single Skip + Group Skip per step",
+            "B": ws.B, "T": ws.T, "H": ws.H, "W": ws.W, "N": ws.N, "heads": ws.heads,
+            "head_dim": ws.head_dim, "sparse_k": ws.sparse_k, "modes": ["single", "group"],
+            "flop_per_launch": flops_launch,
+        },
+        "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "per_mode_ms": {"single": round(single_ms, 4), "group": round(group_ms, 4)},
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "attn_fwd_kernel<128, bf16>",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+            "avg_launch_ms": round(avg_launch_ms, 4),
+        },
+    }
+
+    if not args.no_remap:
+        rq, rk, rv = (torch.empty((ws.sparse_k * ws.B, ws.L, ws.heads, ws.head_dim),
+                                  dtype=qg.dtype, device="cuda") for _ in range(3))
+        for _ in range(3):
+            sk.rope_remap(qg, kg, vg, ws.grid, ws.sparse_k, ws.mode, outs=(rq, rk, rv), stream=stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 20
+        e0.record(stream)
+        for _ in range(reps):
+            sk.rope_remap(qg, kg, vg, ws.grid, ws.sparse_k, ws.mode, outs=(rq, rk, rv), stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        nbytes = 6 * qg.numel() * qg.element_size()    # read q, k, v; write three rearranged copies
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        result["remap_pass"] = {
+            "kernel": "rope_remap_kernel<128, bf16>",
+            "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4), "avg_launch_ms": round(ms, 4),
+            "bytes_per_launch": nbytes,
+        }
+        del rq, rk, rv
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(ws, q, k, v)
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,164 @@
+/*
+ * skiparse.h -- C ABI of the MI355X (gfx950) Skiparse attention library.
+ *
+ * Skiparse attention (Open-Sora Plan documentation, section "Skiparse
+ * Attention") splits the token sequence of a full-3D-attention block into
+ * sparse_k scopes and runs softmax attention inside each scope only:
+ *
+ *   1. 3D RoPE on q and k, at each token's original (t, h, w) grid position
+ *      (the page's implementation note: RoPE goes before the rearrange);
+ *   2. the Single Skip or Group Skip rearrange of q, k, v into sparse_k scopes
+ *      of L = N / sparse_k tokens (the page's einops patterns);
+ *   3. softmax(Q K^T / sqrt(head_dim)) V inside each scope, per head
+ *      (the page's scaled_dot_product_attention call: no mask, non-causal);
+ *   4. the inverse rearrange back to the original token order.
+ *
+ * With sparse_k == 1 this is dense full-3D attention.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Token layout.  q, k, v and out are dense, contiguous (B, N, heads, head_dim)
+ *   arrays, N = T*H*W, token n = (t*H + h)*W + w (Wan 2.1 report, section
+ *   4.2.1: the patchified latent is flattened frame-major into a (B, L, D)
+ *   sequence).  This is the page's (B, N, C) layout with C = heads*head_dim.
+ * Scopes.  Single Skip (mode 0): token n is in scope s = n mod k at in-scope
+ *   position p = n div k.  Group Skip (mode 1): token n is in scope
+ *   s = (n div k) mod k at position p = (n div k^2)*k + n mod k.  In-scope order
+ *   is increasing token index (the page's patterns 'b (g k) d -> (k b) g d' and
+ *   'b (n m k) d -> (m b) (n k) d', m = k).
+ * 3D RoPE.  head_dim is split 2:3:3 over the t, h, w axes (16/24/24 at
+ *   head_dim 64, 32/48/48 at 128), in that order.  Inside an axis chunk of size
+ *   d_a, slot j and slot j + d_a/2 form a rotate-half pair rotated by
+ *   pos_a * 10000^(-2j/d_a):  x1' = x1 cos - x2 sin,  x2' = x2 cos + x1 sin.
+ *   The pages use RoPE without defining it; this is the reading the library
+ *   implements.
+ * Precision.  dtype SKIPARSE_BF16: bf16 in, bf16 out, RoPE in fp32, attention
+ *   operands bf16 on the matrix cores with fp32 accumulation and fp32 softmax.
+ *   dtype SKIPARSE_FP32: fp32 in and out; attention rounds its rotated fp32
+ *   operands to bf16 at tile load (same arithmetic as bf16 otherwise); the
+ *   rearrange/reverse calls keep fp32 throughout.
+ * Pointers.  All array pointers are device pointers (hipMalloc'd or torch CUDA
+ *   tensors' data_ptr), 16-byte aligned.  The caller owns every buffer; the
+ *   library allocates nothing and keeps no state between calls.
+ * Streams.  `stream` is a hipStream_t passed as void* (NULL: the default
+ *   stream).  Calls are asynchronous: they return once the kernels are
+ *   enqueued; execution errors surface at the caller's next synchronization.
+ * Errors.  Every call validates its arguments on the host before any device
+ *   call and returns a skiparse_status; nothing aborts or prints.
+ */
+#ifndef SKIPARSE_H
+#define SKIPARSE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum skiparse_mode { SKIPARSE_SINGLE = 0, SKIPARSE_GROUP = 1 };
+enum skiparse_dtype { SKIPARSE_BF16 = 0, SKIPARSE_FP32 = 1 };
+
+enum skiparse_status {
+    SKIPARSE_OK = 0,
+    SKIPARSE_E_NULL = 1,          /* a required pointer is NULL                              */
+    SKIPARSE_E_SHAPE = 2,         /* a size is < 1, or a size product overflows              */
+    SKIPARSE_E_DIVISIBILITY = 3,  /* Single: N % k != 0; Group: N % k^2 != 0 (no padding)     */
+    SKIPARSE_E_UNSUPPORTED = 4,   /* head_dim not 64/128, bad mode/dtype, grid too large     */
+    SKIPARSE_E_ALIAS = 5,         /* an output buffer overlaps an input buffer               */
+    SKIPARSE_E_DEVICE = 6         /* a HIP call failed (launch error, no device, ...)        */
+};
+
+/* Largest number of (cos, sin) pairs of one 3D-RoPE table,
+ * T*d_t/2 + H*d_h/2 + W*d_w/2; larger grids return SKIPARSE_E_UNSUPPORTED.
+ * (At head_dim 128: 16*T + 24*H + 24*W <= 6144.) */
+#define SKIPARSE_MAX_ROPE_PAIRS 6144
+
+/*
+ * skiparse_attn -- the fused Skiparse attention forward (steps 1-4 above).
+ *
+ * q, k, v : (B, N, heads, head_dim) inputs in `dtype`, N = T*H*W.
+ * out     : (B, N, heads, head_dim) output in `dtype`, in the original token
+ *           order; must not overlap q, k or v.
+ * sparse_k: number of scopes k >= 1 (Single: N % k == 0; Group: N % k^2 == 0).
+ * head_dim: 64 or 128.
+ * One kernel launch.  The rearranged q, k, v are never written to memory:
+ * each tile load gathers its scope's rows and rotates them on the fly, and
+ * the epilogue writes each output row straight to its original token index.
+ * Returns SKIPARSE_OK or an error code; the output is not touched on error.
+ */
+int skiparse_attn(const void* q, const void* k, const void* v,
+                  int B, int T, int H, int W, int heads, int head_dim,
+                  int sparse_k, int mode, int dtype, void* out, void* stream);
+
+/*
+ * skiparse_rope_remap -- the materialised RoPE + rearrange of q, k and v in
+ * one pass (the page's add_rope + *_skip_rearrange calls, before attention).
+ *
+ * q, k, v    : (B, N, heads, head_dim) inputs in `dtype`.
+ * rq, rk, rv : (sparse_k*B, N/sparse_k, heads, head_dim) outputs in `dtype`;
+ *              row s*B + b holds scope s of batch b (the page's '(k b)' /
+ *              '(m b)' batch order).  rq, rk are rotated by 3D RoPE at each
+ *              token's original position; rv is moved unchanged.
+ * No output may overlap any input.  One kernel launch.
+ */
+int skiparse_rope_remap(const void* q, const void* k, const void* v,
+                        int B, int T, int H, int W, int heads, int head_dim,
+                        int sparse_k, int mode, int dtype,
+                        void* rq, void* rk, void* rv, void* stream);
+
+/*
+ * skiparse_rearrange -- one tensor: (B, N, heads, head_dim) ->
+ * (sparse_k*B, N/sparse_k, heads, head_dim), optionally rotated by 3D RoPE
+ * first (apply_rope != 0).  With apply_rope == 0 the bytes are moved
+ * unchanged (bit-exact for either dtype).  out must not overlap x.
+ */
+int skiparse_rearrange(const void* x, int B, int T, int H, int W, int heads,
+                       int head_dim, int sparse_k, int mode, int dtype,
+                       int apply_rope, void* out, void* stream);
+
+/*
+ * skiparse_reverse -- the page's reverse_sparse: (sparse_k*B, N/sparse_k,
+ * heads, head_dim) -> (B, N, heads, head_dim), bytes moved unchanged.
+ * out must not overlap x.
+ */
+int skiparse_reverse(const void* x, int B, int T, int H, int W, int heads,
+                     int head_dim, int sparse_k, int mode, int dtype,
+                     void* out, void* stream);
+
+/*
+ * skiparse_validate -- the argument checks skiparse_attn performs, with no
+ * device call (host-only; usable without a GPU).  Pointers may be any
+ * non-NULL values; only their ranges are compared for overlap.
+ */
+int skiparse_validate(const void* q, const void* k, const void* v,
+                      int B, int T, int H, int W, int heads, int head_dim,
+                      int sparse_k, int mode, int dtype, const void* out);
+
+/*
+ * skiparse_scope_table -- host-only: fills token_of[s*(N/k) + p] with the
+ * token index at position p of scope s (int64, k*(N/k) = N entries, caller-owned).
+ * The same index arithmetic the kernels use.  Returns SKIPARSE_OK, or
+ * E_NULL / E_SHAPE / E_DIVISIBILITY / E_UNSUPPORTED on bad arguments.
+ */
+int skiparse_scope_table(int64_t N, int sparse_k, int mode, int64_t* token_of);
+
+/*
+ * skiparse_attn_flops -- FLOPs counted for one skiparse_attn call:
+ * 4*B*heads*N*(N/k)*head_dim (Wan 2.1 report, section 4.3.1: non-causal
+ * forward attention costs 4*b*s^2*h, here over k scopes of length N/k).
+ * Returns a negative value for invalid sizes.
+ */
+double skiparse_attn_flops(int B, int T, int H, int W, int heads, int head_dim,
+                           int sparse_k);
+
+/* Static English text for a status code (never NULL). */
+const char* skiparse_status_string(int status);
+
+/* Library version string, e.g. "0.1.0 gfx950". */
+const char* skiparse_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SKIPARSE_H */

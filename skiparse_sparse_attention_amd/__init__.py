@@ -1,0 +1,33 @@
+"""Skiparse sparse attention for AMD MI355X (gfx950).
+
+The computation lives in the HIP library ``libskiparse_amd.so`` (C ABI in
+include/skiparse.h); this package is its Python binding.  Loading is lazy:
+importing the package does not open the library, the first call does, and it
+raises if the library has not been built.
+"""
+
+from ._lib import (  # noqa: F401
+    BF16,
+    E_ALIAS,
+    E_DEVICE,
+    E_DIVISIBILITY,
+    E_NULL,
+    E_SHAPE,
+    E_UNSUPPORTED,
+    FP32,
+    GROUP,
+    LIB_PATH,
+    MAX_ROPE_PAIRS,
+    OK,
+    SINGLE,
+    SkiparseError,
+    attn,
+    attn_flops,
+    lib,
+    rearrange,
+    reverse,
+    rope_remap,
+    scope_table,
+    status_string,
+    version,
+)

@@ -1,0 +1,181 @@
+"""ctypes binding of ``libskiparse_amd.so`` (C ABI: include/skiparse.h).
+
+Argument marshalling only: tensors are passed by device pointer, the stream is
+torch's current HIP stream, and every step of the computation runs in the
+library's kernels.  There is no fallback: if the library is not built the
+calls raise.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libskiparse_amd.so")
+
+SINGLE = 0
+GROUP = 1
+BF16 = 0
+FP32 = 1
+
+OK = 0
+E_NULL = 1
+E_SHAPE = 2
+E_DIVISIBILITY = 3
+E_UNSUPPORTED = 4
+E_ALIAS = 5
+E_DEVICE = 6
+
+MAX_ROPE_PAIRS = 6144
+
+_lib = None
+
+
+class SkiparseError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({status_string(status)})")
+
+
+def lib():
+    """Load the HIP library once; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m skiparse_sparse_attention_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+        dims = [i] * 6  # B, T, H, W, heads, head_dim
+        L.skiparse_attn.argtypes = [vp, vp, vp] + dims + [i, i, i, vp, vp]
+        L.skiparse_attn.restype = i
+        L.skiparse_rope_remap.argtypes = [vp, vp, vp] + dims + [i, i, i, vp, vp, vp, vp]
+        L.skiparse_rope_remap.restype = i
+        L.skiparse_rearrange.argtypes = [vp] + dims + [i, i, i, i, vp, vp]
+        L.skiparse_rearrange.restype = i
+        L.skiparse_reverse.argtypes = [vp] + dims + [i, i, i, vp, vp]
+        L.skiparse_reverse.restype = i
+        L.skiparse_validate.argtypes = [vp, vp, vp] + dims + [i, i, i, vp]
+        L.skiparse_validate.restype = i
+        L.skiparse_scope_table.argtypes = [i64, i, i, ctypes.POINTER(ctypes.c_int64)]
+        L.skiparse_scope_table.restype = i
+        L.skiparse_attn_flops.argtypes = [i] * 7
+        L.skiparse_attn_flops.restype = ctypes.c_double
+        L.skiparse_status_string.argtypes = [i]
+        L.skiparse_status_string.restype = ctypes.c_char_p
+        L.skiparse_version.argtypes = []
+        L.skiparse_version.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().skiparse_status_string(int(status)).decode()
+
+
+def version() -> str:
+    return lib().skiparse_version().decode()
+
+
+def _check(status: int, where: str):
+    if status != OK:
+        raise SkiparseError(status, where)
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return FP32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _stream_ptr(stream):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dims(x, grid):
+    if x.dim() != 4:
+        raise ValueError("expected a (B, N, heads, head_dim) tensor")
+    if not x.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    T, H, W = (int(g) for g in grid)
+    B, N, heads, d = x.shape
+    if N != T * H * W:
+        raise ValueError(f"N={N} does not match the grid {T}x{H}x{W}")
+    return B, T, H, W, heads, d
+
+
+def attn(q, k, v, grid, sparse_k, mode, out=None, stream=None):
+    """Fused Skiparse attention: q, k, v (B, N, heads, d) on the GPU -> out, same shape/dtype."""
+    import torch
+    B, T, H, W, heads, d = _dims(q, grid)
+    for t in (k, v):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
+            raise ValueError("q, k, v must share shape, dtype and be contiguous")
+    if out is None:
+        out = torch.empty_like(q)
+    _check(lib().skiparse_attn(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, T, H, W, heads, d,
+                               int(sparse_k), int(mode), _dtype_code(q), out.data_ptr(),
+                               _stream_ptr(stream)), "skiparse_attn")
+    return out
+
+
+def rope_remap(q, k, v, grid, sparse_k, mode, outs=None, stream=None):
+    """RoPE(q), RoPE(k), v rearranged to (k*B, N/k, heads, d); returns (rq, rk, rv)."""
+    import torch
+    B, T, H, W, heads, d = _dims(q, grid)
+    shape = (sparse_k * B, (T * H * W) // sparse_k, heads, d)
+    if outs is None:
+        outs = tuple(torch.empty(shape, dtype=q.dtype, device=q.device) for _ in range(3))
+    rq, rk, rv = outs
+    _check(lib().skiparse_rope_remap(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, T, H, W, heads, d,
+                                     int(sparse_k), int(mode), _dtype_code(q), rq.data_ptr(),
+                                     rk.data_ptr(), rv.data_ptr(), _stream_ptr(stream)),
+           "skiparse_rope_remap")
+    return rq, rk, rv
+
+
+def rearrange(x, grid, sparse_k, mode, apply_rope=False, out=None, stream=None):
+    """One tensor (B, N, heads, d) -> (k*B, N/k, heads, d), optionally rotated by 3D RoPE."""
+    import torch
+    B, T, H, W, heads, d = _dims(x, grid)
+    if out is None:
+        out = torch.empty((sparse_k * B, (T * H * W) // sparse_k, heads, d), dtype=x.dtype, device=x.device)
+    _check(lib().skiparse_rearrange(x.data_ptr(), B, T, H, W, heads, d, int(sparse_k), int(mode),
+                                    _dtype_code(x), int(bool(apply_rope)), out.data_ptr(),
+                                    _stream_ptr(stream)), "skiparse_rearrange")
+    return out
+
+
+def reverse(x, grid, sparse_k, mode, out=None, stream=None):
+    """(k*B, N/k, heads, d) -> (B, N, heads, d), the inverse of :func:`rearrange`."""
+    import torch
+    T, H, W = (int(g) for g in grid)
+    kB, L, heads, d = x.shape
+    B = kB // sparse_k
+    if out is None:
+        out = torch.empty((B, T * H * W, heads, d), dtype=x.dtype, device=x.device)
+    _check(lib().skiparse_reverse(x.data_ptr(), B, T, H, W, heads, d, int(sparse_k), int(mode),
+                                  _dtype_code(x), out.data_ptr(), _stream_ptr(stream)),
+           "skiparse_reverse")
+    return out
+
+
+def scope_table(N, sparse_k, mode):
+    """Host-side (k, N/k) int64 table: token index of position p of scope s (numpy array)."""
+    import numpy as np
+    out = np.empty(int(N), dtype=np.int64)
+    _check(lib().skiparse_scope_table(int(N), int(sparse_k), int(mode),
+                                      out.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))),
+           "skiparse_scope_table")
+    return out.reshape(int(sparse_k), int(N) // int(sparse_k))
+
+
+def attn_flops(B, grid, heads, head_dim, sparse_k):
+    T, H, W = (int(g) for g in grid)
+    return lib().skiparse_attn_flops(int(B), T, H, W, int(heads), int(head_dim), int(sparse_k))

@@ -1,0 +1,198 @@
+// Host side of the C ABI declared in include/skiparse.h: argument validation
+// (no device call before it passes), launch configuration, status codes.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <limits>
+
+#include "../../include/skiparse.h"
+#include "skiparse_index.hpp"
+#include "skiparse_launch.hpp"
+
+namespace {
+
+using skiparse::kGroup;
+using skiparse::kSingle;
+
+constexpr int64_t kI32Max = std::numeric_limits<int32_t>::max();
+
+struct Dims {
+    int64_t N = 0, L = 0, elems = 0, bytes = 0;
+    int esize = 0;
+};
+
+// Checks shared by every device entry point.  Fills `d` on success.
+int check_dims(int B, int T, int H, int W, int heads, int head_dim, int sparse_k,
+               int mode, int dtype, Dims* d) {
+    if (B < 1 || T < 1 || H < 1 || W < 1 || heads < 1 || head_dim < 1 || sparse_k < 1)
+        return SKIPARSE_E_SHAPE;
+    if (mode != SKIPARSE_SINGLE && mode != SKIPARSE_GROUP) return SKIPARSE_E_UNSUPPORTED;
+    if (dtype != SKIPARSE_BF16 && dtype != SKIPARSE_FP32) return SKIPARSE_E_UNSUPPORTED;
+    if (head_dim != 64 && head_dim != 128) return SKIPARSE_E_UNSUPPORTED;
+    if ((int64_t)T * H > kI32Max) return SKIPARSE_E_SHAPE;  // keeps T*H*W inside int64
+    const int64_t N = (int64_t)T * H * W;
+    if (N > kI32Max) return SKIPARSE_E_SHAPE;
+    // every kernel indexes destination rows and (row, head, chunk) tasks in 32 bits
+    const int64_t rows = (int64_t)B * N;
+    if (rows > kI32Max || rows * heads > kI32Max / 8) return SKIPARSE_E_SHAPE;
+    if (mode == SKIPARSE_SINGLE) {
+        if (N % sparse_k) return SKIPARSE_E_DIVISIBILITY;
+    } else {
+        const int64_t k2 = (int64_t)sparse_k * sparse_k;
+        if (k2 > N || N % k2) return SKIPARSE_E_DIVISIBILITY;
+    }
+    if (skiparse::rope_table_pairs(T, H, W, head_dim) > SKIPARSE_MAX_ROPE_PAIRS)
+        return SKIPARSE_E_UNSUPPORTED;
+    d->N = N;
+    d->L = N / sparse_k;
+    d->esize = dtype == SKIPARSE_BF16 ? 2 : 4;
+    d->elems = rows * heads * head_dim;
+    d->bytes = d->elems * d->esize;
+    return SKIPARSE_OK;
+}
+
+bool overlaps(const void* a, const void* b, int64_t bytes) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + (uintptr_t)bytes && y < x + (uintptr_t)bytes;
+}
+
+int to_status(hipError_t e) { return e == hipSuccess ? SKIPARSE_OK : SKIPARSE_E_DEVICE; }
+
+int remap_grid(int64_t tasks) {
+    // persistent-style grid: at most 8 blocks of 256 threads per CU of a 256-CU part
+    const int64_t blocks = (tasks + 255) / 256;
+    return (int)(blocks < 2048 ? (blocks > 0 ? blocks : 1) : 2048);
+}
+
+}  // namespace
+
+extern "C" {
+
+int skiparse_validate(const void* q, const void* k, const void* v, int B, int T, int H, int W,
+                      int heads, int head_dim, int sparse_k, int mode, int dtype, const void* out) {
+    if (!q || !k || !v || !out) return SKIPARSE_E_NULL;
+    Dims d;
+    const int st = check_dims(B, T, H, W, heads, head_dim, sparse_k, mode, dtype, &d);
+    if (st != SKIPARSE_OK) return st;
+    if (overlaps(out, q, d.bytes) || overlaps(out, k, d.bytes) || overlaps(out, v, d.bytes))
+        return SKIPARSE_E_ALIAS;
+    return SKIPARSE_OK;
+}
+
+int skiparse_attn(const void* q, const void* k, const void* v, int B, int T, int H, int W,
+                  int heads, int head_dim, int sparse_k, int mode, int dtype, void* out,
+                  void* stream) {
+    const int st = skiparse_validate(q, k, v, B, T, H, W, heads, head_dim, sparse_k, mode, dtype, out);
+    if (st != SKIPARSE_OK) return st;
+    Dims d;
+    check_dims(B, T, H, W, heads, head_dim, sparse_k, mode, dtype, &d);
+    skiparse::AttnParams a;
+    a.q = q; a.k = k; a.v = v; a.out = out;
+    a.B = B; a.T = T; a.H = H; a.W = W; a.heads = heads;
+    a.sparse_k = sparse_k; a.mode = mode;
+    a.N = (int)d.N; a.L = (int)d.L;
+    const int bm = skiparse::attn_block_rows(), bn = skiparse::attn_tile_keys();
+    a.q_tiles = (int)((d.L + bm - 1) / bm);
+    const int64_t work = (int64_t)B * heads * sparse_k * a.q_tiles;
+    if (work > kI32Max) return SKIPARSE_E_SHAPE;
+    a.num_work = (int)work;
+    a.k_divides_bn = (bn % sparse_k) == 0;
+    a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)head_dim));
+    return to_status(skiparse::launch_attn(a, head_dim, dtype, static_cast<hipStream_t>(stream)));
+}
+
+int skiparse_rope_remap(const void* q, const void* k, const void* v, int B, int T, int H, int W,
+                        int heads, int head_dim, int sparse_k, int mode, int dtype, void* rq,
+                        void* rk, void* rv, void* stream) {
+    if (!q || !k || !v || !rq || !rk || !rv) return SKIPARSE_E_NULL;
+    Dims d;
+    const int st = check_dims(B, T, H, W, heads, head_dim, sparse_k, mode, dtype, &d);
+    if (st != SKIPARSE_OK) return st;
+    const void* ins[3] = {q, k, v};
+    void* outs[3] = {rq, rk, rv};
+    for (int i = 0; i < 3; ++i) {
+        for (int j = 0; j < 3; ++j)
+            if (overlaps(outs[i], ins[j], d.bytes)) return SKIPARSE_E_ALIAS;
+        for (int j = i + 1; j < 3; ++j)
+            if (overlaps(outs[i], outs[j], d.bytes)) return SKIPARSE_E_ALIAS;
+    }
+    skiparse::RemapParams a;
+    for (int i = 0; i < 3; ++i) { a.src[i] = ins[i]; a.dst[i] = outs[i]; }
+    a.ntensors = 3;
+    a.rope_mask = 0x3;  // q and k are rotated, v is moved unchanged
+    a.B = B; a.T = T; a.H = H; a.W = W; a.heads = heads; a.k = sparse_k; a.mode = mode;
+    a.L = (int)d.L; a.N = (int)d.N; a.rows = (int)(B * d.N);
+    return to_status(skiparse::launch_rope_remap(a, head_dim, dtype, static_cast<hipStream_t>(stream),
+                                                 remap_grid((int64_t)a.rows * heads * 8)));
+}
+
+int skiparse_rearrange(const void* x, int B, int T, int H, int W, int heads, int head_dim,
+                       int sparse_k, int mode, int dtype, int apply_rope, void* out, void* stream) {
+    if (!x || !out) return SKIPARSE_E_NULL;
+    Dims d;
+    const int st = check_dims(B, T, H, W, heads, head_dim, sparse_k, mode, dtype, &d);
+    if (st != SKIPARSE_OK) return st;
+    if (overlaps(out, x, d.bytes)) return SKIPARSE_E_ALIAS;
+    skiparse::RemapParams a;
+    a.src[0] = x; a.dst[0] = out;
+    a.src[1] = a.src[2] = nullptr;
+    a.dst[1] = a.dst[2] = nullptr;
+    a.ntensors = 1;
+    a.rope_mask = apply_rope ? 1 : 0;
+    a.B = B; a.T = T; a.H = H; a.W = W; a.heads = heads; a.k = sparse_k; a.mode = mode;
+    a.L = (int)d.L; a.N = (int)d.N; a.rows = (int)(B * d.N);
+    return to_status(skiparse::launch_rope_remap(a, head_dim, dtype, static_cast<hipStream_t>(stream),
+                                                 remap_grid((int64_t)a.rows * heads * 8)));
+}
+
+int skiparse_reverse(const void* x, int B, int T, int H, int W, int heads, int head_dim,
+                     int sparse_k, int mode, int dtype, void* out, void* stream) {
+    if (!x || !out) return SKIPARSE_E_NULL;
+    Dims d;
+    const int st = check_dims(B, T, H, W, heads, head_dim, sparse_k, mode, dtype, &d);
+    if (st != SKIPARSE_OK) return st;
+    if (overlaps(out, x, d.bytes)) return SKIPARSE_E_ALIAS;
+    skiparse::ReverseParams a;
+    a.src = x; a.dst = out;
+    a.B = B; a.N = (int)d.N; a.k = sparse_k; a.mode = mode; a.L = (int)d.L;
+    a.rows = (int)(B * d.N);
+    a.row_bytes = (uint32_t)(heads * head_dim * d.esize);
+    return to_status(skiparse::launch_reverse(a, static_cast<hipStream_t>(stream),
+                                              remap_grid((int64_t)a.rows * (a.row_bytes / 16))));
+}
+
+int skiparse_scope_table(int64_t N, int sparse_k, int mode, int64_t* token_of) {
+    if (!token_of) return SKIPARSE_E_NULL;
+    if (N < 1 || sparse_k < 1) return SKIPARSE_E_SHAPE;
+    if (mode != SKIPARSE_SINGLE && mode != SKIPARSE_GROUP) return SKIPARSE_E_UNSUPPORTED;
+    const int64_t k = sparse_k;
+    if (mode == SKIPARSE_SINGLE ? (N % k) : (k * k > N || N % (k * k))) return SKIPARSE_E_DIVISIBILITY;
+    const int64_t L = N / k;
+    for (int64_t s = 0; s < k; ++s)
+        for (int64_t p = 0; p < L; ++p) token_of[s * L + p] = skiparse::scope_token(p, s, k, mode);
+    return SKIPARSE_OK;
+}
+
+double skiparse_attn_flops(int B, int T, int H, int W, int heads, int head_dim, int sparse_k) {
+    if (B < 1 || T < 1 || H < 1 || W < 1 || heads < 1 || head_dim < 1 || sparse_k < 1) return -1.0;
+    const double N = (double)T * H * W;
+    return 4.0 * B * heads * N * std::floor(N / sparse_k) * head_dim;
+}
+
+const char* skiparse_status_string(int status) {
+    switch (status) {
+        case SKIPARSE_OK: return "ok";
+        case SKIPARSE_E_NULL: return "a required pointer is NULL";
+        case SKIPARSE_E_SHAPE: return "a size is < 1 or a size product overflows";
+        case SKIPARSE_E_DIVISIBILITY: return "N is not divisible by k (Single Skip) or k^2 (Group Skip)";
+        case SKIPARSE_E_UNSUPPORTED: return "unsupported head_dim, mode, dtype or grid size";
+        case SKIPARSE_E_ALIAS: return "an output buffer overlaps an input buffer";
+        case SKIPARSE_E_DEVICE: return "a HIP call failed";
+        default: return "unknown status";
+    }
+}
+
+const char* skiparse_version(void) { return "0.1.0 gfx950"; }
+
+}  // extern "C"

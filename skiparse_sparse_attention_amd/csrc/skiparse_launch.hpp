@@ -1,0 +1,45 @@
+// Kernel parameter blocks and launchers (internal to the library; the public
+// interface is include/skiparse.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace skiparse {
+
+struct RemapParams {
+    const void* src[3];
+    void* dst[3];
+    int ntensors;   // 1 or 3
+    int rope_mask;  // bit i set: rotate tensor i by 3D RoPE before moving it
+    int B, T, H, W, heads, k, mode, L, N;
+    int rows;       // B*N destination rows
+};
+
+struct ReverseParams {
+    const void* src;
+    void* dst;
+    int B, N, k, mode, L;
+    int rows;          // B*N
+    uint32_t row_bytes;  // heads*head_dim*element size (multiple of 16)
+};
+
+struct AttnParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* out;
+    int B, T, H, W, heads, sparse_k, mode, N, L;
+    int q_tiles;     // ceil(L / BM)
+    int num_work;    // B*heads*sparse_k*q_tiles workgroups
+    int k_divides_bn;  // sparse_k divides the key-tile height
+    float scale_log2;  // log2(e) / sqrt(head_dim)
+};
+
+hipError_t launch_rope_remap(const RemapParams& a, int head_dim, int dtype, hipStream_t stream, int grid);
+hipError_t launch_reverse(const ReverseParams& a, hipStream_t stream, int grid);
+hipError_t launch_attn(const AttnParams& a, int head_dim, int dtype, hipStream_t stream);
+int attn_block_rows();  // query rows per attention workgroup
+int attn_tile_keys();   // keys per attention K/V tile
+
+}  // namespace skiparse

@@ -1,0 +1,111 @@
+"""CPU tests of the C-ABI library: it loads, exports every declared symbol, and
+its host-side logic (validation, index tables, FLOP count) is right.  No
+compute call reaches a device here: every call below either runs host code
+only or is rejected by validation before any HIP call."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import skiparse_sparse_attention_amd as sk
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "skiparse.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(sk.LIB_PATH), reason="library not built")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(skiparse_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for want in ("skiparse_attn", "skiparse_rope_remap", "skiparse_rearrange", "skiparse_reverse",
+                 "skiparse_validate", "skiparse_scope_table", "skiparse_attn_flops",
+                 "skiparse_status_string", "skiparse_version"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(sk.LIB_PATH)
+    for name in _declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_version_and_status_strings():
+    assert "gfx950" in sk.version()
+    for st in range(0, 7):
+        assert sk.status_string(st)
+    assert sk.status_string(99) == "unknown status"
+
+
+# fake, non-overlapping "device" addresses: validation only compares ranges
+Q, K, V, OUT = 1 << 40, 2 << 40, 3 << 40, 4 << 40
+GOOD = dict(B=1, T=4, H=8, W=8, heads=2, head_dim=64, sparse_k=2, mode=0, dtype=1)
+
+
+def _validate(q=Q, k=K, v=V, out=OUT, **kw):
+    a = dict(GOOD)
+    a.update(kw)
+    return sk.lib().skiparse_validate(q, k, v, a["B"], a["T"], a["H"], a["W"], a["heads"],
+                                      a["head_dim"], a["sparse_k"], a["mode"], a["dtype"], out)
+
+
+def test_validate_accepts_good_arguments():
+    assert _validate() == sk.OK
+    assert _validate(mode=1) == sk.OK  # 256 % 4 == 0
+    assert _validate(head_dim=128, dtype=0, sparse_k=8, mode=0) == sk.OK
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), sk.E_NULL), (dict(k=None), sk.E_NULL), (dict(v=None), sk.E_NULL),
+    (dict(out=None), sk.E_NULL),
+    (dict(B=0), sk.E_SHAPE), (dict(T=-1), sk.E_SHAPE), (dict(heads=0), sk.E_SHAPE),
+    (dict(sparse_k=0), sk.E_SHAPE),
+    (dict(T=1 << 20, H=1 << 20, W=4), sk.E_SHAPE),          # T*H*W overflows int32
+    (dict(head_dim=96), sk.E_UNSUPPORTED), (dict(mode=2), sk.E_UNSUPPORTED),
+    (dict(dtype=5), sk.E_UNSUPPORTED),
+    (dict(sparse_k=3), sk.E_DIVISIBILITY),                  # 256 % 3
+    (dict(sparse_k=32, mode=1), sk.E_DIVISIBILITY),         # 256 % 1024
+    (dict(sparse_k=512), sk.E_DIVISIBILITY),
+    (dict(T=400, H=4, W=4, head_dim=128), sk.E_UNSUPPORTED),  # RoPE table > 6144 pairs
+    (dict(out=Q + 64), sk.E_ALIAS), (dict(out=V - 64), sk.E_ALIAS), (dict(out=K), sk.E_ALIAS),
+])
+def test_validate_rejects(kw, status):
+    assert _validate(**kw) == status
+
+
+def test_attn_rejects_before_any_device_call():
+    # invalid calls must return their code without touching the (absent) GPU
+    L = sk.lib()
+    assert L.skiparse_attn(Q, K, V, 1, 4, 8, 8, 2, 64, 3, 0, 1, OUT, None) == sk.E_DIVISIBILITY
+    assert L.skiparse_attn(Q, K, V, 1, 4, 8, 8, 2, 64, 2, 0, 1, Q, None) == sk.E_ALIAS
+    assert L.skiparse_rope_remap(Q, K, V, 1, 4, 8, 8, 2, 64, 2, 0, 1, OUT, OUT, OUT + (1 << 30), None) == sk.E_ALIAS
+    assert L.skiparse_rearrange(None, 1, 4, 8, 8, 2, 64, 2, 0, 1, 0, OUT, None) == sk.E_NULL
+    assert L.skiparse_reverse(Q, 1, 4, 8, 8, 2, 65, 2, 0, 1, OUT, None) == sk.E_UNSUPPORTED
+
+
+@pytest.mark.parametrize("N,k", [(256, 1), (256, 2), (256, 4), (256, 8), (21120, 4), (36864, 4),
+                                 (32760, 1), (32760, 2), (46080, 8), (27, 3), (36, 3), (480, 4)])
+@pytest.mark.parametrize("mode", [oracle.SINGLE, oracle.GROUP])
+def test_scope_table_matches_oracle_exactly(N, k, mode):
+    if mode == oracle.GROUP and N % (k * k):
+        with pytest.raises(sk.SkiparseError):
+            sk.scope_table(N, k, mode)
+        return
+    got = sk.scope_table(N, k, mode)
+    assert got.dtype == np.int64
+    assert np.array_equal(got, oracle.scope_table(N, k, mode))
+
+
+def test_attn_flops_matches_definition():
+    assert sk.attn_flops(1, (24, 22, 40), 24, 128, 4) == oracle.skiparse_flops(1, 21120, 24, 128, 4)
+    assert sk.attn_flops(2, (20, 48, 48), 24, 128, 8) == oracle.skiparse_flops(2, 46080, 24, 128, 8)
+    assert sk.attn_flops(0, (1, 1, 1), 1, 64, 1) < 0

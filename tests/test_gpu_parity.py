@@ -1,0 +1,337 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle.
+
+Bars:
+* permutation / index work (rearrange, reverse, the value rows of the
+  materialised pass): bit-exact;
+* 3D RoPE in the materialised pass: within one bf16 ulp of the fp64 value
+  (bf16), within 2e-6 absolute (fp32, |x| ~ N(0,1));
+* attention: max |err| <= 2e-2 and mean |err| <= 2e-3 against the fp64 oracle
+  (bf16 operands on the matrix cores, fp32 accumulation and softmax), plus
+  an internal gate of relative RMS error <= 1e-2;
+* closed-form probes (uniform softmax, one-token scopes): bit-exact.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import skiparse_sparse_attention_amd as sk
+from skiparse_sparse_attention_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS = 2e-2
+MEAN_ABS = 2e-3
+REL_RMS = 1e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a ROCm GPU")
+    sk.lib()
+    yield
+
+
+def _np64(t):
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def _errors(got, want):
+    err = np.abs(got - want)
+    rel = np.sqrt((err ** 2).sum() / max((want ** 2).sum(), 1e-300))
+    return float(err.max()), float(err.mean()), float(rel)
+
+
+def _assert_close(got, want, what):
+    mx, mean, rel = _errors(got, want)
+    print(f"{what}: max {mx:.3e} mean {mean:.3e} relrms {rel:.3e}", flush=True)
+    assert np.isfinite(got).all(), what
+    assert mx <= MAX_ABS and mean <= MEAN_ABS and rel <= REL_RMS, (what, mx, mean, rel)
+
+
+def _inputs(B, T, H, W, heads, d, dtype, seed=0, scale=1.0):
+    w = wl.Workload("case", B, T, H, W, heads, d, 1, 0, "bf16" if dtype == torch.bfloat16 else "fp32", scale)
+    return wl.make_inputs(w, seed=seed, device="cuda")
+
+
+# ---------------------------------------------------------------------------
+# Permutation passes: bit-exact
+# ---------------------------------------------------------------------------
+
+PERM_SHAPES = [
+    # B, T, H, W, heads, d, k, mode, dtype
+    (1, 4, 8, 8, 2, 64, 2, oracle.SINGLE, torch.float32),
+    (1, 4, 8, 8, 2, 64, 4, oracle.GROUP, torch.float32),
+    (2, 4, 10, 12, 3, 128, 1, oracle.SINGLE, torch.bfloat16),
+    (2, 4, 10, 12, 3, 128, 2, oracle.GROUP, torch.bfloat16),
+    (2, 4, 10, 12, 3, 128, 4, oracle.SINGLE, torch.bfloat16),
+    (2, 4, 10, 12, 3, 128, 4, oracle.GROUP, torch.bfloat16),
+    (1, 4, 10, 12, 3, 64, 8, oracle.SINGLE, torch.bfloat16),
+    (1, 2, 8, 16, 2, 128, 8, oracle.GROUP, torch.float32),
+]
+
+
+def _random_bits(shape, dtype, seed):
+    g = torch.Generator().manual_seed(seed)
+    if dtype == torch.bfloat16:
+        bits = torch.randint(-2**15, 2**15, shape, generator=g, dtype=torch.int32).to(torch.int16)
+        return bits.view(torch.bfloat16), bits
+    bits = torch.randint(-2**31, 2**31 - 1, shape, generator=g, dtype=torch.int64).to(torch.int32)
+    return bits.view(torch.float32), bits
+
+
+@pytest.mark.parametrize("B,T,H,W,heads,d,k,mode,dtype", PERM_SHAPES)
+def test_rearrange_and_reverse_bit_exact(B, T, H, W, heads, d, k, mode, dtype):
+    N = T * H * W
+    x, bits = _random_bits((B, N, heads, d), dtype, seed=N + k + mode)   # includes NaN payloads
+    xg = x.cuda()
+    r = sk.rearrange(xg, (T, H, W), k, mode, apply_rope=False)
+    torch.cuda.synchronize()
+    ibits = torch.int16 if dtype == torch.bfloat16 else torch.int32
+    want = oracle.rearrange(bits.numpy().reshape(B, N, heads * d), k, mode).reshape(k * B, N // k, heads, d)
+    assert np.array_equal(r.cpu().view(ibits).numpy(), want)
+    back = sk.reverse(r, (T, H, W), k, mode)
+    torch.cuda.synchronize()
+    assert np.array_equal(back.cpu().view(ibits).numpy(), bits.numpy())
+    # reverse on its own input, against the oracle's reverse
+    y, ybits = _random_bits((k * B, N // k, heads, d), dtype, seed=7 * N + k)
+    got = sk.reverse(y.cuda(), (T, H, W), k, mode)
+    torch.cuda.synchronize()
+    want = oracle.reverse(ybits.numpy().reshape(k * B, N // k, heads * d), k, mode).reshape(B, N, heads, d)
+    assert np.array_equal(got.cpu().view(ibits).numpy(), want)
+
+
+def _bf16_ulps(got_bf16, exact64):
+    """Distance in bf16 ulps between a bf16 tensor and the bf16 rounding of an fp64 array."""
+    ref = torch.from_numpy(exact64).to(torch.bfloat16)
+    a = got_bf16.cpu().view(torch.int16).to(torch.int32)
+    b = ref.view(torch.int16).to(torch.int32)
+    # map sign-magnitude bit patterns onto a monotone integer line
+    a = torch.where(a < 0, -(a & 0x7FFF), a)
+    b = torch.where(b < 0, -(b & 0x7FFF), b)
+    return (a - b).abs()
+
+
+@pytest.mark.parametrize("B,T,H,W,heads,d,k,mode,dtype", PERM_SHAPES)
+def test_rope_remap_matches_oracle(B, T, H, W, heads, d, k, mode, dtype):
+    q, kk, v = _inputs(B, T, H, W, heads, d, dtype, seed=3)
+    rq, rk, rv = sk.rope_remap(q, kk, v, (T, H, W), k, mode)
+    single = sk.rearrange(q, (T, H, W), k, mode, apply_rope=True)
+    torch.cuda.synchronize()
+    eq = oracle.rope_rearrange(_np64(q), T, H, W, k, mode, True)
+    ek = oracle.rope_rearrange(_np64(kk), T, H, W, k, mode, True)
+    ev = oracle.rope_rearrange(_np64(v), T, H, W, k, mode, False)
+    if dtype == torch.bfloat16:
+        assert int(_bf16_ulps(rq, eq).max()) <= 1
+        assert int(_bf16_ulps(rk, ek).max()) <= 1
+    else:
+        assert np.abs(_np64(rq) - eq).max() <= 2e-6
+        assert np.abs(_np64(rk) - ek).max() <= 2e-6
+    assert np.array_equal(_np64(rv), ev)                       # v moves bit-exactly
+    assert torch.equal(single.view(torch.int16 if dtype == torch.bfloat16 else torch.int32),
+                       rq.view(torch.int16 if dtype == torch.bfloat16 else torch.int32))
+
+
+# ---------------------------------------------------------------------------
+# Attention: small sizes, full oracle
+# ---------------------------------------------------------------------------
+
+def test_attn_tiny_config_fp32():
+    w = wl.TINY
+    q, k, v = wl.make_inputs(w, seed=0, device="cuda")
+    out = sk.attn(q, k, v, w.grid, w.sparse_k, w.mode)
+    torch.cuda.synchronize()
+    want = oracle.skiparse_attention(_np64(q), _np64(k), _np64(v), w.T, w.H, w.W, w.sparse_k, w.mode)
+    _assert_close(_np64(out), want, w.name)
+    assert out.dtype == torch.float32
+
+
+SMALL = [
+    # B, T, H, W, heads, d, k, mode, dtype -- N = 480 spans several key tiles, ragged ends
+    (2, 4, 10, 12, 3, 128, 1, oracle.SINGLE, torch.bfloat16),
+    (2, 4, 10, 12, 3, 128, 2, oracle.SINGLE, torch.bfloat16),
+    (2, 4, 10, 12, 3, 128, 2, oracle.GROUP, torch.bfloat16),
+    (2, 4, 10, 12, 3, 128, 4, oracle.SINGLE, torch.bfloat16),
+    (2, 4, 10, 12, 3, 128, 4, oracle.GROUP, torch.bfloat16),
+    (1, 4, 10, 12, 2, 64, 4, oracle.GROUP, torch.bfloat16),
+    (1, 4, 10, 12, 2, 128, 2, oracle.GROUP, torch.float32),
+    (1, 3, 5, 7, 2, 128, 3, oracle.SINGLE, torch.bfloat16),   # k does not divide the key tile
+    (1, 3, 6, 6, 2, 128, 3, oracle.GROUP, torch.bfloat16),
+    (1, 9, 10, 12, 2, 128, 1, oracle.SINGLE, torch.bfloat16),  # L = 1080: 5 q tiles, 34 key tiles
+]
+
+
+@pytest.mark.parametrize("B,T,H,W,heads,d,k,mode,dtype", SMALL)
+def test_attn_small_matches_oracle(B, T, H, W, heads, d, k, mode, dtype):
+    q, kk, v = _inputs(B, T, H, W, heads, d, dtype, seed=11)
+    out = torch.full_like(q, float("nan"))           # coverage sentinel
+    sk.attn(q, kk, v, (T, H, W), k, mode, out=out)
+    torch.cuda.synchronize()
+    got = _np64(out)
+    assert np.isfinite(got).all(), "some output element was not written"
+    want = oracle.skiparse_attention(_np64(q), _np64(kk), _np64(v), T, H, W, k, mode)
+    _assert_close(got, want, f"small {B}x{T}x{H}x{W} h{heads} d{d} k{k} m{mode} {dtype}")
+
+
+def test_attn_peaked_softmax():
+    # q * 4: scores with std ~4 and a sharply peaked softmax.  Rounding the rotated q and
+    # k to bf16 for the matrix cores perturbs each score in proportion to its magnitude,
+    # so the absolute bars of the N(0,1) workloads scale by the same factor of 4 here;
+    # the relative RMS gate is unchanged.
+    B, T, H, W, heads, d, k, mode = 1, 4, 10, 12, 2, 128, 2, oracle.GROUP
+    q, kk, v = _inputs(B, T, H, W, heads, d, torch.bfloat16, seed=5)
+    q = (q.float() * 4.0).to(torch.bfloat16)
+    out = sk.attn(q, kk, v, (T, H, W), k, mode)
+    torch.cuda.synchronize()
+    want = oracle.skiparse_attention(_np64(q), _np64(kk), _np64(v), T, H, W, k, mode)
+    mx, mean, rel = _errors(_np64(out), want)
+    print(f"peaked q*4: max {mx:.3e} mean {mean:.3e} relrms {rel:.3e}", flush=True)
+    assert mx <= 4 * MAX_ABS and mean <= 4 * MEAN_ABS and rel <= REL_RMS
+
+
+def test_attn_huge_scores_stay_finite_and_convex():
+    # q * 32, k * 2: scores of magnitude ~200, whose unshifted exponentials overflow fp32.
+    # The running-max subtraction must keep every output finite, and each output row is a
+    # convex combination of the scope's v rows (bounded by their per-column min and max).
+    # Operand rounding to bf16 moves scores this large by ~0.5, so the row-wise oracle bar
+    # does not apply here; the oracle is compared on the mean error only.
+    B, T, H, W, heads, d, k, mode = 1, 4, 10, 12, 2, 128, 2, oracle.SINGLE
+    q, kk, v = _inputs(B, T, H, W, heads, d, torch.bfloat16, seed=6)
+    q = (q.float() * 32.0).to(torch.bfloat16)
+    kk = (kk.float() * 2.0).to(torch.bfloat16)
+    out = _np64(sk.attn(q, kk, v, (T, H, W), k, mode))
+    assert np.isfinite(out).all()
+    vn = _np64(v)
+    table = oracle.scope_table(T * H * W, k, mode)
+    for s in range(k):
+        lo = vn[0, table[s]].min(axis=0)
+        hi = vn[0, table[s]].max(axis=0)
+        o = out[0, table[s]]
+        assert (o >= lo - 1e-2).all() and (o <= hi + 1e-2).all()
+    want = oracle.skiparse_attention(_np64(q), _np64(kk), vn, T, H, W, k, mode)
+    assert np.abs(out - want).mean() < 0.1
+
+
+def test_attn_uses_original_positions_for_rope():
+    # RoPE before the rearrange: matches the oracle, and is far from the variant that
+    # rotates by in-scope positions instead.
+    B, T, H, W, heads, d, k, mode = 1, 4, 8, 8, 2, 128, 2, oracle.SINGLE
+    q, kk, v = _inputs(B, T, H, W, heads, d, torch.bfloat16, seed=9)
+    out = _np64(sk.attn(q, kk, v, (T, H, W), k, mode))
+    qn, kn, vn = _np64(q), _np64(kk), _np64(v)
+    right = oracle.skiparse_attention(qn, kn, vn, T, H, W, k, mode)
+    rq = oracle.rope_3d(oracle.rope_rearrange(qn, T, H, W, k, mode, False), T // k, H, W)
+    rk = oracle.rope_3d(oracle.rope_rearrange(kn, T, H, W, k, mode, False), T // k, H, W)
+    rv = oracle.rope_rearrange(vn, T, H, W, k, mode, False)
+    o = oracle.attention(rq.transpose(0, 2, 1, 3), rk.transpose(0, 2, 1, 3), rv.transpose(0, 2, 1, 3))
+    wrong = oracle.reverse_rows(o.transpose(0, 2, 1, 3), k, mode)
+    _assert_close(out, right, "rope-before-permute")
+    assert np.abs(out - wrong).max() > 10 * MAX_ABS
+
+
+# ---------------------------------------------------------------------------
+# Closed-form probes: bit-exact
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T,H,W,heads,d,k,mode,dtype", [
+    (4, 8, 8, 2, 64, 2, oracle.SINGLE, torch.float32),      # the tiny grid, L = 128
+    (4, 8, 16, 3, 128, 4, oracle.GROUP, torch.bfloat16),    # L = 128
+    (4, 8, 16, 3, 128, 4, oracle.SINGLE, torch.bfloat16),
+    (2, 16, 16, 2, 128, 1, oracle.SINGLE, torch.bfloat16),  # dense, L = 512
+])
+def test_uniform_softmax_probe_bit_exact(T, H, W, heads, d, k, mode, dtype):
+    # q = 0 -> every score is exactly 0 -> softmax is exactly uniform over the scope, so
+    # out[n] = mean of v over n's scope.  Small-integer v sums exactly in fp32 and L is a
+    # power of two, so the only rounding is the final one to the output type.
+    N = T * H * W
+    g = torch.Generator().manual_seed(17)
+    v = torch.randint(-4, 5, (1, N, heads, d), generator=g).to(dtype)
+    kk = torch.randn(1, N, heads, d, generator=g).to(dtype)
+    q = torch.zeros_like(kk)
+    out = sk.attn(q.cuda(), kk.cuda(), v.cuda(), (T, H, W), k, mode).cpu()
+    table = oracle.scope_table(N, k, mode)
+    vn = v.double().numpy()
+    want = np.empty_like(vn)
+    for s in range(k):
+        want[0, table[s]] = vn[0, table[s]].mean(axis=0)
+    want_t = torch.from_numpy(want).to(dtype)
+    assert torch.equal(out.view(torch.int16 if dtype == torch.bfloat16 else torch.int32),
+                       want_t.view(torch.int16 if dtype == torch.bfloat16 else torch.int32))
+
+
+@pytest.mark.parametrize("T,H,W,k,mode", [(1, 1, 8, 8, oracle.SINGLE), (1, 4, 16, 64, oracle.SINGLE),
+                                          (1, 1, 64, 8, oracle.GROUP)])
+def test_degenerate_short_scopes(T, H, W, k, mode):
+    # L = N/k tokens per scope; with L = 1 every token only attends to itself -> out == v.
+    heads, d = 2, 128
+    q, kk, v = _inputs(1, T, H, W, heads, d, torch.bfloat16, seed=21)
+    out = sk.attn(q, kk, v, (T, H, W), k, mode)
+    torch.cuda.synchronize()
+    if (T * H * W) // k == 1:
+        assert torch.equal(out.view(torch.int16), v.view(torch.int16))
+    want = oracle.skiparse_attention(_np64(q), _np64(kk), _np64(v), T, H, W, k, mode)
+    _assert_close(_np64(out), want, f"short scopes L={(T * H * W) // k}")
+
+
+def test_attn_deterministic_and_stream_ordered():
+    B, T, H, W, heads, d, k, mode = 1, 6, 10, 12, 4, 128, 2, oracle.GROUP
+    q, kk, v = _inputs(B, T, H, W, heads, d, torch.bfloat16, seed=2)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        a = sk.attn(q, kk, v, (T, H, W), k, mode)
+        b = sk.attn(q, kk, v, (T, H, W), k, mode)
+    s.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_attn_errors_surface_as_exceptions():
+    q = torch.zeros(1, 30, 1, 128, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(sk.SkiparseError) as e:
+        sk.attn(q, q.clone(), q.clone(), (1, 5, 6), 4, oracle.SINGLE)
+    assert e.value.status == sk.E_DIVISIBILITY
+    with pytest.raises(sk.SkiparseError) as e:
+        sk.attn(q, q, q, (1, 5, 6), 2, oracle.SINGLE, out=q)
+    assert e.value.status == sk.E_ALIAS
+
+
+# ---------------------------------------------------------------------------
+# Full-size configurations: sampled rows against the oracle, row by row
+# ---------------------------------------------------------------------------
+
+def _sample_rows(w, rng):
+    """(batch, token) pairs: two scopes (first and last), 12 positions each including the
+    first and last in-scope positions and rows of the ragged last q tile."""
+    table = oracle.scope_table(w.N, w.sparse_k, w.mode)
+    picks_b, picks_t = [], []
+    for b in sorted({0, w.B - 1}):
+        for s in sorted({0, w.sparse_k - 1}):
+            pos = {0, w.L - 1, w.L - 2, (w.L // 256) * 256, w.L // 2}
+            pos |= set(rng.integers(0, w.L, size=7).tolist())
+            for p in sorted(pos):
+                if 0 <= p < w.L:
+                    picks_b.append(b)
+                    picks_t.append(int(table[s, p]))
+    return np.array(picks_b), np.array(picks_t)
+
+
+FULL = [wl.OSP_SINGLE, wl.OSP_GROUP, wl.HC_GROUP, wl.WAN_DENSE, wl.LONG_GROUP, wl.LONG_SINGLE]
+
+
+@pytest.mark.parametrize("w", FULL, ids=[w.name for w in FULL])
+def test_full_size_config_sampled_rows(w):
+    print(f"case {w.name}", flush=True)
+    q, k, v = wl.make_inputs(w, seed=0, device="cpu")
+    qg, kg, vg = q.cuda(), k.cuda(), v.cuda()
+    out = torch.full_like(qg, float("nan"))
+    sk.attn(qg, kg, vg, w.grid, w.sparse_k, w.mode, out=out)
+    torch.cuda.synchronize()
+    assert not torch.isnan(out).any().item(), "some output element was not written"
+    rng = np.random.default_rng(0)
+    b_idx, t_idx = _sample_rows(w, rng)
+    # exact fp32 views of the bf16 inputs; the oracle widens the rows it uses to fp64
+    qn, kn, vn = (x.float().numpy() for x in (q, k, v))
+    want = oracle.skiparse_attention_rows(qn, kn, vn, w.T, w.H, w.W, w.sparse_k, w.mode, b_idx, t_idx)
+    got = out[torch.from_numpy(b_idx).cuda(), torch.from_numpy(t_idx).cuda()]
+    _assert_close(_np64(got), want, f"{w.name} ({len(t_idx)} rows)")
