@@ -73,12 +73,16 @@ __device__ __forceinline__ int row_addr(int row, int byte_in_row) {
 }
 
 // V^T rows: one row of kBN key slots (2*kBN bytes) per head-dim index d.  The
-// 16-byte granule index is XOR-swizzled so that 16 consecutive d rows read at
-// one granule column land in 16 different bank groups of a 256-byte line.
+// 16-byte granule index is XOR-swizzled with bits of d so that both access
+// patterns spread over the bank groups of a 256-byte line: 16 consecutive d
+// rows read at one granule column (the MFMA operand reads) hit 16 different
+// groups, and the staging writes of one key quad to rows d = 8c + 2i for 16
+// consecutive c hit each group at most twice.
 __device__ __forceinline__ int vt_addr(int d, int slot) {
     constexpr int VG = kBN / 8;       // granules per V^T row
     constexpr int RPL = 128 / kBN;    // V^T rows per 256-byte line
-    return d * (kBN * 2) + ((((slot >> 3) ^ ((d / RPL) & (VG - 1)))) << 4) + ((slot & 7) << 1);
+    const int f = ((d / RPL) ^ (d / (RPL * VG))) & (VG - 1);
+    return d * (kBN * 2) + (((slot >> 3) ^ f) << 4) + ((slot & 7) << 1);
 }
 
 // Key quad (keys 4*quad .. 4*quad+3 of a tile) -> its first V^T slot.  Inside each group of 16 keys the
@@ -406,17 +410,34 @@ attn_fwd_kernel(AttnParams a) {
             for (int qb = 0; qb < kQB; ++qb)
 #pragma unroll
                 for (int x = 0; x < 16; ++x) sacc[kb][qb][x] = 0.f;
+        bf16x8 ka[2][KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+            ka[0][kb] = *reinterpret_cast<const bf16x8*>(kcur + row_addr<D>(kb * 32 + l32, hf * 16));
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
+            if (ks + 1 < KS) {
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-                const int row = kb * 32 + l32;
-                const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kcur + row_addr<D>(row, (2 * ks + hf) * 16));
+                for (int kb = 0; kb < KB; ++kb)
+                    ka[(ks + 1) & 1][kb] = *reinterpret_cast<const bf16x8*>(
+                        kcur + row_addr<D>(kb * 32 + l32, (2 * (ks + 1) + hf) * 16));
+            }
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                 for (int qb = 0; qb < kQB; ++qb)
-                    sacc[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[qb][ks], sacc[kb][qb], 0, 0, 0);
-            }
+                    sacc[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks & 1][kb], qreg[qb][ks], sacc[kb][qb], 0, 0, 0);
         }
+        // keep the operand reads one k-step ahead of the MFMAs that consume them
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * KB, 0);
+#pragma unroll
+        for (int i = 0; i < KS - 1; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, KB * kQB, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, KB, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, KB * kQB, 0);
+        __builtin_amdgcn_s_setprio(0);
 
         // keys past the end of the scope (last tile only)
         if (j == nt - 1 && (a.L % kBN) != 0) {
@@ -488,17 +509,34 @@ attn_fwd_kernel(AttnParams a) {
             l_part[qb] = lsum;
         }
 
-        // O^T += V^T P^T
+        // O^T += V^T P^T, V operands prefetched one step ahead
+        bf16x8 va[2][DB];
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+            va[0][db] = *reinterpret_cast<const bf16x8*>(vcur + vt_addr(db * 32 + l32, hf * 8));
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
+            if (kk + 1 < KK) {
 #pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                const bf16x8 va = *reinterpret_cast<const bf16x8*>(vcur + vt_addr(db * 32 + l32, kk * 16 + hf * 8));
+                for (int db = 0; db < DB; ++db)
+                    va[(kk + 1) & 1][db] = *reinterpret_cast<const bf16x8*>(
+                        vcur + vt_addr(db * 32 + l32, (kk + 1) * 16 + hf * 8));
+            }
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
 #pragma unroll
                 for (int qb = 0; qb < kQB; ++qb)
-                    o[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[qb][kk], o[db][qb], 0, 0, 0);
-            }
+                    o[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[kk & 1][db], pb[qb][kk], o[db][qb], 0, 0, 0);
         }
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * DB, 0);
+#pragma unroll
+        for (int i = 0; i < KK - 1; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, DB * kQB, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, DB, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, DB * kQB, 0);
+        __builtin_amdgcn_s_setprio(0);
 
         if (has_next) store_tile(cur ^ 1, j + 1);
         __syncthreads();
