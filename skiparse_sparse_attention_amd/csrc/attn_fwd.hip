@@ -107,21 +107,6 @@ struct ChunkRaw {
     uint32_t w[kDwords];
 };
 
-template <int NDW>
-__device__ __forceinline__ void load_dwords(const void* p, uint32_t (&w)[NDW]) {
-    if constexpr (NDW == 2) {
-        const u32x2 v = *reinterpret_cast<const u32x2*>(p);
-        w[0] = v[0]; w[1] = v[1];
-    } else {
-        static_assert(NDW % 4 == 0, "chunk must be a multiple of 16 bytes");
-#pragma unroll
-        for (int i = 0; i < NDW / 4; ++i) {
-            const u32x4 v = reinterpret_cast<const u32x4*>(p)[i];
-            w[4 * i] = v[0]; w[4 * i + 1] = v[1]; w[4 * i + 2] = v[2]; w[4 * i + 3] = v[3];
-        }
-    }
-}
-
 template <typename E, int CH>
 __device__ __forceinline__ void raw_to_f32(const ChunkRaw<E, CH>& r, float (&x)[CH]) {
     if constexpr (E::kBytes == 2) {
@@ -136,17 +121,55 @@ __device__ __forceinline__ void raw_to_f32(const ChunkRaw<E, CH>& r, float (&x)[
     }
 }
 
-// Raw element storage of 8 consecutive elements of E, as 4 dwords of bf16 pairs.
+
+// Buffer loads of one RoPE chunk (CH elements of E) as dwords.
+template <int NDW>
+__device__ __forceinline__ void buffer_load_dwords(__amdgpu_buffer_rsrc_t r, int off, uint32_t (&w)[NDW]) {
+    if constexpr (NDW == 2) {
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+        w[0] = v[0]; w[1] = v[1];
+    } else {
+        static_assert(NDW % 4 == 0, "chunk must be a multiple of 16 bytes");
+#pragma unroll
+        for (int i = 0; i < NDW / 4; ++i) {
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16 * i, 0, 0);
+            w[4 * i] = v[0]; w[4 * i + 1] = v[1]; w[4 * i + 2] = v[2]; w[4 * i + 3] = v[3];
+        }
+    }
+}
+
+// 8 consecutive elements of E as 4 dwords of bf16 pairs (fp32 is rounded to bf16).
 template <typename E>
-__device__ __forceinline__ void load_8_as_bf16x2(const void* p, uint32_t (&w)[4]) {
+__device__ __forceinline__ void buffer_load_8_as_bf16x2(__amdgpu_buffer_rsrc_t r, int off, uint32_t (&w)[4]) {
     if constexpr (E::kBytes == 2) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
         w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
     } else {
-        const f32x4 a = reinterpret_cast<const f32x4*>(p)[0];
-        const f32x4 b = reinterpret_cast<const f32x4*>(p)[1];
-        w[0] = pack_bf16x2(a[0], a[1]); w[1] = pack_bf16x2(a[2], a[3]);
-        w[2] = pack_bf16x2(b[0], b[1]); w[3] = pack_bf16x2(b[2], b[3]);
+        const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+        const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 0);
+        w[0] = pack_bf16x2(__uint_as_float(a[0]), __uint_as_float(a[1]));
+        w[1] = pack_bf16x2(__uint_as_float(a[2]), __uint_as_float(a[3]));
+        w[2] = pack_bf16x2(__uint_as_float(b[0]), __uint_as_float(b[1]));
+        w[3] = pack_bf16x2(__uint_as_float(b[2]), __uint_as_float(b[3]));
+    }
+}
+
+// Round a rotated chunk pair to bf16 and write it to its (swizzled) places in an LDS row.
+template <int D, int CH, int CB>
+__device__ __forceinline__ void store_rotated_chunks(char* base, int row, const RopePair& rp,
+                                                     const float (&x1)[CH], const float (&x2)[CH]) {
+    uint32_t w1[CH / 2], w2[CH / 2];
+#pragma unroll
+    for (int i = 0; i < CH / 2; ++i) {
+        w1[i] = pack_bf16x2(x1[2 * i], x1[2 * i + 1]);
+        w2[i] = pack_bf16x2(x2[2 * i], x2[2 * i + 1]);
+    }
+    if constexpr (CH == 8) {
+        *reinterpret_cast<u32x4*>(base + row_addr<D>(row, rp.c1 * CB)) = u32x4{w1[0], w1[1], w1[2], w1[3]};
+        *reinterpret_cast<u32x4*>(base + row_addr<D>(row, rp.c2 * CB)) = u32x4{w2[0], w2[1], w2[2], w2[3]};
+    } else {
+        *reinterpret_cast<u32x2*>(base + row_addr<D>(row, rp.c1 * CB)) = u32x2{w1[0], w1[1]};
+        *reinterpret_cast<u32x2*>(base + row_addr<D>(row, rp.c2 * CB)) = u32x2{w2[0], w2[1]};
     }
 }
 
@@ -166,6 +189,10 @@ attn_fwd_kernel(AttnParams a) {
     constexpr int KS = D / 16;   // 16-deep k-steps of Q K^T
     constexpr int DB = D / 32;   // 32-row blocks of O^T
     constexpr int VCH = D / 8;   // 8-element d-chunks per V row
+    constexpr int KB = kBN / 32; // 32-key blocks of S^T
+    constexpr int KK = kBN / 16; // 16-deep k-steps of P V
+    constexpr int ES = E::kBytes;
+    constexpr int kOOB = 1 << 30;  // buffer offset past every record (slices are < 2^30 bytes): loads read 0, stores drop
     float2* tab = reinterpret_cast<float2*>(lds + L::kTabOff);
 
     const int tid = threadIdx.x;
@@ -181,8 +208,19 @@ attn_fwd_kernel(AttnParams a) {
     const int head = bh % a.heads;
     const int b = bh / a.heads;
     const int64_t k_ = a.sparse_k;
-    const int64_t row_stride = (int64_t)a.heads * D;                      // elements per token
-    const int64_t batch_head_off = (int64_t)b * a.N * row_stride + (int64_t)head * D;
+    const int row_bytes = a.heads * D * ES;                 // bytes per token
+    // Buffer descriptors over this (batch, head) slice: offsets are token*row_bytes + byte
+    // in the head row; an offset of kOOB reads zeros / drops the store.
+    const int64_t slice = ((int64_t)b * a.N * a.heads + head) * D * ES;
+    const int slice_bytes = a.N * row_bytes - head * D * ES;
+    const __amdgpu_buffer_rsrc_t qbuf = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(reinterpret_cast<const char*>(a.q) + slice), (short)0, slice_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t kbuf = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(reinterpret_cast<const char*>(a.k) + slice), (short)0, slice_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vbuf = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(reinterpret_cast<const char*>(a.v) + slice), (short)0, slice_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t obuf = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(reinterpret_cast<char*>(a.out) + slice), (short)0, slice_bytes, 0x00020000);
     const int HW = a.H * a.W;
 
     build_rope_table<D>(tab, a.T, a.H, a.W);
@@ -197,36 +235,18 @@ attn_fwd_kernel(AttnParams a) {
         for (int it = 0; it < kBM * 8 / kThreads; ++it) {
             const int r = (tid >> 3) + it * (kThreads / 8);
             const int p = p0 + r;
+            const bool valid = p < a.L;
+            const int n = valid ? (int)scope_token(p, s, k_, a.mode) : 0;
+            const int off = valid ? n * row_bytes : kOOB;
+            ChunkRaw<E, CH> r1, r2;
+            buffer_load_dwords(qbuf, off + rp.c1 * CH * ES, r1.w);
+            buffer_load_dwords(qbuf, off + rp.c2 * CH * ES, r2.w);
             float x1[CH], x2[CH];
-            if (p < a.L) {
-                const int64_t n = scope_token(p, s, k_, a.mode);
-                const char* src = reinterpret_cast<const char*>(a.q) +
-                                  (batch_head_off + n * row_stride) * E::kBytes;
-                ChunkRaw<E, CH> r1, r2;
-                load_dwords(src + rp.c1 * CH * E::kBytes, r1.w);
-                load_dwords(src + rp.c2 * CH * E::kBytes, r2.w);
-                raw_to_f32(r1, x1);
-                raw_to_f32(r2, x2);
-                const int nn = (int)n;
-                const int pos = rp.axis == 0 ? nn / HW : (rp.axis == 1 ? (nn / a.W) % a.H : nn % a.W);
-                rope_rotate<CH>(x1, x2, tab + rope_row<D>(rp.axis, pos, a.T, a.H) + rp.jchunk * CH);
-            } else {
-#pragma unroll
-                for (int e = 0; e < CH; ++e) { x1[e] = 0.f; x2[e] = 0.f; }
-            }
-            uint32_t w1[CH / 2], w2[CH / 2];
-#pragma unroll
-            for (int i = 0; i < CH / 2; ++i) {
-                w1[i] = pack_bf16x2(x1[2 * i], x1[2 * i + 1]);
-                w2[i] = pack_bf16x2(x2[2 * i], x2[2 * i + 1]);
-            }
-            if constexpr (CH == 8) {
-                *reinterpret_cast<u32x4*>(lds + row_addr<D>(r, rp.c1 * CB)) = u32x4{w1[0], w1[1], w1[2], w1[3]};
-                *reinterpret_cast<u32x4*>(lds + row_addr<D>(r, rp.c2 * CB)) = u32x4{w2[0], w2[1], w2[2], w2[3]};
-            } else {
-                *reinterpret_cast<u32x2*>(lds + row_addr<D>(r, rp.c1 * CB)) = u32x2{w1[0], w1[1]};
-                *reinterpret_cast<u32x2*>(lds + row_addr<D>(r, rp.c2 * CB)) = u32x2{w2[0], w2[1]};
-            }
+            raw_to_f32(r1, x1);
+            raw_to_f32(r2, x2);
+            const int pos = rp.axis == 0 ? n / HW : (rp.axis == 1 ? (n / a.W) % a.H : n % a.W);
+            rope_rotate<CH>(x1, x2, tab + rope_row<D>(rp.axis, pos, a.T, a.H) + rp.jchunk * CH);
+            store_rotated_chunks<D, CH, CB>(lds, r, rp, x1, x2);
         }
     }
     __syncthreads();
@@ -240,22 +260,25 @@ attn_fwd_kernel(AttnParams a) {
     }
     __syncthreads();  // the Q area is reused by the K/V buffers below
 
-    // ---- per-thread staging assignment: NKR key rows (K) and one key quad (V) ----
-    constexpr int NKR = kBN * 8 / kThreads;   // K rows staged per thread per tile
-    constexpr int KB = kBN / 32;              // 32-key blocks of S^T
-    constexpr int KK = kBN / 16;              // 16-deep k-steps of P V
-    const int kcp = tid & 7;
-    const RopePair krp = rope_pair(kcp);
-    const int vquad = tid / VCH;              // keys 4*vquad .. 4*vquad+3
-    const int vdc = tid % VCH;                // d = 8*vdc .. 8*vdc+7
-    const bool v_active = tid < (kBN / 4) * VCH;
-    const int vslot = key_slot_quad(vquad & (kBN / 4 - 1));
-    auto krow = [&](int i) { return (tid >> 3) + i * (kThreads / 8); };
+    // ---- per-thread staging assignment ----
+    // K: one (key row, RoPE chunk pair) task per thread.
+    // V: one (key pair, 8-element d chunk) task per thread; lanes 0..31 of a wave
+    //    take the 32 key pairs of one d chunk, so the transposed 4-byte LDS writes
+    //    of 16 consecutive lanes fill 64 contiguous bytes of one V^T row.
+    static_assert(kBN * 8 == kThreads, "one K staging task per thread");
+    constexpr int VPAIRS = kBN / 2;
+    constexpr int VTASKS = VPAIRS * VCH;
+    static_assert(VTASKS <= kThreads, "at most one V staging task per thread");
+    const int krow = tid >> 3;
+    const RopePair krp = rope_pair(tid & 7);
+    const int vpair = tid % VPAIRS;
+    const int vdc = tid / VPAIRS;
+    const bool v_active = VTASKS == kThreads || tid < VTASKS;
+    const int vslot = key_slot_quad(vpair >> 1) + (vpair & 1) * 2;
 
-    // token index and grid position of each staged key row, advanced per tile
-    int kn[NKR];
-    Pos kpos[NKR];
-    int vn[4];
+    // token of each staged key row (as a byte offset) and grid position of the K row
+    int koff, voff[2];
+    Pos kpos;
     const int tile_dn = kBN * a.sparse_k;     // token advance per tile when k | kBN
     const int dt = tile_dn / HW, rem = tile_dn % HW;
     const int dh = rem / a.W, dw = rem % a.W;
@@ -264,108 +287,67 @@ attn_fwd_kernel(AttnParams a) {
         q.t = nn / HW; q.h = (nn / a.W) % a.H; q.w = nn % a.W;
         return q;
     };
+    auto set_rows = [&](int p0) {
+        const int kn = (int)scope_token(p0 + krow, s, k_, a.mode);
+        koff = kn * row_bytes;
+        kpos = pos_of(kn);
 #pragma unroll
-    for (int i = 0; i < NKR; ++i) {
-        kn[i] = (int)scope_token(krow(i), s, k_, a.mode);
-        kpos[i] = pos_of(kn[i]);
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) vn[e] = (int)scope_token(4 * vquad + e, s, k_, a.mode);
-
+        for (int e = 0; e < 2; ++e) voff[e] = (int)scope_token(p0 + 2 * vpair + e, s, k_, a.mode) * row_bytes;
+    };
+    set_rows(0);
     auto advance_rows = [&](int tile) {
         if (a.k_divides_bn) {
             // n(p + kBN) = n(p) + kBN*k in both modes when k divides kBN
-#pragma unroll
-            for (int i = 0; i < NKR; ++i) {
-                kn[i] += tile_dn;
-                int w = kpos[i].w + dw, c = w >= a.W;
-                kpos[i].w = w - (c ? a.W : 0);
-                int h = kpos[i].h + dh + c;
-                c = h >= a.H;
-                kpos[i].h = h - (c ? a.H : 0);
-                kpos[i].t += dt + c;
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) vn[e] += tile_dn;
+            koff += tile_dn * row_bytes;
+            int w = kpos.w + dw, c = w >= a.W;
+            kpos.w = w - (c ? a.W : 0);
+            int h = kpos.h + dh + c;
+            c = h >= a.H;
+            kpos.h = h - (c ? a.H : 0);
+            kpos.t += dt + c;
+            voff[0] += tile_dn * row_bytes;
+            voff[1] += tile_dn * row_bytes;
         } else {
-            const int p0 = tile * kBN;
-#pragma unroll
-            for (int i = 0; i < NKR; ++i) {
-                kn[i] = (int)scope_token(p0 + krow(i), s, k_, a.mode);
-                kpos[i] = pos_of(kn[i]);
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) vn[e] = (int)scope_token(p0 + 4 * vquad + e, s, k_, a.mode);
+            set_rows(tile * kBN);
         }
     };
 
-    ChunkRaw<E, CH> kraw[NKR][2];
-    uint32_t vraw[4][4];
-    const char* kbase = reinterpret_cast<const char*>(a.k) + batch_head_off * E::kBytes;
-    const char* vbase = reinterpret_cast<const char*>(a.v) + batch_head_off * E::kBytes;
-
+    ChunkRaw<E, CH> kraw[2];
+    uint32_t vraw[2][4];
     auto load_tile = [&](int tile) {
         const int p0 = tile * kBN;
-#pragma unroll
-        for (int i = 0; i < NKR; ++i) {
-            if (p0 + krow(i) < a.L) {
-                const char* src = kbase + (int64_t)kn[i] * row_stride * E::kBytes;
-                load_dwords(src + krp.c1 * CH * E::kBytes, kraw[i][0].w);
-                load_dwords(src + krp.c2 * CH * E::kBytes, kraw[i][1].w);
-            } else {
-#pragma unroll
-                for (int x = 0; x < ChunkRaw<E, CH>::kDwords; ++x) { kraw[i][0].w[x] = 0u; kraw[i][1].w[x] = 0u; }
-            }
-        }
+        const int ko = p0 + krow < a.L ? koff : kOOB;
+        buffer_load_dwords(kbuf, ko + krp.c1 * CH * ES, kraw[0].w);
+        buffer_load_dwords(kbuf, ko + krp.c2 * CH * ES, kraw[1].w);
         if (v_active) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                if (p0 + 4 * vquad + e < a.L) {
-                    load_8_as_bf16x2<E>(vbase + ((int64_t)vn[e] * row_stride + vdc * 8) * E::kBytes, vraw[e]);
-                } else {
-                    vraw[e][0] = vraw[e][1] = vraw[e][2] = vraw[e][3] = 0u;
-                }
+            for (int e = 0; e < 2; ++e) {
+                const int vo = p0 + 2 * vpair + e < a.L ? voff[e] : kOOB;
+                buffer_load_8_as_bf16x2<E>(vbuf, vo + vdc * 8 * ES, vraw[e]);
             }
         }
     };
 
     auto store_tile = [&](int buf, int tile) {
         char* kdst = lds + L::kKOff + buf * L::kKTile;
-#pragma unroll
-        for (int i = 0; i < NKR; ++i) {
-            float x1[CH], x2[CH];
-            raw_to_f32(kraw[i][0], x1);
-            raw_to_f32(kraw[i][1], x2);
-            // rows past the end of the scope hold zeros; their (out-of-grid) position is not looked up
-            const bool valid = tile * kBN + krow(i) < a.L;
-            const int pos = !valid ? 0 : (krp.axis == 0 ? kpos[i].t : (krp.axis == 1 ? kpos[i].h : kpos[i].w));
-            rope_rotate<CH>(x1, x2, tab + rope_row<D>(krp.axis, pos, a.T, a.H) + krp.jchunk * CH);
-            uint32_t w1[CH / 2], w2[CH / 2];
-#pragma unroll
-            for (int j = 0; j < CH / 2; ++j) {
-                w1[j] = pack_bf16x2(x1[2 * j], x1[2 * j + 1]);
-                w2[j] = pack_bf16x2(x2[2 * j], x2[2 * j + 1]);
-            }
-            if constexpr (CH == 8) {
-                *reinterpret_cast<u32x4*>(kdst + row_addr<D>(krow(i), krp.c1 * CB)) = u32x4{w1[0], w1[1], w1[2], w1[3]};
-                *reinterpret_cast<u32x4*>(kdst + row_addr<D>(krow(i), krp.c2 * CB)) = u32x4{w2[0], w2[1], w2[2], w2[3]};
-            } else {
-                *reinterpret_cast<u32x2*>(kdst + row_addr<D>(krow(i), krp.c1 * CB)) = u32x2{w1[0], w1[1]};
-                *reinterpret_cast<u32x2*>(kdst + row_addr<D>(krow(i), krp.c2 * CB)) = u32x2{w2[0], w2[1]};
-            }
-        }
+        float x1[CH], x2[CH];
+        raw_to_f32(kraw[0], x1);
+        raw_to_f32(kraw[1], x2);
+        // rows past the end of the scope hold zeros; their (out-of-grid) position is not looked up
+        const bool valid = tile * kBN + krow < a.L;
+        const int pos = !valid ? 0 : (krp.axis == 0 ? kpos.t : (krp.axis == 1 ? kpos.h : kpos.w));
+        rope_rotate<CH>(x1, x2, tab + rope_row<D>(krp.axis, pos, a.T, a.H) + krp.jchunk * CH);
+        store_rotated_chunks<D, CH, CB>(kdst, krow, krp, x1, x2);
         if (v_active) {
             char* vdst = lds + L::kVOff + buf * L::kVTile;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 // dword i of each key row holds d = 8*vdc + 2i (low half) and + 2i + 1 (high half)
-                const uint32_t lo01 = __builtin_amdgcn_perm(vraw[1][i], vraw[0][i], 0x05040100u);
-                const uint32_t lo23 = __builtin_amdgcn_perm(vraw[3][i], vraw[2][i], 0x05040100u);
-                const uint32_t hi01 = __builtin_amdgcn_perm(vraw[1][i], vraw[0][i], 0x07060302u);
-                const uint32_t hi23 = __builtin_amdgcn_perm(vraw[3][i], vraw[2][i], 0x07060302u);
+                const uint32_t lo = __builtin_amdgcn_perm(vraw[1][i], vraw[0][i], 0x05040100u);
+                const uint32_t hi = __builtin_amdgcn_perm(vraw[1][i], vraw[0][i], 0x07060302u);
                 const int d = 8 * vdc + 2 * i;
-                *reinterpret_cast<u32x2*>(vdst + vt_addr(d, vslot)) = u32x2{lo01, lo23};
-                *reinterpret_cast<u32x2*>(vdst + vt_addr(d + 1, vslot)) = u32x2{hi01, hi23};
+                *reinterpret_cast<uint32_t*>(vdst + vt_addr(d, vslot)) = lo;
+                *reinterpret_cast<uint32_t*>(vdst + vt_addr(d + 1, vslot)) = hi;
             }
         }
     };
@@ -550,23 +532,22 @@ attn_fwd_kernel(AttnParams a) {
         const float lsum = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
         const float inv = 1.0f / lsum;
         const int p = qt * kBM + (wave * kQB + qb) * 32 + l32;
-        if (p < a.L) {
-            const int64_t n = scope_token(p, s, k_, a.mode);
-            char* dst = reinterpret_cast<char*>(a.out) + (batch_head_off + n * row_stride) * E::kBytes;
+        const int off = p < a.L ? (int)scope_token(p, s, k_, a.mode) * row_bytes : kOOB;
 #pragma unroll
-            for (int db = 0; db < DB; ++db)
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int d0 = db * 32 + 8 * g + 4 * hf;
-                    const float y0 = o[db][qb][4 * g] * inv, y1 = o[db][qb][4 * g + 1] * inv;
-                    const float y2 = o[db][qb][4 * g + 2] * inv, y3 = o[db][qb][4 * g + 3] * inv;
-                    if constexpr (E::kBytes == 2) {
-                        *reinterpret_cast<u32x2*>(dst + d0 * 2) = u32x2{pack_bf16x2(y0, y1), pack_bf16x2(y2, y3)};
-                    } else {
-                        *reinterpret_cast<f32x4*>(dst + d0 * 4) = f32x4{y0, y1, y2, y3};
-                    }
+            for (int g = 0; g < 4; ++g) {
+                const int d0 = db * 32 + 8 * g + 4 * hf;
+                const float y0 = o[db][qb][4 * g] * inv, y1 = o[db][qb][4 * g + 1] * inv;
+                const float y2 = o[db][qb][4 * g + 2] * inv, y3 = o[db][qb][4 * g + 3] * inv;
+                if constexpr (ES == 2) {
+                    const u32x2 v2 = {pack_bf16x2(y0, y1), pack_bf16x2(y2, y3)};
+                    __builtin_amdgcn_raw_buffer_store_b64(v2, obuf, off + d0 * 2, 0, 0);
+                } else {
+                    const u32x4 v4 = {__float_as_uint(y0), __float_as_uint(y1), __float_as_uint(y2), __float_as_uint(y3)};
+                    __builtin_amdgcn_raw_buffer_store_b128(v4, obuf, off + d0 * 4, 0, 0);
                 }
-        }
+            }
     }
 }
 

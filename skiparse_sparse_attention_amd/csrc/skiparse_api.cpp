@@ -16,6 +16,7 @@ using skiparse::kGroup;
 using skiparse::kSingle;
 
 constexpr int64_t kI32Max = std::numeric_limits<int32_t>::max();
+constexpr int64_t kAttnSlabMax = (int64_t(1) << 30) - (int64_t(1) << 16);
 
 struct Dims {
     int64_t N = 0, L = 0, elems = 0, bytes = 0;
@@ -75,6 +76,8 @@ int skiparse_validate(const void* q, const void* k, const void* v, int B, int T,
     Dims d;
     const int st = check_dims(B, T, H, W, heads, head_dim, sparse_k, mode, dtype, &d);
     if (st != SKIPARSE_OK) return st;
+    // the attention kernel addresses one batch's (N, heads, head_dim) slab with 32-bit offsets
+    if (d.N * heads * head_dim * d.esize > kAttnSlabMax) return SKIPARSE_E_UNSUPPORTED;
     if (overlaps(out, q, d.bytes) || overlaps(out, k, d.bytes) || overlaps(out, v, d.bytes))
         return SKIPARSE_E_ALIAS;
     return SKIPARSE_OK;

@@ -82,6 +82,12 @@ def test_validate_rejects(kw, status):
     assert _validate(**kw) == status
 
 
+def test_attn_rejects_slabs_beyond_32bit_offsets():
+    # 1 batch x 65536 tokens x 64 heads x 128 x 2 bytes = 1 GiB > the per-batch limit
+    L = sk.lib()
+    assert L.skiparse_attn(Q, K, V, 1, 16, 64, 64, 64, 128, 1, 0, 0, OUT, None) == sk.E_UNSUPPORTED
+
+
 def test_attn_rejects_before_any_device_call():
     # invalid calls must return their code without touching the (absent) GPU
     L = sk.lib()
