@@ -81,9 +81,10 @@ enum skiparse_status {
  *           order; must not overlap q, k or v.
  * sparse_k: number of scopes k >= 1 (Single: N % k == 0; Group: N % k^2 == 0).
  * head_dim: 64 or 128.
- * Limit: one batch's slab, N*heads*head_dim*sizeof(dtype), must be below
- * 2^30 - 2^16 bytes (the kernel addresses it with 32-bit offsets); larger
- * inputs return SKIPARSE_E_UNSUPPORTED.
+ * Limit: the kernel addresses one batch's (N, heads, head_dim) slab with
+ * 32-bit byte offsets, so (N + 256*k + k^2) * heads*head_dim*sizeof(dtype)
+ * + 4096 must stay below 2^31 (about 2 GiB per batch); larger inputs return
+ * SKIPARSE_E_UNSUPPORTED.
  * One kernel launch.  The rearranged q, k, v are never written to memory:
  * each tile load gathers its scope's rows and rotates them on the fly, and
  * the epilogue writes each output row straight to its original token index.

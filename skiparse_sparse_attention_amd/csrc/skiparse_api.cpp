@@ -16,7 +16,6 @@ using skiparse::kGroup;
 using skiparse::kSingle;
 
 constexpr int64_t kI32Max = std::numeric_limits<int32_t>::max();
-constexpr int64_t kAttnSlabMax = (int64_t(1) << 30) - (int64_t(1) << 16);
 
 struct Dims {
     int64_t N = 0, L = 0, elems = 0, bytes = 0;
@@ -76,8 +75,12 @@ int skiparse_validate(const void* q, const void* k, const void* v, int B, int T,
     Dims d;
     const int st = check_dims(B, T, H, W, heads, head_dim, sparse_k, mode, dtype, &d);
     if (st != SKIPARSE_OK) return st;
-    // the attention kernel addresses one batch's (N, heads, head_dim) slab with 32-bit offsets
-    if (d.N * heads * head_dim * d.esize > kAttnSlabMax) return SKIPARSE_E_UNSUPPORTED;
+    // The attention kernel addresses one batch's (N, heads, head_dim) slab with 32-bit
+    // offsets token*row_bytes; tokens of rows past the end of a scope (up to one
+    // workgroup of queries beyond L) reach N + 256*k + k^2.
+    const int64_t row_bytes = (int64_t)heads * head_dim * d.esize;
+    if ((d.N + 256 * (int64_t)sparse_k + (int64_t)sparse_k * sparse_k) * row_bytes + 4096 > kI32Max)
+        return SKIPARSE_E_UNSUPPORTED;
     if (overlaps(out, q, d.bytes) || overlaps(out, k, d.bytes) || overlaps(out, v, d.bytes))
         return SKIPARSE_E_ALIAS;
     return SKIPARSE_OK;

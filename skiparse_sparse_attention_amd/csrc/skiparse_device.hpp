@@ -38,8 +38,11 @@ __device__ __forceinline__ uint16_t float_to_bf16_bits(float f) {
     return __builtin_bit_cast(uint16_t, h);
 }
 
+// Two floats -> one dword of two bf16 (low half = lo), one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return (uint32_t)float_to_bf16_bits(lo) | ((uint32_t)float_to_bf16_bits(hi) << 16);
+    typedef float f32x2v __attribute__((ext_vector_type(2)));
+    const f32x2v v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 // ---------------------------------------------------------------------------

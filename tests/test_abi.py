@@ -83,9 +83,12 @@ def test_validate_rejects(kw, status):
 
 
 def test_attn_rejects_slabs_beyond_32bit_offsets():
-    # 1 batch x 65536 tokens x 64 heads x 128 x 2 bytes = 1 GiB > the per-batch limit
+    # 1 batch x 131072 tokens x 64 heads x 128 x 2 bytes = 2 GiB > the 32-bit offset range
     L = sk.lib()
-    assert L.skiparse_attn(Q, K, V, 1, 16, 64, 64, 64, 128, 1, 0, 0, OUT, None) == sk.E_UNSUPPORTED
+    assert L.skiparse_attn(Q, K, V, 1, 32, 64, 64, 64, 128, 1, 0, 0, OUT, None) == sk.E_UNSUPPORTED
+    # a huge k pushes the tokens of out-of-scope rows (up to N + 256k + k^2) past the range
+    assert L.skiparse_validate(Q, K, V, 1, 64, 32, 32, 8, 128, 65536, 0, 0, OUT) == sk.E_UNSUPPORTED
+    assert L.skiparse_validate(Q, K, V, 1, 64, 32, 32, 8, 128, 256, 0, 0, OUT) == sk.OK
 
 
 def test_attn_rejects_before_any_device_call():
