@@ -68,10 +68,10 @@ enum skiparse_status {
     SKIPARSE_E_DEVICE = 6         /* a HIP call failed (launch error, no device, ...)        */
 };
 
-/* Largest number of (cos, sin) pairs of one 3D-RoPE table,
- * T*d_t/2 + H*d_h/2 + W*d_w/2; larger grids return SKIPARSE_E_UNSUPPORTED.
- * (At head_dim 128: 16*T + 24*H + 24*W <= 6144.) */
-#define SKIPARSE_MAX_ROPE_PAIRS 6144
+/* Largest T + H + W: every kernel keeps a 3D-RoPE cos/sin table with one row per
+ * axis position in LDS (the attention kernel: 256 bytes per row, beside its K/V tile
+ * buffers).  Larger grids return SKIPARSE_E_UNSUPPORTED. */
+#define SKIPARSE_MAX_GRID_SUM 192
 
 /*
  * skiparse_attn -- the fused Skiparse attention forward (steps 1-4 above).

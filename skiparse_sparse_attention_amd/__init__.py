@@ -17,7 +17,7 @@ from ._lib import (  # noqa: F401
     FP32,
     GROUP,
     LIB_PATH,
-    MAX_ROPE_PAIRS,
+    MAX_GRID_SUM,
     OK,
     SINGLE,
     SkiparseError,

@@ -27,7 +27,7 @@ E_UNSUPPORTED = 4
 E_ALIAS = 5
 E_DEVICE = 6
 
-MAX_ROPE_PAIRS = 6144
+MAX_GRID_SUM = 192
 
 _lib = None
 

@@ -23,22 +23,30 @@
 //     swap with the lane 32 away;
 //   * P^T (bf16) is fed to O^T += V^T P^T straight from the accumulator
 //     registers as the B operand.  The MFMA contracts over whatever key order
-//     the operand slots carry, so V is staged transposed in LDS with its keys
-//     in exactly the slot order in which P^T's accumulator layout holds them;
-//   * online softmax in fp32 with exp2 and log2(e)/sqrt(d) folded into one FMA;
-//     the row sum is accumulated from the bf16 P pairs with a 2-way dot
+//     the operand slots carry; V is staged row-major (a plain copy) and its
+//     V^T operands are read with the LDS transpose read ds_read_b64_tr_b16,
+//     whose per-lane addresses pick the keys in exactly the slot order in which
+//     P^T's accumulator layout holds them;
+//   * online softmax in fp32 on exp2: the scale log2(e)/sqrt(d) is folded into q
+//     before its bf16 rounding and the QK MFMAs accumulate onto -m_ref, so the
+//     scores arrive already shifted and each weight costs one v_exp_f32.  The
+//     row sum is accumulated from the bf16 P pairs with a 2-way dot
 //     instruction, so it sums exactly the weights the PV product uses.  The
-//     running maximum is only moved when a tile raises it by more than 2^8 in
-//     the exponent (the result is identical up to rounding, since the same
-//     maximum is used for numerator and denominator), which skips most
-//     rescales of the O^T accumulator;
-//   * K and V^T are double-buffered in LDS with padded row pitches (one extra
-//     16-byte granule per row), which keeps the 16-lane access groups of both
-//     the MFMA operand reads and the staging writes on distinct bank groups
-//     while every LDS address stays "lane base + immediate"; the tile loop is
-//     unrolled by two so the buffer index is a compile-time constant;
-//   * the next tile's rows are fetched into registers before the current
-//     tile's MFMAs so global latency hides behind the math;
+//     reference maximum m_ref is set from the first tile and afterwards only
+//     moved when a tile exceeds it by more than 2^8 (the result is identical up
+//     to rounding, since the same reference scales numerator and denominator),
+//     which skips almost every rescale of the O^T accumulator;
+//   * the two wavefronts of each SIMD run the per-tile blocks (QK MFMAs,
+//     softmax VALU, PV MFMAs, staging VALU) in a ping-pong: one half of the
+//     workgroup runs the iteration rotated by two blocks, so one wave's MFMA
+//     blocks coincide with the other's VALU blocks.  K and V^T tiles are
+//     triple-buffered in LDS, which keeps one barrier per tile sufficient;
+//   * LDS rows have padded pitches (one extra 16-byte granule per row), which
+//     keeps the 16-lane access groups of both the MFMA operand reads and the
+//     staging writes on distinct bank groups with plain "base + offset"
+//     addressing;
+//   * the next tile's rows are fetched into registers at the start of each
+//     iteration so global latency hides behind the math;
 //   * all global traffic uses buffer instructions with 32-bit offsets into the
 //     (batch, head) slice; rows past the end of a scope have token indices
 //     >= N, i.e. offsets past the slice, which the hardware range check turns
@@ -62,25 +70,75 @@ constexpr float kRescaleLog2 = 8.0f;
 
 template <int D>
 struct Lds {
-    static constexpr int kRowPitch = D * 2 + 16;          // Q / K rows (bf16) + pad granule
-    static constexpr int kVtPitch = kBN * 2 + 16;         // V^T rows (kBN bf16 slots) + pad granule
+    static constexpr int kRowPitch = D * 2;               // Q / K rows (bf16), granules swizzled
+    static constexpr int kVPitch = D * 2 + 64;            // V rows (bf16) + four pad granules
     static constexpr int kKTile = kBN * kRowPitch;
-    static constexpr int kVTile = D * kVtPitch;
+    static constexpr int kVTile = kBN * kVPitch;
+    static constexpr int kBufs = 3;                       // K/V tiles in flight (see the schedule)
     static constexpr int kKOff = 0;
-    static constexpr int kVOff = 2 * kKTile;
-    static constexpr int kTiles = 2 * kKTile + 2 * kVTile;
+    static constexpr int kVOff = kBufs * kKTile;
+    static constexpr int kTiles = kBufs * (kKTile + kVTile);
     static constexpr int kQBytes = kBM * kRowPitch;       // Q staging, aliases the tiles
     static constexpr int kTabOff = kTiles > kQBytes ? kTiles : kQBytes;
+    static constexpr int kTabRow = 256;                   // bytes per RoPE table row
 };
 
-// Key quad (keys 4*quad .. 4*quad+3 of a tile) -> its first V^T slot.  Inside
-// each group of 16 keys the slot order is keys [0-3, 8-11, 4-7, 12-15]: the
-// order in which the 32x32 accumulator layout hands P^T's keys to the lanes of
-// a 16-deep MFMA step (lanes 0-31 hold keys {0-3, 8-11}, lanes 32-63 hold
-// {4-7, 12-15}).
-__device__ __forceinline__ int key_slot_quad(int quad) {
-    const int m = quad & 3;
-    return (quad >> 2) * 16 + ((((m & 1) << 1) | (m >> 1)) << 2);
+// Q and K rows in LDS hold the 16-byte granules of a row in a permuted order:
+//  * RoPE chunk pair cp (first-half chunk c1, partner c2) is stored in chunk slots cp and
+//    8 + cp, so the partners sit in opposite halves of the row (Q and K use the same order,
+//    and Q K^T contracts over head_dim in any order);
+//  * granule g of row r is then stored at granule g ^ kswz(r).  kswz is injective on every
+//    aligned run of G/2*2 = G consecutive rows, so the MFMA operand reads (one granule of 16
+//    consecutive rows per 16 lanes) hit distinct banks, and its top bit alternates between
+//    even and odd rows, which separates the two rows written by each 16-lane staging group.
+template <int D>
+__device__ __forceinline__ int kswz(int r) {
+    constexpr int G = D / 8;  // granules per row
+    return ((r & 1) * (G / 2)) | ((r >> 1) & (G / 2 - 1));
+}
+
+// 3D-RoPE (cos, sin) table of the attention kernel: one 256-byte row per axis position
+// (T t rows, then H h rows, then W w rows); pair j of a row sits at byte 16*off + 8*j.
+// Each staging group of 16 lanes covers two consecutive key rows times the eight chunk
+// pairs, and in instruction i the lanes of one axis read granules off + i + m*CH/2.  The
+// offsets put t, h and the w rows of even and odd "phi" into different granule classes, so
+// those reads never share a bank whenever the two rows share their t and h positions (the
+// common case): t at 0, h at 1 (D = 128) or 4 (D = 64), w at 2 + phi or 9 + phi, where phi
+// is the parity of w div phi_div -- phi_div being the w step between consecutive rows of a
+// scope (k for Single Skip, 1 for Group Skip).  phi only moves data, never changes values.
+template <int D>
+struct RopeBank {
+    static constexpr int kOffH = D == 128 ? 1 : 4;
+    static constexpr int kOffW = D == 128 ? 2 : 9;
+    static_assert(D == 64 || D == 128, "head_dim");
+};
+
+__device__ __forceinline__ int rope_phi(int w, int phi_mul) { return ((w * phi_mul) >> 16) & 1; }
+
+template <int D>
+__device__ __forceinline__ void build_banked_rope_table(char* tab, int T, int H, int W, int phi_mul) {
+    constexpr int kT = D / 8;        // pairs per t position
+    constexpr int kHW = 3 * D / 16;  // pairs per h or w position
+    const int nt = T * kT, nh = H * kHW, nw = W * kHW;
+    const int total = nt + nh + nw;
+    for (int e = threadIdx.x; e < total; e += blockDim.x) {
+        int pos, j, da, off;
+        if (e < nt) {
+            pos = e / kT; j = e - pos * kT; da = D / 4;
+            off = pos * 256;
+        } else if (e < nt + nh) {
+            const int r = e - nt; pos = r / kHW; j = r - pos * kHW; da = 3 * D / 8;
+            off = (T + pos) * 256 + RopeBank<D>::kOffH * 16;
+        } else {
+            const int r = e - nt - nh; pos = r / kHW; j = r - pos * kHW; da = 3 * D / 8;
+            off = (T + H + pos) * 256 + (RopeBank<D>::kOffW + rope_phi(pos, phi_mul)) * 16;
+        }
+        const double inv_freq = pow(10000.0, -2.0 * (double)j / (double)da);
+        const double theta = (double)pos * inv_freq;
+        double sn, cs;
+        sincos(theta, &sn, &cs);
+        *reinterpret_cast<float2*>(tab + off + 8 * j) = make_float2((float)cs, (float)sn);
+    }
 }
 
 __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
@@ -160,6 +218,14 @@ __device__ __forceinline__ void store_rotated_chunks(char* a1, char* a2, const f
     }
 }
 
+// LDS transpose read of 4 bf16 (ds_read_b64_tr_b16): within each group of 16 lanes,
+// lane j receives element j % 4 of the 4-element runs addressed by lanes 4t + j / 4,
+// t = 0..3.
+__device__ __forceinline__ i16x4 ds_read_tr16(const char* p) {
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+}
+
 // Grid position of a token, tracked across tiles by adding a fixed token delta
 // decomposed as (dt, dh, dw) with carries.
 struct Pos {
@@ -182,7 +248,7 @@ attn_fwd_kernel(AttnParams a) {
     constexpr int KK = kBN / 16; // 16-deep k-steps of P V
     constexpr int ES = E::kBytes;
     constexpr int kT = D / 8, kHW = 3 * D / 16;   // RoPE table pairs per t / h,w position
-    float2* tab = reinterpret_cast<float2*>(lds + L::kTabOff);
+    char* tab = lds + L::kTabOff;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -212,22 +278,30 @@ attn_fwd_kernel(AttnParams a) {
         (void*)(reinterpret_cast<char*>(a.out) + slice), (short)0, slice_bytes, 0x00020000);
     const int HW = a.H * a.W;
 
-    build_rope_table<D>(tab, a.T, a.H, a.W);
+    build_banked_rope_table<D>(tab, a.T, a.H, a.W, a.phi_mul);
 
-    // This thread's RoPE chunk pair (same for its Q and K staging tasks): table rows of
-    // its axis start at tbase + pos * tstride.
-    const RopePair rp = rope_pair(tid & 7);
-    const int tstride = rp.axis == 0 ? kT : kHW;
-    const int tbase = (rp.axis == 0 ? 0 : (rp.axis == 1 ? a.T * kT : a.T * kT + a.H * kHW)) + rp.jchunk * CH;
-    auto axis_pos = [&](const Pos& q) {
+    // This thread's RoPE chunk pair (same for its Q and K staging tasks) and the byte
+    // offsets of its table entries: tab_base + pos * 256 (+ 16 * phi on the w axis).
+    const int cp = tid & 7;
+    const RopePair rp = rope_pair(cp);
+    const int tab_base = (rp.axis == 0 ? 0
+                          : rp.axis == 1 ? a.T * 256 + RopeBank<D>::kOffH * 16
+                                         : (a.T + a.H) * 256 + RopeBank<D>::kOffW * 16) +
+                         rp.jchunk * CH * 8;
+    const int tab_phi_mul = rp.axis == 2 ? a.phi_mul : 0;
+    auto tab_row = [&](const Pos& q) __attribute__((always_inline)) {
         // t can exceed T-1 only on rows past the end of the scope, whose data is zero
-        const int t = min(q.t, a.T - 1);
-        return rp.axis == 0 ? t : (rp.axis == 1 ? q.h : q.w);
+        const int pos = rp.axis == 0 ? min(q.t, a.T - 1) : (rp.axis == 1 ? q.h : q.w);
+        return reinterpret_cast<const float2*>(tab + tab_base + pos * 256 + rope_phi(pos, tab_phi_mul) * 16);
     };
-    auto pos_of = [&](int nn) {
+    auto pos_of = [&](int nn) __attribute__((always_inline)) {
         Pos q;
         q.t = nn / HW; q.h = (nn / a.W) % a.H; q.w = nn % a.W;
         return q;
+    };
+    // byte offsets, inside a row, of the two chunks of this thread's pair in row r
+    auto chunk_off = [&](int r, int slot) __attribute__((always_inline)) {
+        return (slot * CB) ^ (kswz<D>(r) * 16);
     };
 
     // ---- stage the Q tile (rotated) into LDS, then into registers ----
@@ -245,65 +319,85 @@ attn_fwd_kernel(AttnParams a) {
             float x1[CH], x2[CH];
             raw_to_f32(r1, x1);
             raw_to_f32(r2, x2);
-            rope_rotate<CH>(x1, x2, tab + tbase + axis_pos(pos_of(n)) * tstride);
-            store_rotated_chunks<CH>(lds + r * L::kRowPitch + rp.c1 * CB, lds + r * L::kRowPitch + rp.c2 * CB, x1, x2);
+            rope_rotate<CH>(x1, x2, tab_row(pos_of(n)));
+            // fold the softmax scale log2(e)/sqrt(d) into q: scores come out in log2 units
+#pragma unroll
+            for (int e = 0; e < CH; ++e) {
+                x1[e] *= a.scale_log2;
+                x2[e] *= a.scale_log2;
+            }
+            store_rotated_chunks<CH>(lds + r * L::kRowPitch + chunk_off(r, cp), lds + r * L::kRowPitch + chunk_off(r, 8 + cp), x1, x2);
         }
     }
     __syncthreads();
     bf16x8 qreg[KS];
     {
-        const char* qrow = lds + (wave * 32 + l32) * L::kRowPitch + hf * 16;
+        const int qr = wave * 32 + l32;
+        const char* qrow = lds + qr * L::kRowPitch;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) qreg[ks] = *reinterpret_cast<const bf16x8*>(qrow + ks * 32);
+        for (int ks = 0; ks < KS; ++ks)
+            qreg[ks] = *reinterpret_cast<const bf16x8*>(qrow + (((2 * ks + hf) ^ kswz<D>(qr)) * 16));
     }
     __syncthreads();  // the Q area is reused by the K/V buffers below
 
     // ---- per-thread staging assignment ----
     // K: one (key row, RoPE chunk pair) task per thread.
-    // V: one (key pair, 8-element d chunk) task per thread; lanes 0..31 of a wave take
-    //    the 32 key pairs of one d chunk, so the transposed 4-byte LDS writes of 16
-    //    consecutive lanes fill one V^T row segment.
+    // V: rows are copied unchanged (row-major); thread t moves 16-byte chunk t % 16 of
+    //    rows t / 16 and t / 16 + 32, so each 16 lanes read and write one whole row.
     static_assert(kBN * 8 == kThreads, "one K staging task per thread");
-    constexpr int VPAIRS = kBN / 2;
-    constexpr int VTASKS = VPAIRS * VCH;
-    static_assert(VTASKS <= kThreads, "at most one V staging task per thread");
+    constexpr int VCPR = D / 8;             // 16-byte bf16 chunks per V row
+    constexpr int VROWS_PER_PASS = kThreads / VCPR;
+    constexpr int VPASSES = kBN / VROWS_PER_PASS;
+    static_assert(kBN % VROWS_PER_PASS == 0, "whole V rows per pass");
     const int krow = tid >> 3;
-    const int vpair = tid % VPAIRS;
-    const int vdc = tid / VPAIRS;
-    const bool v_active = VTASKS == kThreads || tid < VTASKS;
-    const int vslot = key_slot_quad(vpair >> 1) + (vpair & 1) * 2;
+    const int vrow = tid / VCPR;
+    const int vchunk = tid % VCPR;
 
-    // loop-invariant LDS addresses (the buffer index is added as an immediate)
-    const int k_rd = l32 * L::kRowPitch + hf * 16;                   // + kb*32 rows + ks*32 bytes
-    const int v_rd = l32 * L::kVtPitch + hf * 16;                    // + db*32 rows + kk*32 bytes
-    const int k_wr1 = krow * L::kRowPitch + rp.c1 * CB;
-    const int k_wr2 = krow * L::kRowPitch + rp.c2 * CB;
-    const int v_wr = 8 * vdc * L::kVtPitch + vslot * 2;              // + (2i + {0,1}) rows
+    // loop-invariant LDS addresses (the buffer base is added per tile)
+    // K operand reads: granule 2 ks + hf of row 32 kb + l32 sits at granule (2 ks + hf) ^ kswz(l32),
+    // i.e. at byte k_rd ^ (32 ks) (bits 5-7 of k_rd are the swizzle's, the rest is the row)
+    const int k_rd = l32 * L::kRowPitch + (((hf ^ kswz<D>(l32)) & 1) * 16) + ((kswz<D>(l32) & ~1) * 16);
+    const int k_wr1 = krow * L::kRowPitch + chunk_off(krow, cp);
+    const int k_wr2 = krow * L::kRowPitch + chunk_off(krow, 8 + cp);
+    const int v_wr = vrow * L::kVPitch + vchunk * 16;                // + pass * VROWS_PER_PASS rows
+    // PV operand reads with ds_read_b64_tr_b16.  Within each group of 16 lanes, lane
+    // i = 4t + q points at 4 consecutive d of key row t; the instruction then hands lane j
+    // the value at d0 + j of each of those 4 keys.  Lanes 0-31 need keys {0-3, 8-11} and
+    // lanes 32-63 keys {4-7, 12-15} of every 16-key step (the order in which the 32x32
+    // accumulator layout holds P^T), d0 = 16 * ((lane / 16) % 2) within a 32-row block.
+    const int tr_i = lane & 15;
+    const int v_rd = ((tr_i >> 2) + 4 * hf) * L::kVPitch + ((lane >> 4) & 1) * 32 + (tr_i & 3) * 8;
+    // + (16 kk + 8 h) rows + db * 64 bytes, h selecting keys {0-3,4-7} (h = 0) or {8-11,12-15}
 
-    // global offsets of the staged rows, advanced per tile
-    int koff1, koff2, voff[2];
+    // Global offsets of the rows to be loaded next (the load cursor runs two tiles ahead
+    // of the compute) and grid position of the K row to be staged next.
+    int koff1, koff2, voff[VPASSES];
     Pos kpos;
     const int tile_dn = kBN * a.sparse_k;     // token advance per tile when k | kBN
     const int dt = tile_dn / HW, rem = tile_dn % HW;
     const int dh = rem / a.W, dw = rem % a.W;
-    auto set_rows = [&](int p0) {
+    auto set_load_rows = [&](int p0) __attribute__((always_inline)) {
         const int kn = (int)scope_token(p0 + krow, s, k_, a.mode);
         koff1 = kn * row_bytes + rp.c1 * CH * ES;
         koff2 = kn * row_bytes + rp.c2 * CH * ES;
-        kpos = pos_of(kn);
 #pragma unroll
-        for (int e = 0; e < 2; ++e)
-            voff[e] = (int)scope_token(p0 + 2 * vpair + e, s, k_, a.mode) * row_bytes + vdc * 8 * ES;
+        for (int e = 0; e < VPASSES; ++e)
+            voff[e] = (int)scope_token(p0 + vrow + e * VROWS_PER_PASS, s, k_, a.mode) * row_bytes + vchunk * 8 * ES;
     };
-    set_rows(0);
-    auto advance_rows = [&](int tile) {
+    auto advance_load_rows = [&](int tile) __attribute__((always_inline)) {   // to tile `tile`, from tile - 1
         if (a.k_divides_bn) {
             // n(p + kBN) = n(p) + kBN*k in both modes when k divides kBN
             const int db_ = tile_dn * row_bytes;
             koff1 += db_;
             koff2 += db_;
-            voff[0] += db_;
-            voff[1] += db_;
+#pragma unroll
+            for (int e = 0; e < VPASSES; ++e) voff[e] += db_;
+        } else {
+            set_load_rows(tile * kBN);
+        }
+    };
+    auto advance_stage_pos = [&](int tile) __attribute__((always_inline)) {   // to tile `tile`, from tile - 1
+        if (a.k_divides_bn) {
             int w = kpos.w + dw, c = w >= a.W;
             kpos.w = w - (c ? a.W : 0);
             int h = kpos.h + dh + c;
@@ -311,100 +405,92 @@ attn_fwd_kernel(AttnParams a) {
             kpos.h = h - (c ? a.H : 0);
             kpos.t += dt + c;
         } else {
-            set_rows(tile * kBN);
+            kpos = pos_of((int)scope_token(tile * kBN + krow, s, k_, a.mode));
         }
     };
+    set_load_rows(0);
+    kpos = pos_of((int)scope_token(krow, s, k_, a.mode));
 
-    ChunkRaw<E, CH> kraw[2];
-    uint32_t vraw[2][4];
-    auto load_tile = [&]() {
-        buffer_load_dwords(kbuf, koff1, kraw[0].w);
-        buffer_load_dwords(kbuf, koff2, kraw[1].w);
-        if (v_active) {
-            buffer_load_8_as_bf16x2<E>(vbuf, voff[0], vraw[0]);
-            buffer_load_8_as_bf16x2<E>(vbuf, voff[1], vraw[1]);
-        }
+    // two register sets for staged rows: tile t is loaded into set t % 2
+    ChunkRaw<E, CH> kraw[2][2];
+    uint32_t vraw[2][VPASSES][4];
+    auto load_tile = [&](auto setc) __attribute__((always_inline)) {
+        constexpr int st = decltype(setc)::value;
+        buffer_load_dwords(kbuf, koff1, kraw[st][0].w);
+        buffer_load_dwords(kbuf, koff2, kraw[st][1].w);
+#pragma unroll
+        for (int e = 0; e < VPASSES; ++e) buffer_load_8_as_bf16x2<E>(vbuf, voff[e], vraw[st][e]);
     };
 
-    auto store_tile = [&](auto bufc) {
-        constexpr int buf = decltype(bufc)::value;
+    auto store_tile = [&](auto setc, int buf) __attribute__((always_inline)) {
+        constexpr int st = decltype(setc)::value;
         char* kdst = lds + L::kKOff + buf * L::kKTile;
         float x1[CH], x2[CH];
-        raw_to_f32(kraw[0], x1);
-        raw_to_f32(kraw[1], x2);
-        rope_rotate<CH>(x1, x2, tab + tbase + axis_pos(kpos) * tstride);
+        raw_to_f32(kraw[st][0], x1);
+        raw_to_f32(kraw[st][1], x2);
+        rope_rotate<CH>(x1, x2, tab_row(kpos));
         store_rotated_chunks<CH>(kdst + k_wr1, kdst + k_wr2, x1, x2);
-        if (v_active) {
-            char* vdst = lds + L::kVOff + buf * L::kVTile + v_wr;
+        char* vdst = lds + L::kVOff + buf * L::kVTile + v_wr;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                // dword i of each key row holds d = 8*vdc + 2i (low half) and + 2i + 1 (high half)
-                const uint32_t lo = __builtin_amdgcn_perm(vraw[1][i], vraw[0][i], 0x05040100u);
-                const uint32_t hi = __builtin_amdgcn_perm(vraw[1][i], vraw[0][i], 0x07060302u);
-                *reinterpret_cast<uint32_t*>(vdst + (2 * i) * L::kVtPitch) = lo;
-                *reinterpret_cast<uint32_t*>(vdst + (2 * i + 1) * L::kVtPitch) = hi;
-            }
-        }
+        for (int e = 0; e < VPASSES; ++e)
+            *reinterpret_cast<u32x4*>(vdst + e * VROWS_PER_PASS * L::kVPitch) =
+                u32x4{vraw[st][e][0], vraw[st][e][1], vraw[st][e][2], vraw[st][e][3]};
     };
 
-    // ---- main loop over key tiles ----
+    // ---- accumulators and softmax state ----
     f32x16 o[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int x = 0; x < 16; ++x) o[db][x] = 0.f;
-    float m_run = -__builtin_inff(), l_part = 0.f;
-    const float c = a.scale_log2;
+    // Softmax reference: scores are kept as S' = s*log2(e)/sqrt(d) - m_ref, with m_ref the
+    // running reference maximum (log2 units).  The QK MFMAs start from an accumulator that
+    // holds -m_ref in every slot, so they produce S' directly.
+    float m_ref = 0.f, l_part = 0.f;
+    f32x16 s_init;
+#pragma unroll
+    for (int x = 0; x < 16; ++x) s_init[x] = 0.f;
     const int nt = (a.L + kBN - 1) / kBN;
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-    load_tile();
-    store_tile(std::integral_constant<int, 0>{});
-    __syncthreads();
+    // ---- the four blocks of work per key tile ----
+    f32x16 sacc[KB];     // S'^T of the tile being processed
+    bf16x8 pb[KK];       // its bf16 weights, the B operand of P V
 
-    auto tile_step = [&](auto bufc, int j) {
-        constexpr int cur = decltype(bufc)::value;
-        const bool has_next = j + 1 < nt;
-        if (has_next) {
-            advance_rows(j + 1);
-            load_tile();
-        }
-        const char* kcur = lds + L::kKOff + cur * L::kKTile + k_rd;
-        const char* vcur = lds + L::kVOff + cur * L::kVTile + v_rd;
-
-        // S^T = K Q^T, operand reads kept one k-step ahead of the MFMAs that consume them
-        f32x16 sacc[KB];
+    // S'^T = K Q'^T onto -m_ref.  The 16 MFMAs run in (ks, kb) order; their K operands
+    // come from a 3-deep register ring, read 2 steps ahead.
+    constexpr int kRing = 3;
+    auto qk = [&](int buf) __attribute__((always_inline)) {
+        const char* kcur = lds + L::kKOff + buf * L::kKTile;
+        constexpr int NST = KS * KB;
+        auto kop = [&](int st) __attribute__((always_inline)) {
+            return *reinterpret_cast<const bf16x8*>(kcur + (k_rd ^ ((st / KB) * 32)) + (st % KB) * 32 * L::kRowPitch);
+        };
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
+        for (int kb = 0; kb < KB; ++kb) sacc[kb] = s_init;
+        bf16x8 ka[kRing];
 #pragma unroll
-            for (int x = 0; x < 16; ++x) sacc[kb][x] = 0.f;
-        bf16x8 ka[2][KB];
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) ka[0][kb] = *reinterpret_cast<const bf16x8*>(kcur + kb * 32 * L::kRowPitch);
+        for (int st = 0; st < kRing - 1; ++st) ka[st] = kop(st);
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            if (ks + 1 < KS) {
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb)
-                    ka[(ks + 1) & 1][kb] =
-                        *reinterpret_cast<const bf16x8*>(kcur + kb * 32 * L::kRowPitch + (ks + 1) * 32);
-            }
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks & 1][kb], qreg[ks], sacc[kb], 0, 0, 0);
+        for (int st = 0; st < NST; ++st) {
+            if (st + kRing - 1 < NST) ka[(st + kRing - 1) % kRing] = kop(st + kRing - 1);
+            sacc[st % KB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[st % kRing], qreg[st / KB], sacc[st % KB], 0, 0, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x100, 2 * KB, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, kRing - 1, 0);
 #pragma unroll
-        for (int i = 0; i < KS - 1; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, KB, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, KB, 0);
+        for (int i = 0; i < NST - (kRing - 1); ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, KB, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, kRing - 1, 0);
         __builtin_amdgcn_s_setprio(0);
+    };
 
-        // keys past the end of the scope (last tile only)
+    // online softmax of tile j: weights P = exp2(S'), row sums, lazy reference moves
+    auto softmax = [&](int j) __attribute__((always_inline)) {
         if (j == nt - 1 && (a.L % kBN) != 0) {
+            // keys past the end of the scope
             const int valid = a.L - j * kBN;
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
@@ -414,8 +500,9 @@ attn_fwd_kernel(AttnParams a) {
                     for (int jj = 0; jj < 4; ++jj)
                         if (kb * 32 + 8 * g + 4 * hf + jj >= valid) sacc[kb][4 * g + jj] = -__builtin_inff();
         }
-
-        // online softmax: tile max per query (in-lane, then across the two lane halves)
+        // tile max per query (in-lane, then across the two lane halves), relative to the
+        // reference.  The reference moves on the first tile (to this tile's max) and
+        // afterwards only when a tile exceeds it by more than 2^8.
         float mt = sacc[0][0];
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
@@ -423,73 +510,137 @@ attn_fwd_kernel(AttnParams a) {
             for (int x = 0; x < 16; ++x) mt = fmaxf(mt, sacc[kb][x]);
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
         mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-        const float mnew = fmaxf(m_run, mt);
-        if (__ballot((mnew - m_run) * c > kRescaleLog2) != 0ull) {
-            const float alpha = __builtin_amdgcn_exp2f((m_run - mnew) * c);
-            m_run = mnew;
+        if (j == 0 || __ballot(mt > kRescaleLog2) != 0ull) {
+            const float delta = j == 0 ? mt : fmaxf(mt, 0.f);
+            const float alpha = __builtin_amdgcn_exp2f(-delta);
+            m_ref += delta;
             l_part *= alpha;
 #pragma unroll
             for (int db = 0; db < DB; ++db)
 #pragma unroll
                 for (int x = 0; x < 16; ++x) o[db][x] *= alpha;
-        }
-        bf16x8 pb[KK];
-        {
-            const float mc = m_run * c;
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    // keys 32kb + 8g + 4hf + jj sit in k-step 2kb + g/2, slots (g%2)*4 + jj
-                    const int kk = 2 * kb + (g >> 1), sl = (g & 1) * 4;
+                for (int x = 0; x < 16; ++x) sacc[kb][x] -= delta;
 #pragma unroll
-                    for (int jj = 0; jj < 4; ++jj)
-                        pb[kk][sl + jj] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][4 * g + jj], c, -mc));
-                }
-            float lsum = l_part;
-#pragma unroll
-            for (int kk = 0; kk < KK; ++kk)
-#pragma unroll
-                for (int x = 0; x < 4; ++x) {
-                    const bf16x2 pair = {pb[kk][2 * x], pb[kk][2 * x + 1]};
-                    lsum = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, lsum, false);
-                }
-            l_part = lsum;
+            for (int x = 0; x < 16; ++x) s_init[x] = -m_ref;
         }
-
-        // O^T += V^T P^T, V operands read one k-step ahead
-        bf16x8 va[2][DB];
 #pragma unroll
-        for (int db = 0; db < DB; ++db) va[0][db] = *reinterpret_cast<const bf16x8*>(vcur + db * 32 * L::kVtPitch);
-        __builtin_amdgcn_s_setprio(1);
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-            if (kk + 1 < KK) {
+            for (int g = 0; g < 4; ++g) {
+                // keys 32kb + 8g + 4hf + jj sit in k-step 2kb + g/2, slots (g%2)*4 + jj
+                const int kk = 2 * kb + (g >> 1), sl = (g & 1) * 4;
 #pragma unroll
-                for (int db = 0; db < DB; ++db)
-                    va[(kk + 1) & 1][db] =
-                        *reinterpret_cast<const bf16x8*>(vcur + db * 32 * L::kVtPitch + (kk + 1) * 32);
+                for (int jj = 0; jj < 4; ++jj) pb[kk][sl + jj] = (__bf16)__builtin_amdgcn_exp2f(sacc[kb][4 * g + jj]);
             }
+        float lsum = l_part;
 #pragma unroll
-            for (int db = 0; db < DB; ++db)
-                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[kk & 1][db], pb[kk], o[db], 0, 0, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x100, 2 * DB, 0);
+        for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
-        for (int i = 0; i < KK - 1; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, DB, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, DB, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, DB, 0);
-        __builtin_amdgcn_s_setprio(0);
-
-        if (has_next) store_tile(std::integral_constant<int, cur ^ 1>{});
-        __syncthreads();
+            for (int x = 0; x < 4; ++x) {
+                const bf16x2 pair = {pb[kk][2 * x], pb[kk][2 * x + 1]};
+                lsum = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, lsum, false);
+            }
+        l_part = lsum;
     };
 
+    // O^T += V^T P^T; the V^T operands come transposed out of the row-major V tile, two
+    // transpose reads per operand, through a 3-deep register ring read 2 steps ahead.
+    auto pv = [&](int buf) __attribute__((always_inline)) {
+        const char* vcur = lds + L::kVOff + buf * L::kVTile + v_rd;
+        constexpr int NST = KK * DB;
+        auto vop = [&](int st) __attribute__((always_inline)) {
+            const int kk = st / DB, db = st % DB;
+            const i16x4 lo = ds_read_tr16(vcur + (16 * kk) * L::kVPitch + db * 64);
+            const i16x4 hi = ds_read_tr16(vcur + (16 * kk + 8) * L::kVPitch + db * 64);
+            const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            return __builtin_bit_cast(bf16x8, v);
+        };
+        bf16x8 va[kRing];
+#pragma unroll
+        for (int st = 0; st < kRing - 1; ++st) va[st] = vop(st);
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int st = 0; st < NST; ++st) {
+            if (st + kRing - 1 < NST) va[(st + kRing - 1) % kRing] = vop(st + kRing - 1);
+            o[st % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[st % kRing], pb[st / DB], o[st % DB], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * (kRing - 1), 0);
+#pragma unroll
+        for (int i = 0; i < NST - (kRing - 1); ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, kRing - 1, 0);
+        __builtin_amdgcn_s_setprio(0);
+    };
+
+    // ---- schedule ----
+    // Tile j lives in LDS buffer j % 3.  Waves 0-3 (one per SIMD) run each iteration as
+    //     QK(j), softmax(j), PV(j), stage(j+1)
+    // and waves 4-7 run it rotated by two blocks,
+    //     softmax(j-1), PV(j-1), stage(j+1), QK(j),
+    // with one workgroup barrier at the end of every iteration.  On each SIMD the MFMA
+    // blocks of one wave then coincide with the VALU blocks of the other.  Hazards: the
+    // staging of tile j+1 overwrites buffer (j-2) % 3, whose last readers (PV(j-2) of the
+    // second group) finished before the barrier that opened iteration j; QK of tile j+1
+    // runs after the barrier that closes the iteration in which both groups staged it.
+    // Global rows are requested two tiles ahead, into the register set of their tile's
+    // parity, so each load has a full iteration to arrive.
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    load_tile(S0{});
+    if (nt > 1) {
+        advance_load_rows(1);
+        load_tile(S1{});
+    }
+    store_tile(S0{}, 0);
+    __syncthreads();
+
+    const bool rotated = wave >= kWaves / 2;   // wave-uniform
+    int buf = 0, pbuf = 0;
+    auto next_buf = [](int b_) __attribute__((always_inline)) { return b_ == L::kBufs - 1 ? 0 : b_ + 1; };
+    // iteration j of either schedule; `par` is j % 2 (the register set that tile j + 2
+    // is loaded into and tile j + 1 is staged from is the other one)
+    auto iteration = [&](auto par, int j) __attribute__((always_inline)) {
+        constexpr int p = decltype(par)::value;
+        const int nbuf = next_buf(buf);
+        if (j + 2 < nt) {
+            advance_load_rows(j + 2);
+            load_tile(std::integral_constant<int, p>{});
+        }
+        if (!rotated) {
+            qk(buf);
+            softmax(j);
+            pv(buf);
+            if (j + 1 < nt) {
+                advance_stage_pos(j + 1);
+                store_tile(std::integral_constant<int, 1 - p>{}, nbuf);
+            }
+        } else {
+            if (j > 0) {
+                softmax(j - 1);
+                pv(pbuf);
+            }
+            if (j + 1 < nt) {
+                advance_stage_pos(j + 1);
+                store_tile(std::integral_constant<int, 1 - p>{}, nbuf);
+            }
+            qk(buf);
+        }
+        __syncthreads();
+        pbuf = buf;
+        buf = nbuf;
+    };
     for (int j = 0; j < nt; j += 2) {
-        tile_step(std::integral_constant<int, 0>{}, j);
-        if (j + 1 < nt) tile_step(std::integral_constant<int, 1>{}, j + 1);
+        iteration(S0{}, j);
+        if (j + 1 < nt) iteration(S1{}, j + 1);
+    }
+    if (rotated) {
+        softmax(nt - 1);
+        pv(pbuf);
     }
 
     // ---- epilogue: normalise and scatter rows back to their tokens ----
@@ -519,7 +670,7 @@ attn_fwd_kernel(AttnParams a) {
 template <int D, typename E>
 static hipError_t launch_attn_t(const AttnParams& a, hipStream_t stream) {
     typedef Lds<D> L;
-    const size_t lds = (size_t)L::kTabOff + (size_t)rope_table_pairs(a.T, a.H, a.W, D) * sizeof(float2);
+    const size_t lds = (size_t)L::kTabOff + (size_t)(a.T + a.H + a.W) * L::kTabRow;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_kernel<D, E>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;

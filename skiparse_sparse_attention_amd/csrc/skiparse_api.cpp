@@ -42,8 +42,7 @@ int check_dims(int B, int T, int H, int W, int heads, int head_dim, int sparse_k
         const int64_t k2 = (int64_t)sparse_k * sparse_k;
         if (k2 > N || N % k2) return SKIPARSE_E_DIVISIBILITY;
     }
-    if (skiparse::rope_table_pairs(T, H, W, head_dim) > SKIPARSE_MAX_ROPE_PAIRS)
-        return SKIPARSE_E_UNSUPPORTED;
+    if ((int64_t)T + H + W > SKIPARSE_MAX_GRID_SUM) return SKIPARSE_E_UNSUPPORTED;
     d->N = N;
     d->L = N / sparse_k;
     d->esize = dtype == SKIPARSE_BF16 ? 2 : 4;
@@ -105,6 +104,9 @@ int skiparse_attn(const void* q, const void* k, const void* v, int B, int T, int
     a.num_work = (int)work;
     a.k_divides_bn = (bn % sparse_k) == 0;
     a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)head_dim));
+    // consecutive rows of a scope step w by k (Single Skip) or by 1 (Group Skip)
+    const int phi_div = mode == SKIPARSE_SINGLE ? sparse_k : 1;
+    a.phi_mul = phi_div > 65536 ? 0 : (65536 + phi_div - 1) / phi_div;
     return to_status(skiparse::launch_attn(a, head_dim, dtype, static_cast<hipStream_t>(stream)));
 }
 

@@ -34,6 +34,7 @@ struct AttnParams {
     int num_work;    // B*heads*sparse_k*q_tiles workgroups
     int k_divides_bn;  // sparse_k divides the key-tile height
     float scale_log2;  // log2(e) / sqrt(head_dim)
+    int phi_mul;       // ceil(2^16 / phi_div), phi_div = w step between consecutive scope rows
 };
 
 hipError_t launch_rope_remap(const RemapParams& a, int head_dim, int dtype, hipStream_t stream, int grid);

@@ -75,7 +75,7 @@ def test_validate_accepts_good_arguments():
     (dict(sparse_k=3), sk.E_DIVISIBILITY),                  # 256 % 3
     (dict(sparse_k=32, mode=1), sk.E_DIVISIBILITY),         # 256 % 1024
     (dict(sparse_k=512), sk.E_DIVISIBILITY),
-    (dict(T=400, H=4, W=4, head_dim=128), sk.E_UNSUPPORTED),  # RoPE table > 6144 pairs
+    (dict(T=400, H=4, W=4, head_dim=128), sk.E_UNSUPPORTED),  # T + H + W > 192
     (dict(out=Q + 64), sk.E_ALIAS), (dict(out=V - 64), sk.E_ALIAS), (dict(out=K), sk.E_ALIAS),
 ])
 def test_validate_rejects(kw, status):
