@@ -12,47 +12,41 @@
 //     table each workgroup builds in LDS;
 //   * the epilogue stores row p straight to token n(s, p).
 //
-// Tiling (one workgroup = 8 wavefronts = 256 query rows of one scope; two
-// wavefronts per SIMD so one wave's VALU work can fill the other's MFMA time):
-//   * each wavefront owns 32 query rows and keeps Q^T for them in registers
-//     as the B operand of v_mfma_f32_32x32x16_bf16;
-//   * K tiles of 64 keys are staged (rotated, bf16, row-major) in LDS and are
-//     the A operand, so the scores come out transposed: S^T = K Q^T.  In the
-//     32x32 accumulator layout a lane then owns one query column and 16 of its
-//     keys per 32-key block, so the row max is an in-lane reduction plus one
-//     swap with the lane 32 away;
-//   * P^T (bf16) is fed to O^T += V^T P^T straight from the accumulator
-//     registers as the B operand.  The MFMA contracts over whatever key order
-//     the operand slots carry; V is staged row-major (a plain copy) and its
-//     V^T operands are read with the LDS transpose read ds_read_b64_tr_b16,
-//     whose per-lane addresses pick the keys in exactly the slot order in which
-//     P^T's accumulator layout holds them;
-//   * online softmax in fp32 on exp2: the scale log2(e)/sqrt(d) is folded into q
-//     before its bf16 rounding and the QK MFMAs accumulate onto -m_ref, so the
-//     scores arrive already shifted and each weight costs one v_exp_f32.  The
-//     row sum is accumulated from the bf16 P pairs with a 2-way dot
-//     instruction, so it sums exactly the weights the PV product uses.  The
-//     reference maximum m_ref is set from the first tile and afterwards only
-//     moved when a tile exceeds it by more than 2^8 (the result is identical up
-//     to rounding, since the same reference scales numerator and denominator),
-//     which skips almost every rescale of the O^T accumulator;
-//   * the two wavefronts of each SIMD run the per-tile blocks (QK MFMAs,
-//     softmax VALU, PV MFMAs, staging VALU) in a ping-pong: one half of the
-//     workgroup runs the iteration rotated by two blocks, so one wave's MFMA
-//     blocks coincide with the other's VALU blocks.  K and V^T tiles are
-//     triple-buffered in LDS, which keeps one barrier per tile sufficient;
-//   * LDS rows have padded pitches (one extra 16-byte granule per row), which
-//     keeps the 16-lane access groups of both the MFMA operand reads and the
-//     staging writes on distinct bank groups with plain "base + offset"
-//     addressing;
-//   * the next tile's rows are fetched into registers at the start of each
-//     iteration so global latency hides behind the math;
+// Tiling (one workgroup = 8 wavefronts = 256 query rows of one scope; two wavefronts per
+// SIMD):
+//   * each wavefront owns 32 query rows and keeps Q^T for them in registers as the B
+//     operand of v_mfma_f32_32x32x16_bf16;
+//   * K tiles of 64 keys are staged (rotated, bf16, row-major) in LDS and are the A operand,
+//     so the scores come out transposed: S^T = K Q^T.  In the 32x32 accumulator layout a
+//     lane then owns one query column and 16 of its keys per 32-key block, so the row max is
+//     an in-lane reduction plus one swap with the lane 32 away;
+//   * P^T (bf16) is fed to O^T += V^T P^T straight from the accumulator registers as the B
+//     operand.  The MFMA contracts over whatever key order the operand slots carry; V is
+//     copied row-major into LDS by buffer loads that write LDS directly, and its V^T
+//     operands are read with the LDS transpose read ds_read_b64_tr_b16, whose per-lane
+//     addresses pick the keys in exactly the slot order in which P^T's accumulator layout
+//     holds them;
+//   * online softmax in fp32 on exp2: the scale log2(e)/sqrt(d) is folded into q before its
+//     bf16 rounding and the QK MFMAs accumulate onto -m_ref, so the scores arrive already
+//     shifted and each weight costs one v_exp_f32.  The row sum is accumulated from the bf16
+//     P pairs with a 2-way dot instruction, so it sums exactly the weights the PV product
+//     uses.  The reference maximum m_ref is set from the first tile and afterwards only
+//     moved when a tile exceeds it by more than 2^8 (the result is identical up to rounding,
+//     since the same reference scales numerator and denominator), which skips almost every
+//     rescale of the O^T accumulator;
+//   * the two wavefronts of each SIMD belong to different groups (waves 0-3, waves 4-7), and
+//     the groups alternate between an MFMA block (PV of the previous tile, QK of the current
+//     one) and a VALU block (softmax, RoPE staging of the next K tile, load requests), one
+//     phase apart with a workgroup barrier per phase, so one wave's MFMAs run beside the
+//     other's vector work;
+//   * LDS layouts are bank-conflict-free for every access: padded Q/K rows, XOR-swizzled V
+//     rows, and a RoPE table with one row per axis position at axis-dependent offsets;
 //   * all global traffic uses buffer instructions with 32-bit offsets into the
-//     (batch, head) slice; rows past the end of a scope have token indices
-//     >= N, i.e. offsets past the slice, which the hardware range check turns
-//     into zero loads and dropped stores;
-//   * workgroup ids are remapped so the q tiles of one scope run on the same
-//     XCD and share its L2 copy of the scope's K and V.
+//     (batch, head) slice; rows past the end of a scope have token indices >= N, i.e.
+//     offsets past the slice, which the hardware range check turns into zero loads and
+//     dropped stores;
+//   * workgroup ids are remapped so the q tiles of one scope run on the same XCD and share
+//     its L2 copy of the scope's K and V.
 #include <type_traits>
 
 #include "skiparse_device.hpp"
@@ -70,32 +64,27 @@ constexpr float kRescaleLog2 = 8.0f;
 
 template <int D>
 struct Lds {
-    static constexpr int kRowPitch = D * 2;               // Q / K rows (bf16), granules swizzled
-    static constexpr int kVPitch = D * 2 + 64;            // V rows (bf16) + four pad granules
+    static constexpr int kRowPitch = D * 2 + 16;          // Q / K rows (bf16) + one pad granule
+    static constexpr int kVPitch = D * 2;                 // V rows (bf16), granules swizzled
     static constexpr int kKTile = kBN * kRowPitch;
     static constexpr int kVTile = kBN * kVPitch;
-    static constexpr int kBufs = 3;                       // K/V tiles in flight (see the schedule)
+    static constexpr int kKBufs = 2;                      // K tiles in LDS (see the schedule)
+    static constexpr int kVBufs = 3;                      // V tiles in LDS
     static constexpr int kKOff = 0;
-    static constexpr int kVOff = kBufs * kKTile;
-    static constexpr int kTiles = kBufs * (kKTile + kVTile);
+    static constexpr int kVOff = kKBufs * kKTile;
+    static constexpr int kTiles = kKBufs * kKTile + kVBufs * kVTile;
     static constexpr int kQBytes = kBM * kRowPitch;       // Q staging, aliases the tiles
     static constexpr int kTabOff = kTiles > kQBytes ? kTiles : kQBytes;
     static constexpr int kTabRow = 256;                   // bytes per RoPE table row
 };
 
-// Q and K rows in LDS hold the 16-byte granules of a row in a permuted order:
-//  * RoPE chunk pair cp (first-half chunk c1, partner c2) is stored in chunk slots cp and
-//    8 + cp, so the partners sit in opposite halves of the row (Q and K use the same order,
-//    and Q K^T contracts over head_dim in any order);
-//  * granule g of row r is then stored at granule g ^ kswz(r).  kswz is injective on every
-//    aligned run of G/2*2 = G consecutive rows, so the MFMA operand reads (one granule of 16
-//    consecutive rows per 16 lanes) hit distinct banks, and its top bit alternates between
-//    even and odd rows, which separates the two rows written by each 16-lane staging group.
-template <int D>
-__device__ __forceinline__ int kswz(int r) {
-    constexpr int G = D / 8;  // granules per row
-    return ((r & 1) * (G / 2)) | ((r >> 1) & (G / 2 - 1));
-}
+// Q and K rows in LDS hold RoPE chunk pair cp (first-half chunk c1, partner c2) in chunk slots
+// 2 cp and 2 cp + 1, i.e. each rotate-half pair in one 32-byte span (Q and K use the same order,
+// and Q K^T contracts over head_dim in any order).  With the one-granule row pad, granule g of
+// row r falls in bank group (r + g) mod 16 (D = 128): the MFMA operand reads (one granule of 16
+// consecutive rows per 16 lanes) are conflict-free, and so are the staging writes of a 16-lane
+// group (two consecutive rows times eight pairs), whose first store covers the even slots and
+// whose second store covers the odd ones.
 
 // 3D-RoPE (cos, sin) table of the attention kernel: one 256-byte row per axis position
 // (T t rows, then H h rows, then W w rows); pair j of a row sits at byte 16*off + 8*j.
@@ -112,6 +101,17 @@ struct RopeBank {
     static constexpr int kOffW = D == 128 ? 2 : 9;
     static_assert(D == 64 || D == 128, "head_dim");
 };
+
+// V rows in LDS: granule g of row r is stored at granule g ^ vswz(r).  The PV operand reads
+// (ds_read_b64_tr_b16) fetch, per 32 lanes, the same four-granule block of four consecutive
+// rows; vswz moves those rows' blocks apart (by r mod 4 at D = 128; at D = 64 the row parity
+// already separates rows r and r + 1 and vswz separates r and r + 2), so the 32 lanes hit
+// distinct banks.  Rows are written whole by 64-lane 1 KiB loads, conflict-free in any order.
+template <int D>
+__device__ __forceinline__ int vswz(int r) {
+    if constexpr (D == 128) return (r & 3) << 2;
+    else return ((r >> 1) & 1) << 2;
+}
 
 __device__ __forceinline__ int rope_phi(int w, int phi_mul) { return ((w * phi_mul) >> 16) & 1; }
 
@@ -168,6 +168,18 @@ __device__ __forceinline__ void raw_to_f32(const ChunkRaw<E, CH>& r, float (&x)[
     }
 }
 
+// Rotate-half pair rotation with table entries preloaded as f32x4 = two (cos, sin) pairs.
+template <int CH>
+__device__ __forceinline__ void rope_rotate_cs(float (&x1)[CH], float (&x2)[CH], const f32x4 (&cs)[CH / 2]) {
+#pragma unroll
+    for (int e = 0; e < CH; ++e) {
+        const float c = cs[e / 2][2 * (e % 2)], sn = cs[e / 2][2 * (e % 2) + 1];
+        const float a = x1[e], b = x2[e];
+        x1[e] = a * c - b * sn;
+        x2[e] = b * c + a * sn;
+    }
+}
+
 // Buffer load of NDW dwords at a byte offset.
 template <int NDW>
 __device__ __forceinline__ void buffer_load_dwords(__amdgpu_buffer_rsrc_t r, int off, uint32_t (&w)[NDW]) {
@@ -218,6 +230,24 @@ __device__ __forceinline__ void store_rotated_chunks(char* a1, char* a2, const f
     }
 }
 
+// 16 bytes per lane from a buffer straight into LDS: lane l's bytes land at dst + 16 l (dst
+// must be wave-uniform; out-of-range offsets write zeros).  Issued as inline assembly so the
+// compiler does not treat every later LDS read as a possible reader of this write and wait for
+// all outstanding loads before it; the caller instead waits for the load counter (vmcnt) before
+// the barrier after which the data is read.  The s_nop covers the M0-write hazard.
+__device__ __forceinline__ void buffer_load_to_lds16(__amdgpu_buffer_rsrc_t r, char* dst, int off) {
+    const unsigned lds_addr = (unsigned)(size_t)((__attribute__((address_space(3))) char*)dst);
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off), "s"(r), "{m0}"(lds_addr) : "memory");
+}
+
+// Wait until every vector memory load of this wave has completed (including loads into LDS).
+__device__ __forceinline__ void wait_vm_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Wait until at most N vector memory instructions of this wave are outstanding: every load
+// issued before the N most recent ones has completed (loads complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vm_loads_but() { asm volatile("s_waitcnt vmcnt(%0)" ::"i"(N) : "memory"); }
+
 // LDS transpose read of 4 bf16 (ds_read_b64_tr_b16): within each group of 16 lanes,
 // lane j receives element j % 4 of the 4-element runs addressed by lanes 4t + j / 4,
 // t = 0..3.
@@ -234,7 +264,9 @@ struct Pos {
 
 }  // namespace
 
-template <int D, typename E>
+// KDIV: sparse_k divides kBN, so row p + kBN of a scope is token n(p) + kBN*k in both modes
+// and the load cursors advance by a constant.
+template <int D, typename E, bool KDIV>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kThreads / 256, kThreads / 256)))
 attn_fwd_kernel(AttnParams a) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
@@ -243,15 +275,14 @@ attn_fwd_kernel(AttnParams a) {
     constexpr int CB = CH * 2;   // bytes per RoPE chunk in LDS (bf16)
     constexpr int KS = D / 16;   // 16-deep k-steps of Q K^T
     constexpr int DB = D / 32;   // 32-row blocks of O^T
-    constexpr int VCH = D / 8;   // 8-element d-chunks per V row
     constexpr int KB = kBN / 32; // 32-key blocks of S^T
     constexpr int KK = kBN / 16; // 16-deep k-steps of P V
     constexpr int ES = E::kBytes;
-    constexpr int kT = D / 8, kHW = 3 * D / 16;   // RoPE table pairs per t / h,w position
     char* tab = lds + L::kTabOff;
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int l32 = lane & 31, hf = lane >> 5;
 
     // ---- which (batch, head, scope, q tile) this workgroup computes ----
@@ -289,20 +320,21 @@ attn_fwd_kernel(AttnParams a) {
                                          : (a.T + a.H) * 256 + RopeBank<D>::kOffW * 16) +
                          rp.jchunk * CH * 8;
     const int tab_phi_mul = rp.axis == 2 ? a.phi_mul : 0;
-    auto tab_row = [&](const Pos& q) __attribute__((always_inline)) {
+    // the CH (cos, sin) pairs of this thread's chunk pair at grid position q, as CH/2 16-byte reads
+    auto load_tab = [&](const Pos& q, f32x4 (&cs)[CH / 2]) __attribute__((always_inline)) {
         // t can exceed T-1 only on rows past the end of the scope, whose data is zero
         const int pos = rp.axis == 0 ? min(q.t, a.T - 1) : (rp.axis == 1 ? q.h : q.w);
-        return reinterpret_cast<const float2*>(tab + tab_base + pos * 256 + rope_phi(pos, tab_phi_mul) * 16);
+        const char* row = tab + tab_base + pos * 256 + rope_phi(pos, tab_phi_mul) * 16;
+#pragma unroll
+        for (int i = 0; i < CH / 2; ++i) cs[i] = *reinterpret_cast<const f32x4*>(row + 16 * i);
     };
     auto pos_of = [&](int nn) __attribute__((always_inline)) {
         Pos q;
         q.t = nn / HW; q.h = (nn / a.W) % a.H; q.w = nn % a.W;
         return q;
     };
-    // byte offsets, inside a row, of the two chunks of this thread's pair in row r
-    auto chunk_off = [&](int r, int slot) __attribute__((always_inline)) {
-        return (slot * CB) ^ (kswz<D>(r) * 16);
-    };
+    // byte offsets, inside a Q/K row, of the chunks of this thread's pair (slots 2 cp, 2 cp + 1)
+    const int c1_off = 2 * cp * CB, c2_off = (2 * cp + 1) * CB;
 
     // ---- stage the Q tile (rotated) into LDS, then into registers ----
     {
@@ -319,14 +351,16 @@ attn_fwd_kernel(AttnParams a) {
             float x1[CH], x2[CH];
             raw_to_f32(r1, x1);
             raw_to_f32(r2, x2);
-            rope_rotate<CH>(x1, x2, tab_row(pos_of(n)));
+            f32x4 cs[CH / 2];
+            load_tab(pos_of(n), cs);
+            rope_rotate_cs<CH>(x1, x2, cs);
             // fold the softmax scale log2(e)/sqrt(d) into q: scores come out in log2 units
 #pragma unroll
             for (int e = 0; e < CH; ++e) {
                 x1[e] *= a.scale_log2;
                 x2[e] *= a.scale_log2;
             }
-            store_rotated_chunks<CH>(lds + r * L::kRowPitch + chunk_off(r, cp), lds + r * L::kRowPitch + chunk_off(r, 8 + cp), x1, x2);
+            store_rotated_chunks<CH>(lds + r * L::kRowPitch + c1_off, lds + r * L::kRowPitch + c2_off, x1, x2);
         }
     }
     __syncthreads();
@@ -336,68 +370,82 @@ attn_fwd_kernel(AttnParams a) {
         const char* qrow = lds + qr * L::kRowPitch;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-            qreg[ks] = *reinterpret_cast<const bf16x8*>(qrow + (((2 * ks + hf) ^ kswz<D>(qr)) * 16));
+            qreg[ks] = *reinterpret_cast<const bf16x8*>(qrow + (2 * ks + hf) * 16);
     }
     __syncthreads();  // the Q area is reused by the K/V buffers below
 
     // ---- per-thread staging assignment ----
     // K: one (key row, RoPE chunk pair) task per thread.
-    // V: rows are copied unchanged (row-major); thread t moves 16-byte chunk t % 16 of
-    //    rows t / 16 and t / 16 + 32, so each 16 lanes read and write one whole row.
+    // V: rows are copied unchanged in 1 KiB pieces (kVRows whole rows): in piece i, lane l
+    //    moves granule l % G of row i*kVRows + l / G into LDS position l, loading for it the
+    //    granule that the row swizzle puts there.  Each wave moves kVOps pieces per tile.
     static_assert(kBN * 8 == kThreads, "one K staging task per thread");
-    constexpr int VCPR = D / 8;             // 16-byte bf16 chunks per V row
-    constexpr int VROWS_PER_PASS = kThreads / VCPR;
-    constexpr int VPASSES = kBN / VROWS_PER_PASS;
-    static_assert(kBN % VROWS_PER_PASS == 0, "whole V rows per pass");
+    constexpr int G = D / 8;                      // 16-byte bf16 granules per row
+    constexpr int kVRows = 64 / G;                // rows per 1 KiB piece
+    constexpr int kVOps = kBN / kVRows / kWaves;  // pieces per wave per tile
+    static_assert(kVOps * kVRows * kWaves == kBN, "whole V tile in 1 KiB pieces");
     const int krow = tid >> 3;
-    const int vrow = tid / VCPR;
-    const int vchunk = tid % VCPR;
+    int vrow[kVOps], vgran[kVOps];
+#pragma unroll
+    for (int i = 0; i < kVOps; ++i) {
+        vrow[i] = (wave * kVOps + i) * kVRows + lane / G;
+        vgran[i] = (lane % G) ^ vswz<D>(vrow[i]);
+    }
 
     // loop-invariant LDS addresses (the buffer base is added per tile)
-    // K operand reads: granule 2 ks + hf of row 32 kb + l32 sits at granule (2 ks + hf) ^ kswz(l32),
-    // i.e. at byte k_rd ^ (32 ks) (bits 5-7 of k_rd are the swizzle's, the rest is the row)
-    const int k_rd = l32 * L::kRowPitch + (((hf ^ kswz<D>(l32)) & 1) * 16) + ((kswz<D>(l32) & ~1) * 16);
-    const int k_wr1 = krow * L::kRowPitch + chunk_off(krow, cp);
-    const int k_wr2 = krow * L::kRowPitch + chunk_off(krow, 8 + cp);
-    const int v_wr = vrow * L::kVPitch + vchunk * 16;                // + pass * VROWS_PER_PASS rows
+    const int k_rd = l32 * L::kRowPitch + hf * 16;                   // + kb*32 rows + ks*32 bytes
+    const int k_wr1 = krow * L::kRowPitch + c1_off;
+    const int k_wr2 = krow * L::kRowPitch + c2_off;
     // PV operand reads with ds_read_b64_tr_b16.  Within each group of 16 lanes, lane
     // i = 4t + q points at 4 consecutive d of key row t; the instruction then hands lane j
     // the value at d0 + j of each of those 4 keys.  Lanes 0-31 need keys {0-3, 8-11} and
     // lanes 32-63 keys {4-7, 12-15} of every 16-key step (the order in which the 32x32
     // accumulator layout holds P^T), d0 = 16 * ((lane / 16) % 2) within a 32-row block.
+    // Row 16 kk + 8 h + tr_row, granule 4 db + tr_gran, byte tr_byte within the granule.
     const int tr_i = lane & 15;
-    const int v_rd = ((tr_i >> 2) + 4 * hf) * L::kVPitch + ((lane >> 4) & 1) * 32 + (tr_i & 3) * 8;
-    // + (16 kk + 8 h) rows + db * 64 bytes, h selecting keys {0-3,4-7} (h = 0) or {8-11,12-15}
+    const int tr_row = (tr_i >> 2) + 4 * (lane >> 5);
+    const int tr_gran = 2 * ((lane >> 4) & 1) + ((tr_i & 3) >> 1);
+    const int tr_byte = (tr_i & 1) * 8;
+    auto v_rd = [&](int h, int db) __attribute__((always_inline)) {
+        const int r = 8 * h + tr_row;   // the row modulo 16, which is all vswz looks at
+        return r * L::kVPitch + (((4 * db + tr_gran) ^ vswz<D>(r)) * 16) + tr_byte;
+    };
 
     // Global offsets of the rows to be loaded next (the load cursor runs two tiles ahead
     // of the compute) and grid position of the K row to be staged next.
-    int koff1, koff2, voff[VPASSES];
+    int koff1, koff2, voff[kVOps];
     Pos kpos;
     const int tile_dn = kBN * a.sparse_k;     // token advance per tile when k | kBN
     const int dt = tile_dn / HW, rem = tile_dn % HW;
     const int dh = rem / a.W, dw = rem % a.W;
-    auto set_load_rows = [&](int p0) __attribute__((always_inline)) {
+    auto set_k_rows = [&](int p0) __attribute__((always_inline)) {
         const int kn = (int)scope_token(p0 + krow, s, k_, a.mode);
         koff1 = kn * row_bytes + rp.c1 * CH * ES;
         koff2 = kn * row_bytes + rp.c2 * CH * ES;
-#pragma unroll
-        for (int e = 0; e < VPASSES; ++e)
-            voff[e] = (int)scope_token(p0 + vrow + e * VROWS_PER_PASS, s, k_, a.mode) * row_bytes + vchunk * 8 * ES;
     };
-    auto advance_load_rows = [&](int tile) __attribute__((always_inline)) {   // to tile `tile`, from tile - 1
-        if (a.k_divides_bn) {
-            // n(p + kBN) = n(p) + kBN*k in both modes when k divides kBN
-            const int db_ = tile_dn * row_bytes;
-            koff1 += db_;
-            koff2 += db_;
+    auto set_v_rows = [&](int p0) __attribute__((always_inline)) {
 #pragma unroll
-            for (int e = 0; e < VPASSES; ++e) voff[e] += db_;
+        for (int i = 0; i < kVOps; ++i)
+            voff[i] = (int)scope_token(p0 + vrow[i], s, k_, a.mode) * row_bytes + vgran[i] * 8 * ES;
+    };
+    auto advance_k_rows = [&](int tile) __attribute__((always_inline)) {   // to tile `tile`, from tile - 1
+        if constexpr (KDIV) {
+            koff1 += tile_dn * row_bytes;
+            koff2 += tile_dn * row_bytes;
         } else {
-            set_load_rows(tile * kBN);
+            set_k_rows(tile * kBN);
+        }
+    };
+    auto advance_v_rows = [&](int tile) __attribute__((always_inline)) {
+        if constexpr (KDIV) {
+#pragma unroll
+            for (int i = 0; i < kVOps; ++i) voff[i] += tile_dn * row_bytes;
+        } else {
+            set_v_rows(tile * kBN);
         }
     };
     auto advance_stage_pos = [&](int tile) __attribute__((always_inline)) {   // to tile `tile`, from tile - 1
-        if (a.k_divides_bn) {
+        if constexpr (KDIV) {
             int w = kpos.w + dw, c = w >= a.W;
             kpos.w = w - (c ? a.W : 0);
             int h = kpos.h + dh + c;
@@ -408,33 +456,44 @@ attn_fwd_kernel(AttnParams a) {
             kpos = pos_of((int)scope_token(tile * kBN + krow, s, k_, a.mode));
         }
     };
-    set_load_rows(0);
+    set_k_rows(0);
+    set_v_rows(0);
     kpos = pos_of((int)scope_token(krow, s, k_, a.mode));
 
-    // two register sets for staged rows: tile t is loaded into set t % 2
-    ChunkRaw<E, CH> kraw[2][2];
-    uint32_t vraw[2][VPASSES][4];
-    auto load_tile = [&](auto setc) __attribute__((always_inline)) {
-        constexpr int st = decltype(setc)::value;
-        buffer_load_dwords(kbuf, koff1, kraw[st][0].w);
-        buffer_load_dwords(kbuf, koff2, kraw[st][1].w);
-#pragma unroll
-        for (int e = 0; e < VPASSES; ++e) buffer_load_8_as_bf16x2<E>(vbuf, voff[e], vraw[st][e]);
+    // K rows: loaded into registers two phases before they are rotated and staged.
+    // V rows: bf16 goes straight from memory into the LDS tile (buffer loads to LDS); fp32 is
+    // loaded through registers and rounded to bf16.
+    ChunkRaw<E, CH> kraw[2];
+    auto load_k = [&]() __attribute__((always_inline)) {
+        buffer_load_dwords(kbuf, koff1, kraw[0].w);
+        buffer_load_dwords(kbuf, koff2, kraw[1].w);
     };
-
-    auto store_tile = [&](auto setc, int buf) __attribute__((always_inline)) {
-        constexpr int st = decltype(setc)::value;
-        char* kdst = lds + L::kKOff + buf * L::kKTile;
-        float x1[CH], x2[CH];
-        raw_to_f32(kraw[st][0], x1);
-        raw_to_f32(kraw[st][1], x2);
-        rope_rotate<CH>(x1, x2, tab_row(kpos));
-        store_rotated_chunks<CH>(kdst + k_wr1, kdst + k_wr2, x1, x2);
-        char* vdst = lds + L::kVOff + buf * L::kVTile + v_wr;
+    auto load_v = [&](int vb) __attribute__((always_inline)) {
 #pragma unroll
-        for (int e = 0; e < VPASSES; ++e)
-            *reinterpret_cast<u32x4*>(vdst + e * VROWS_PER_PASS * L::kVPitch) =
-                u32x4{vraw[st][e][0], vraw[st][e][1], vraw[st][e][2], vraw[st][e][3]};
+        for (int i = 0; i < kVOps; ++i) {
+            char* dst = lds + L::kVOff + vb * L::kVTile + (wave * kVOps + i) * 1024;
+            if constexpr (ES == 2) {
+                buffer_load_to_lds16(vbuf, dst, voff[i]);
+            } else {
+                uint32_t w[4];
+                buffer_load_8_as_bf16x2<E>(vbuf, voff[i], w);
+                *reinterpret_cast<u32x4*>(dst + lane * 16) = u32x4{w[0], w[1], w[2], w[3]};
+            }
+        }
+    };
+    // vector memory instructions one staging block issues (the V loads to LDS, then the K loads)
+    constexpr int kKLoadOps = 2 * (CH * ES >= 32 ? 2 : 1);
+    constexpr int kVmOps = (ES == 2 ? kVOps : 0) + kKLoadOps;
+
+    // table entries for the K row to be staged next, read at the start of the staging block
+    f32x4 kcs[CH / 2];
+    auto stage_k = [&](int kb) __attribute__((always_inline)) {
+        char* kdst = lds + L::kKOff + kb * L::kKTile;
+        float x1[CH], x2[CH];
+        raw_to_f32(kraw[0], x1);
+        raw_to_f32(kraw[1], x2);
+        rope_rotate_cs<CH>(x1, x2, kcs);
+        store_rotated_chunks<CH>(kdst + k_wr1, kdst + k_wr2, x1, x2);
     };
 
     // ---- accumulators and softmax state ----
@@ -458,13 +517,13 @@ attn_fwd_kernel(AttnParams a) {
     bf16x8 pb[KK];       // its bf16 weights, the B operand of P V
 
     // S'^T = K Q'^T onto -m_ref.  The 16 MFMAs run in (ks, kb) order; their K operands
-    // come from a 3-deep register ring, read 2 steps ahead.
-    constexpr int kRing = 3;
+    // come from a 4-deep register ring, read 3 steps ahead.
+    constexpr int kRing = 4;
     auto qk = [&](int buf) __attribute__((always_inline)) {
         const char* kcur = lds + L::kKOff + buf * L::kKTile;
         constexpr int NST = KS * KB;
         auto kop = [&](int st) __attribute__((always_inline)) {
-            return *reinterpret_cast<const bf16x8*>(kcur + (k_rd ^ ((st / KB) * 32)) + (st % KB) * 32 * L::kRowPitch);
+            return *reinterpret_cast<const bf16x8*>(kcur + k_rd + (st % KB) * 32 * L::kRowPitch + (st / KB) * 32);
         };
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) sacc[kb] = s_init;
@@ -535,26 +594,26 @@ attn_fwd_kernel(AttnParams a) {
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) pb[kk][sl + jj] = (__bf16)__builtin_amdgcn_exp2f(sacc[kb][4 * g + jj]);
             }
-        float lsum = l_part;
+        float lsum[2] = {l_part, 0.f};   // two independent chains
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
                 const bf16x2 pair = {pb[kk][2 * x], pb[kk][2 * x + 1]};
-                lsum = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, lsum, false);
+                lsum[x & 1] = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, lsum[x & 1], false);
             }
-        l_part = lsum;
+        l_part = lsum[0] + lsum[1];
     };
 
     // O^T += V^T P^T; the V^T operands come transposed out of the row-major V tile, two
-    // transpose reads per operand, through a 3-deep register ring read 2 steps ahead.
+    // transpose reads per operand, through a 4-deep register ring read 3 steps ahead.
     auto pv = [&](int buf) __attribute__((always_inline)) {
-        const char* vcur = lds + L::kVOff + buf * L::kVTile + v_rd;
+        const char* vcur = lds + L::kVOff + buf * L::kVTile;
         constexpr int NST = KK * DB;
         auto vop = [&](int st) __attribute__((always_inline)) {
             const int kk = st / DB, db = st % DB;
-            const i16x4 lo = ds_read_tr16(vcur + (16 * kk) * L::kVPitch + db * 64);
-            const i16x4 hi = ds_read_tr16(vcur + (16 * kk + 8) * L::kVPitch + db * 64);
+            const i16x4 lo = ds_read_tr16(vcur + (16 * kk) * L::kVPitch + v_rd(0, db));
+            const i16x4 hi = ds_read_tr16(vcur + (16 * kk) * L::kVPitch + v_rd(1, db));
             const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
             return __builtin_bit_cast(bf16x8, v);
         };
@@ -578,69 +637,76 @@ attn_fwd_kernel(AttnParams a) {
     };
 
     // ---- schedule ----
-    // Tile j lives in LDS buffer j % 3.  Waves 0-3 (one per SIMD) run each iteration as
-    //     QK(j), softmax(j), PV(j), stage(j+1)
-    // and waves 4-7 run it rotated by two blocks,
-    //     softmax(j-1), PV(j-1), stage(j+1), QK(j),
-    // with one workgroup barrier at the end of every iteration.  On each SIMD the MFMA
-    // blocks of one wave then coincide with the VALU blocks of the other.  Hazards: the
-    // staging of tile j+1 overwrites buffer (j-2) % 3, whose last readers (PV(j-2) of the
-    // second group) finished before the barrier that opened iteration j; QK of tile j+1
-    // runs after the barrier that closes the iteration in which both groups staged it.
-    // Global rows are requested two tiles ahead, into the register set of their tile's
-    // parity, so each load has a full iteration to arrive.
-    using S0 = std::integral_constant<int, 0>;
-    using S1 = std::integral_constant<int, 1>;
-    load_tile(S0{});
+    // Waves 0-3 (group 0, one per SIMD) and waves 4-7 (group 1) alternate between an MFMA
+    // block and a VALU block, one phase apart, with a workgroup barrier closing every phase,
+    // so on each SIMD one wave's MFMAs run beside the other wave's vector work.  Phase
+    // numbers ph = 1, 2, ...; group g runs in phase ph
+    //   MFMA block (ph + g odd), m = (ph - 1 - g) / 2:   PV(m-1) if m >= 1, QK(m) if m < nt;
+    //   VALU block (ph + g even), m = (ph - 2 + g) / 2:  softmax(m) (g = 0) or softmax(m-1)
+    //     (g = 1); the group's half of the rows of K tile m+1 rotated and staged; its half of
+    //     V tile m+1 requested into LDS; its K rows of tile m+2 requested into registers.
+    // K tile m lives in K buffer m % 2 and V tile m in V buffer m % 3.  K tile m+1 is staged
+    // in phases 2m+1 and 2m+2, after the last reads of K tile m-1 (QK(m-1) in phases 2m-1 and
+    // 2m) and before the first read (QK(m+1) in phase 2m+3).  V tile m+1 is requested in
+    // phases 2m+1 and 2m+2, after the last reads of V tile m-2 (PV(m-2) in phases 2m-1 and
+    // 2m); each VALU block ends by waiting until the loads of the wave's previous VALU block
+    // have landed, so V tile m+1 is complete after phase 2m+4, before PV(m+1) in phase 2m+5.
+    // P(m) stays in registers from softmax(m) to PV(m) in the group's next MFMA block.
+    const int grp = wave >= kWaves / 2 ? 1 : 0;   // wave-uniform
+    // prologue: K tile 0 staged by every wave, V tile 0 in LDS, the K rows of tile 1 requested
+    load_v(0);
+    load_k();
+    load_tab(kpos, kcs);
+    stage_k(0);
     if (nt > 1) {
-        advance_load_rows(1);
-        load_tile(S1{});
+        advance_k_rows(1);
+        load_k();
     }
-    store_tile(S0{}, 0);
+    wait_vm_loads();
     __syncthreads();
 
-    const bool rotated = wave >= kWaves / 2;   // wave-uniform
-    int buf = 0, pbuf = 0;
-    auto next_buf = [](int b_) __attribute__((always_inline)) { return b_ == L::kBufs - 1 ? 0 : b_ + 1; };
-    // iteration j of either schedule; `par` is j % 2 (the register set that tile j + 2
-    // is loaded into and tile j + 1 is staged from is the other one)
-    auto iteration = [&](auto par, int j) __attribute__((always_inline)) {
-        constexpr int p = decltype(par)::value;
-        const int nbuf = next_buf(buf);
-        if (j + 2 < nt) {
-            advance_load_rows(j + 2);
-            load_tile(std::integral_constant<int, p>{});
-        }
-        if (!rotated) {
-            qk(buf);
-            softmax(j);
-            pv(buf);
-            if (j + 1 < nt) {
-                advance_stage_pos(j + 1);
-                store_tile(std::integral_constant<int, 1 - p>{}, nbuf);
-            }
-        } else {
-            if (j > 0) {
-                softmax(j - 1);
-                pv(pbuf);
-            }
-            if (j + 1 < nt) {
-                advance_stage_pos(j + 1);
-                store_tile(std::integral_constant<int, 1 - p>{}, nbuf);
-            }
-            qk(buf);
-        }
-        __syncthreads();
-        pbuf = buf;
-        buf = nbuf;
+    // Buffer indices pass through readfirstlane, which keeps the compiler from turning every
+    // LDS address of the loop into an induction variable of its own.
+    auto opaque = [](int x) __attribute__((always_inline)) { return __builtin_amdgcn_readfirstlane(x); };
+    auto mfma_block = [&](int m) __attribute__((always_inline)) {
+        if (m >= 1) pv(opaque((m - 1) % 3));
+        if (m < nt) qk(opaque(m & 1));
     };
-    for (int j = 0; j < nt; j += 2) {
-        iteration(S0{}, j);
-        if (j + 1 < nt) iteration(S1{}, j + 1);
-    }
-    if (rotated) {
-        softmax(nt - 1);
-        pv(pbuf);
+    auto valu_block = [&](int m, int sm) __attribute__((always_inline)) {
+        if (m + 1 < nt) {
+            advance_v_rows(m + 1);
+            load_v(opaque((m + 1) % 3));
+        }
+        if (sm >= 0 && sm < nt) softmax(sm);
+        if (m + 1 < nt) {
+            advance_stage_pos(m + 1);
+            load_tab(kpos, kcs);
+            stage_k(opaque((m + 1) & 1));
+        }
+        if (m + 2 < nt) {
+            advance_k_rows(m + 2);
+            load_k();
+            wait_vm_loads_but<kVmOps>();   // this block's loads may stay in flight
+        } else {
+            wait_vm_loads();
+        }
+    };
+    // One loop per group, so that only P (group 0) or only S (group 1) is carried around
+    // each loop's back edge.
+    if (grp == 0) {
+        for (int m = 0; m <= nt; ++m) {
+            mfma_block(m);       // phase 2m+1
+            __syncthreads();
+            valu_block(m, m);    // phase 2m+2
+            __syncthreads();
+        }
+    } else {
+        for (int m = 0; m <= nt; ++m) {
+            valu_block(m, m - 1);   // phase 2m+1
+            __syncthreads();
+            mfma_block(m);          // phase 2m+2
+            __syncthreads();
+        }
     }
 
     // ---- epilogue: normalise and scatter rows back to their tokens ----
@@ -667,15 +733,20 @@ attn_fwd_kernel(AttnParams a) {
     }
 }
 
-template <int D, typename E>
-static hipError_t launch_attn_t(const AttnParams& a, hipStream_t stream) {
+template <int D, typename E, bool KDIV>
+static hipError_t launch_attn_k(const AttnParams& a, hipStream_t stream) {
     typedef Lds<D> L;
     const size_t lds = (size_t)L::kTabOff + (size_t)(a.T + a.H + a.W) * L::kTabRow;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_kernel<D, E>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_kernel<D, E, KDIV>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((attn_fwd_kernel<D, E>), dim3(a.num_work), dim3(kThreads), lds, stream, a);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, E, KDIV>), dim3(a.num_work), dim3(kThreads), lds, stream, a);
     return hipGetLastError();
+}
+
+template <int D, typename E>
+static hipError_t launch_attn_t(const AttnParams& a, hipStream_t stream) {
+    return a.k_divides_bn ? launch_attn_k<D, E, true>(a, stream) : launch_attn_k<D, E, false>(a, stream);
 }
 
 hipError_t launch_attn(const AttnParams& a, int head_dim, int dtype, hipStream_t stream) {
