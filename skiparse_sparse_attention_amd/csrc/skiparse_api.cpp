@@ -58,10 +58,12 @@ bool overlaps(const void* a, const void* b, int64_t bytes) {
 
 int to_status(hipError_t e) { return e == hipSuccess ? SKIPARSE_OK : SKIPARSE_E_DEVICE; }
 
-int remap_grid(int64_t tasks) {
-    // persistent-style grid: at most 8 blocks of 256 threads per CU of a 256-CU part
-    const int64_t blocks = (tasks + 255) / 256;
-    return (int)(blocks < 2048 ? (blocks > 0 ? blocks : 1) : 2048);
+int remap_grid(int64_t rows) {
+    // one wavefront per token row at a time, 4 per block; grid-stride loop over at most 16
+    // blocks per CU of a 256-CU part (more than are resident, which keeps the memory system
+    // fed while blocks start and drain)
+    const int64_t blocks = (rows + 3) / 4;
+    return (int)(blocks < 4096 ? (blocks > 0 ? blocks : 1) : 4096);
 }
 
 }  // namespace
@@ -132,7 +134,7 @@ int skiparse_rope_remap(const void* q, const void* k, const void* v, int B, int 
     a.B = B; a.T = T; a.H = H; a.W = W; a.heads = heads; a.k = sparse_k; a.mode = mode;
     a.L = (int)d.L; a.N = (int)d.N; a.rows = (int)(B * d.N);
     return to_status(skiparse::launch_rope_remap(a, head_dim, dtype, static_cast<hipStream_t>(stream),
-                                                 remap_grid((int64_t)a.rows * heads * 8)));
+                                                 remap_grid(a.rows)));
 }
 
 int skiparse_rearrange(const void* x, int B, int T, int H, int W, int heads, int head_dim,
@@ -151,7 +153,7 @@ int skiparse_rearrange(const void* x, int B, int T, int H, int W, int heads, int
     a.B = B; a.T = T; a.H = H; a.W = W; a.heads = heads; a.k = sparse_k; a.mode = mode;
     a.L = (int)d.L; a.N = (int)d.N; a.rows = (int)(B * d.N);
     return to_status(skiparse::launch_rope_remap(a, head_dim, dtype, static_cast<hipStream_t>(stream),
-                                                 remap_grid((int64_t)a.rows * heads * 8)));
+                                                 remap_grid(a.rows)));
 }
 
 int skiparse_reverse(const void* x, int B, int T, int H, int W, int heads, int head_dim,
@@ -167,7 +169,7 @@ int skiparse_reverse(const void* x, int B, int T, int H, int W, int heads, int h
     a.rows = (int)(B * d.N);
     a.row_bytes = (uint32_t)(heads * head_dim * d.esize);
     return to_status(skiparse::launch_reverse(a, static_cast<hipStream_t>(stream),
-                                              remap_grid((int64_t)a.rows * (a.row_bytes / 16))));
+                                              remap_grid(a.rows)));
 }
 
 int skiparse_scope_table(int64_t N, int sparse_k, int mode, int64_t* token_of) {

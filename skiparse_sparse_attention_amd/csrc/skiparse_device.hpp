@@ -50,33 +50,62 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // ---------------------------------------------------------------------------
 // 3D RoPE table
 // ---------------------------------------------------------------------------
+// Inverse frequencies 10000^(-2j/d_a) in fp64: inv[j] for the t axis (j < D/8, d_a = D/4),
+// then inv[D/8 + j] for the h and w axes (j < 3D/16, d_a = 3D/8).  kRopeFreqs doubles.
+template <int D>
+struct RopeFreqs {
+    static constexpr int kT = D / 8;
+    static constexpr int kHW = 3 * D / 16;
+    static constexpr int kCount = kT + kHW;
+};
+
+template <int D>
+__device__ __forceinline__ void rope_inv_freqs(double* inv) {
+    typedef RopeFreqs<D> F;
+    for (int i = threadIdx.x; i < F::kCount; i += blockDim.x) {
+        const bool t = i < F::kT;
+        const int j = t ? i : i - F::kT;
+        const double da = t ? (double)(D / 4) : (double)(3 * D / 8);
+        inv[i] = pow(10000.0, -2.0 * (double)j / da);
+    }
+}
+
+// (cos, sin) of pos * inv_freq: the angle is formed and reduced to [-pi, pi] in fp64 and
+// evaluated with the fp32 sincos, within about one fp32 ulp of the fp64 values.
+__device__ __forceinline__ float2 rope_cos_sin(int pos, double inv_freq) {
+    const double theta = (double)pos * inv_freq;
+    const double q = rint(theta * 0.15915494309189533577);     // 1 / (2 pi)
+    const float r = (float)fma(-q, 6.2831853071795864769, theta);
+    float sn, cs;
+    sincosf(r, &sn, &cs);
+    return make_float2(cs, sn);
+}
+
 // Layout (float2 = (cos, sin)):
 //   [0, T*D/8)                      t axis: entry pos*(D/8) + j,    j < d_t/2 = D/8
 //   [T*D/8, +H*3D/16)               h axis: entry pos*(3D/16) + j,  j < d_h/2 = 3D/16
 //   [.., +W*3D/16)                  w axis: entry pos*(3D/16) + j,  j < d_w/2 = 3D/16
-// Entry value: cos/sin of pos * 10000^(-2j/d_a), evaluated in double and
-// rounded to float.
+// Entry value: cos/sin of pos * 10000^(-2j/d_a) (rope_cos_sin).  `inv` is LDS scratch of
+// RopeFreqs<D>::kCount doubles; the function ends with a workgroup barrier.
 template <int D>
-__device__ __forceinline__ void build_rope_table(float2* tab, int T, int H, int W) {
-    constexpr int kT = D / 8;        // pairs per t position
-    constexpr int kHW = 3 * D / 16;  // pairs per h or w position
-    const int nt = T * kT, nh = H * kHW, nw = W * kHW;
+__device__ __forceinline__ void build_rope_table(float2* tab, int T, int H, int W, double* inv) {
+    typedef RopeFreqs<D> F;
+    rope_inv_freqs<D>(inv);
+    __syncthreads();
+    const int nt = T * F::kT, nh = H * F::kHW, nw = W * F::kHW;
     const int total = nt + nh + nw;
     for (int e = threadIdx.x; e < total; e += blockDim.x) {
-        int pos, j, da;
+        int pos, j;
         if (e < nt) {
-            pos = e / kT; j = e - pos * kT; da = D / 4;
+            pos = e / F::kT; j = e - pos * F::kT;
         } else if (e < nt + nh) {
-            int r = e - nt; pos = r / kHW; j = r - pos * kHW; da = 3 * D / 8;
+            const int r = e - nt; pos = r / F::kHW; j = F::kT + r - pos * F::kHW;
         } else {
-            int r = e - nt - nh; pos = r / kHW; j = r - pos * kHW; da = 3 * D / 8;
+            const int r = e - nt - nh; pos = r / F::kHW; j = F::kT + r - pos * F::kHW;
         }
-        double inv_freq = pow(10000.0, -2.0 * (double)j / (double)da);
-        double theta = (double)pos * inv_freq;
-        double sn, cs;
-        sincos(theta, &sn, &cs);
-        tab[e] = make_float2((float)cs, (float)sn);
+        tab[e] = rope_cos_sin(pos, inv[j]);
     }
+    __syncthreads();
 }
 
 // Offset of the table row of (axis, pos); entries j follow contiguously.
