@@ -37,6 +37,8 @@ def parse_args():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
     ap.add_argument("--no-remap", action="store_true", help="skip the standalone RoPE+remap pass")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the per-workload attention timings (other grids, k in {1,2,4,8})")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -96,6 +98,42 @@ def cpu_baseline(w, q, k, v, budget_s=15.0):
         "sample": (f"{nrows} query tokens of scope 0 (all {w.heads} heads, all {w.L} keys of the scope) "
                    f"of {w.name}, fp64 numpy, {t:.1f} s"),
     }
+
+
+def sweep(sk, wl, stream, reps=3):
+    """Fused-attention TFLOP/s on the other workloads (median of `reps` launches after one warmup
+    launch, HIP events on the launch stream): the k sweep on the 24x22x40 grid and the larger grids."""
+    import torch
+    works = []
+    for k_ in (1, 2, 4, 8):
+        for mode in (0, 1):
+            works.append(wl.OSP_SINGLE.with_mode(mode, sparse_k=k_))
+    works += [wl.HC_GROUP, wl.WAN_DENSE, wl.LONG_GROUP, wl.LONG_SINGLE]
+    res = {}
+    cache = {}
+    for w in works:
+        key = (w.B, w.T, w.H, w.W, w.heads, w.head_dim, w.scale)
+        if key not in cache:
+            cache.clear()
+            cache[key] = tuple(t.cuda() for t in wl.make_inputs(w, seed=0, device="cpu"))
+        q, k, v = cache[key]
+        out = torch.empty_like(q)
+        sk.attn(q, k, v, w.grid, w.sparse_k, w.mode, out=out, stream=stream)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev[0].record(stream)
+        for i in range(reps):
+            sk.attn(q, k, v, w.grid, w.sparse_k, w.mode, out=out, stream=stream)
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        ms = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(reps))[reps // 2]
+        flops = sk.attn_flops(w.B, w.grid, w.heads, w.head_dim, w.sparse_k)
+        tf = flops / (ms * 1e-3) / 1e12
+        name = f"{w.T}x{w.H}x{w.W}_b{w.B}_h{w.heads}_k{w.sparse_k}_{'single' if w.mode == 0 else 'group'}"
+        res[name] = {"N": w.N, "ms": round(ms, 4), "tflops": round(tf, 1),
+                     "pct_of_bf16_peak": round(100.0 * tf / PEAK_BF16_TFLOPS, 2)}
+        del out
+    cache.clear()
+    return res
 
 
 def main():
@@ -219,6 +257,9 @@ def main():
             "bytes_per_launch": nbytes,
         }
         del rq, rk, rv
+
+    if not args.no_sweep:
+        result["sweep"] = sweep(sk, wl, stream)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(ws, q, k, v)
