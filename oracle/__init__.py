@@ -10,6 +10,7 @@ from .skiparse_oracle import (  # noqa: F401
     ROPE_BASE,
     SINGLE,
     attention,
+    attention_backward,
     group_skip_rearrange,
     group_skip_reverse,
     rearrange,
@@ -17,12 +18,16 @@ from .skiparse_oracle import (  # noqa: F401
     reverse_rows,
     rope_3d,
     rope_3d_at,
+    rope_3d_transpose_at,
     rope_axis_sizes,
     rope_rearrange,
     scope_table,
     single_skip_rearrange,
     single_skip_reverse,
     skiparse_attention,
+    skiparse_attention_backward,
+    skiparse_attention_backward_scope,
+    skiparse_backward_flops,
     skiparse_attention_rows,
     skiparse_flops,
     token_positions,

@@ -40,6 +40,13 @@ Token flattening: n = (t*H + h)*W + w (Wan 2.1 report, section 4.2.1
 "Video Diffusion Transformer": the patchified latent is flattened into a
 (B, L, D) sequence).
 
+The backward (gradients of a loss through the whole forward) follows the same
+steps in reverse, by the chain rule: scatter the output gradient into the
+scopes, differentiate softmax attention inside each scope, rotate the q and k
+gradients back with the transposed RoPE rotation, and scatter them to their
+original tokens.  Open-Sora Plan's page says Skiparse exists to speed up
+training, which is what needs these gradients.
+
 Every pin of this module lives in ``tests/test_oracle_pins.py``.
 """
 
@@ -117,6 +124,18 @@ def rope_3d(x, T: int, H: int, W: int, base: float = ROPE_BASE):
     """3D RoPE of a full (B, N, heads, d) tensor laid out on the T x H x W grid."""
     t, h, w = token_positions(T, H, W)
     return rope_3d_at(x, t, h, w, base)
+
+
+def rope_3d_transpose_at(x, t, h, w, base: float = ROPE_BASE):
+    """The transpose of :func:`rope_3d_at`: every rotate-half pair turned by -theta.
+
+    RoPE rotates each pair (x1, x2) by the angle theta, i.e. multiplies it by
+    [[cos, -sin], [sin, cos]]; the transpose of that matrix is the rotation by
+    -theta.  Since theta = pos * freq is linear in the position, turning by
+    -theta is RoPE at the negated positions.  This is what carries a gradient
+    with respect to rotated q or k back to the unrotated input.
+    """
+    return rope_3d_at(x, -np.asarray(t), -np.asarray(h), -np.asarray(w), base)
 
 
 # ---------------------------------------------------------------------------
@@ -219,6 +238,35 @@ def attention(q, k, v):
     return np.matmul(p, v)
 
 
+def attention_backward(q, k, v, do):
+    """Gradients of sum(attention(q, k, v) * do) with respect to q, k and v, float64.
+
+    One (L, d) problem per leading index, as in :func:`attention`.  The chain
+    rule written out, with S = q k^T / sqrt(d), P = softmax(S) row-wise and
+    O = P v:
+        dv = P^T do
+        dP = do v^T
+        dS = P * (dP - rowsum(dP * P))      (the softmax Jacobian, row by row)
+        dq = dS k / sqrt(d)
+        dk = dS^T q / sqrt(d)
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    d = q.shape[-1]
+    s = np.matmul(q, np.swapaxes(k, -1, -2)) / math.sqrt(d)
+    s = s - s.max(axis=-1, keepdims=True)
+    p = np.exp(s)
+    p = p / p.sum(axis=-1, keepdims=True)
+    dv = np.matmul(np.swapaxes(p, -1, -2), do)
+    dp = np.matmul(do, np.swapaxes(v, -1, -2))
+    ds = p * (dp - (dp * p).sum(axis=-1, keepdims=True))
+    dq = np.matmul(ds, k) / math.sqrt(d)
+    dk = np.matmul(np.swapaxes(ds, -1, -2), q) / math.sqrt(d)
+    return dq, dk, dv
+
+
 # ---------------------------------------------------------------------------
 # The full Skiparse forward
 # ---------------------------------------------------------------------------
@@ -298,6 +346,68 @@ def skiparse_attention_rows(q, k, v, T, H, W, sparse_k, mode, batch_idx, token_i
         o = attention(qq.transpose(1, 0, 2), kk.transpose(1, 0, 2), vv.transpose(1, 0, 2))
         out[sel] = o.transpose(1, 0, 2)
     return out
+
+
+def skiparse_attention_backward(q, k, v, do, T, H, W, sparse_k, mode, base=ROPE_BASE):
+    """Gradients (dq, dk, dv) of sum(skiparse_attention(q, k, v) * do), float64.
+
+    All arrays (B, N, heads, d).  The forward's steps taken backwards:
+    the output gradient ``do`` goes through the same rearrange as v (the
+    reverse's adjoint is the forward rearrange, since the permutation is a
+    bijection); softmax attention is differentiated per rearranged batch row
+    and head (:func:`attention_backward`); the gradients are reversed to the
+    original token order; the q and k gradients are rotated back by the
+    transposed RoPE (:func:`rope_3d_transpose_at`).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    B, N, heads, d = q.shape
+    if N != T * H * W:
+        raise ValueError("N must equal T*H*W")
+    rq = rope_rearrange(q, T, H, W, sparse_k, mode, True, base)
+    rk = rope_rearrange(k, T, H, W, sparse_k, mode, True, base)
+    rv = rope_rearrange(v, T, H, W, sparse_k, mode, False, base)
+    rdo = rope_rearrange(do, T, H, W, sparse_k, mode, False, base)
+    tr = lambda x: x.transpose(0, 2, 1, 3)
+    dq, dk, dv = attention_backward(tr(rq), tr(rk), tr(rv), tr(rdo))
+    dq = reverse_rows(tr(dq), sparse_k, mode)
+    dk = reverse_rows(tr(dk), sparse_k, mode)
+    dv = reverse_rows(tr(dv), sparse_k, mode)
+    t, h, w = token_positions(T, H, W)
+    return rope_3d_transpose_at(dq, t, h, w, base), rope_3d_transpose_at(dk, t, h, w, base), dv
+
+
+def skiparse_attention_backward_scope(q, k, v, do, T, H, W, sparse_k, mode, b, s, heads_idx,
+                                      base=ROPE_BASE):
+    """Gradients of every member token of scope ``s`` of batch ``b``, selected heads only.
+
+    Returns (tokens, dq, dk, dv): ``tokens`` are the scope's member token
+    indices in in-scope order, and dq/dk/dv are (L, len(heads_idx), d).  The
+    gradients of a scope depend only on that scope's rows (no token belongs
+    to two scopes), so this is :func:`skiparse_attention_backward` restricted
+    to one scope, for checking large inputs on a sample.
+    """
+    heads_idx = np.asarray(heads_idx, dtype=np.int64)
+    B, N, heads, d = np.shape(q)
+    members = scope_table(N, sparse_k, mode)[s]
+    t_all, h_all, w_all = token_positions(T, H, W)
+    tm, hm, wm = t_all[members], h_all[members], w_all[members]
+    sel = lambda x: np.asarray(x[b][members][:, heads_idx], dtype=np.float64)
+    qq = rope_3d_at(sel(q), tm, hm, wm, base)
+    kk = rope_3d_at(sel(k), tm, hm, wm, base)
+    tr = lambda x: x.transpose(1, 0, 2)
+    dq, dk, dv = attention_backward(tr(qq), tr(kk), tr(sel(v)), tr(sel(do)))
+    dq = rope_3d_transpose_at(tr(dq), tm, hm, wm, base)
+    dk = rope_3d_transpose_at(tr(dk), tm, hm, wm, base)
+    return members, dq, dk, tr(dv)
+
+
+def skiparse_backward_flops(B, N, heads, head_dim, sparse_k):
+    """Backward attention FLOPs counted for a Skiparse call: 8 * B * heads * N * (N/k) * d.
+
+    Wan 2.1 report, section 4.3.1: the backward pass of attention costs twice
+    the forward (beta = 8 against 4), applied to k scopes of length N/k.
+    """
+    return 8.0 * B * heads * N * (N // sparse_k) * head_dim
 
 
 def skiparse_flops(B, N, heads, head_dim, sparse_k):
