@@ -95,6 +95,61 @@ int skiparse_attn(const void* q, const void* k, const void* v,
                   int sparse_k, int mode, int dtype, void* out, void* stream);
 
 /*
+ * skiparse_attn_lse -- skiparse_attn that also writes, for the backward pass,
+ * each output row's log2-sum-exp.
+ *
+ * Everything as skiparse_attn, plus
+ * lse : (B, heads, N) fp32, device memory, caller-owned; entry
+ *       [b, head, n] = log2 of sum_m 2^(z_nm), with z_nm = (q'_n . k'_m) *
+ *       log2(e) / sqrt(head_dim) over the members m of token n's scope (q', k'
+ *       the rotated rows): the softmax denominator of row n in base-2 units of
+ *       the scaled scores.  Must not overlap q, k, v or out.
+ * The same single kernel launch; the rows of lse are written in its epilogue.
+ */
+int skiparse_attn_lse(const void* q, const void* k, const void* v,
+                      int B, int T, int H, int W, int heads, int head_dim,
+                      int sparse_k, int mode, int dtype, void* out, float* lse,
+                      void* stream);
+
+/*
+ * skiparse_attn_bwd -- gradients of a loss through skiparse_attn (the chain
+ * rule of steps 1-4, taken backwards).  Open-Sora Plan's page says Skiparse
+ * exists to speed up training; these are the gradients training needs.
+ *
+ * q, k, v : the forward inputs, (B, N, heads, head_dim) in `dtype`.
+ * out     : the forward output (skiparse_attn_lse's out), same layout.
+ * dout    : gradient of the loss with respect to out, same layout.
+ * lse     : skiparse_attn_lse's log2-sum-exp of the same call, (B, heads, N) fp32.
+ * dq, dk, dv : gradients with respect to q, k, v, (B, N, heads, head_dim) in
+ *           `dtype`, original token order; dq and dk include the transposed RoPE
+ *           rotation (each rotate-half pair turned back by -theta).
+ * delta   : (B, heads, N) fp32 workspace, caller-owned: receives
+ *           rowsum(dout * out) of every row (written, then read, by this call).
+ * Per scope, with Z = q' k'^T / sqrt(d) and P = softmax(Z):
+ *   dv = P^T dout,  dZ = P * (dout v^T - delta),  dq' = dZ k' / sqrt(d),
+ *   dk' = dZ^T q' / sqrt(d),  dq and dk = the transposed RoPE of dq', dk'.
+ * Precision: bf16 operands on the matrix cores, fp32 accumulation, P and dZ
+ *   rounded to bf16 as MFMA operands, delta and the rotations in fp32.
+ * Two kernel launches on `stream` (dq and delta first, then dk and dv).  No
+ * output (dq, dk, dv, delta) may overlap any input or another output.  Same
+ * size limits as skiparse_attn.  Returns SKIPARSE_OK or an error code.
+ */
+int skiparse_attn_bwd(const void* q, const void* k, const void* v,
+                      const void* out, const void* dout, const float* lse,
+                      int B, int T, int H, int W, int heads, int head_dim,
+                      int sparse_k, int mode, int dtype,
+                      void* dq, void* dk, void* dv, float* delta, void* stream);
+
+/*
+ * skiparse_attn_bwd_flops -- FLOPs counted for one skiparse_attn_bwd call:
+ * twice the forward's (Wan 2.1 report, section 4.3.1: the backward of
+ * non-causal attention costs 8*b*s^2*h against 4 forward), i.e.
+ * 8*B*heads*N*(N/k)*head_dim.  Negative for invalid sizes.
+ */
+double skiparse_attn_bwd_flops(int B, int T, int H, int W, int heads, int head_dim,
+                               int sparse_k);
+
+/*
  * skiparse_rope_remap -- the materialised RoPE + rearrange of q, k and v in
  * one pass (the page's add_rope + *_skip_rearrange calls, before attention).
  *

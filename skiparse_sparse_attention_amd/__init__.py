@@ -22,7 +22,10 @@ from ._lib import (  # noqa: F401
     SINGLE,
     SkiparseError,
     attn,
+    attn_bwd,
+    attn_bwd_flops,
     attn_flops,
+    attn_lse,
     lib,
     rearrange,
     reverse,

@@ -62,6 +62,12 @@ def lib():
         L.skiparse_scope_table.restype = i
         L.skiparse_attn_flops.argtypes = [i] * 7
         L.skiparse_attn_flops.restype = ctypes.c_double
+        L.skiparse_attn_lse.argtypes = [vp, vp, vp] + dims + [i, i, i, vp, vp, vp]
+        L.skiparse_attn_lse.restype = i
+        L.skiparse_attn_bwd.argtypes = [vp] * 6 + dims + [i, i, i] + [vp] * 5
+        L.skiparse_attn_bwd.restype = i
+        L.skiparse_attn_bwd_flops.argtypes = [i] * 7
+        L.skiparse_attn_bwd_flops.restype = ctypes.c_double
         L.skiparse_status_string.argtypes = [i]
         L.skiparse_status_string.restype = ctypes.c_char_p
         L.skiparse_version.argtypes = []
@@ -123,6 +129,54 @@ def attn(q, k, v, grid, sparse_k, mode, out=None, stream=None):
                                int(sparse_k), int(mode), _dtype_code(q), out.data_ptr(),
                                _stream_ptr(stream)), "skiparse_attn")
     return out
+
+
+def attn_lse(q, k, v, grid, sparse_k, mode, out=None, lse=None, stream=None):
+    """Fused Skiparse attention that also returns each row's log2-sum-exp (B, heads, N) fp32."""
+    import torch
+    B, T, H, W, heads, d = _dims(q, grid)
+    for t in (k, v):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
+            raise ValueError("q, k, v must share shape, dtype and be contiguous")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, heads, T * H * W), dtype=torch.float32, device=q.device)
+    _check(lib().skiparse_attn_lse(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, T, H, W, heads, d,
+                                   int(sparse_k), int(mode), _dtype_code(q), out.data_ptr(),
+                                   lse.data_ptr(), _stream_ptr(stream)), "skiparse_attn_lse")
+    return out, lse
+
+
+def attn_bwd(q, k, v, out, dout, lse, grid, sparse_k, mode, grads=None, delta=None, stream=None):
+    """Gradients (dq, dk, dv) of a loss through Skiparse attention, given dout = dLoss/dout.
+
+    ``out`` and ``lse`` come from :func:`attn_lse` on the same inputs; ``delta`` is an
+    optional (B, heads, N) fp32 workspace.
+    """
+    import torch
+    B, T, H, W, heads, d = _dims(q, grid)
+    for t in (k, v, out, dout):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
+            raise ValueError("q, k, v, out, dout must share shape, dtype and be contiguous")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, heads, T * H * W) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous (B, heads, N) float32 tensor")
+    if grads is None:
+        grads = tuple(torch.empty_like(q) for _ in range(3))
+    if delta is None:
+        delta = torch.empty((B, heads, T * H * W), dtype=torch.float32, device=q.device)
+    dq, dk, dv = grads
+    _check(lib().skiparse_attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                   dout.data_ptr(), lse.data_ptr(), B, T, H, W, heads, d,
+                                   int(sparse_k), int(mode), _dtype_code(q), dq.data_ptr(),
+                                   dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
+                                   _stream_ptr(stream)), "skiparse_attn_bwd")
+    return dq, dk, dv
+
+
+def attn_bwd_flops(B, grid, heads, head_dim, sparse_k):
+    T, H, W = (int(g) for g in grid)
+    return float(lib().skiparse_attn_bwd_flops(int(B), T, H, W, int(heads), int(head_dim), int(sparse_k)))
 
 
 def rope_remap(q, k, v, grid, sparse_k, mode, outs=None, stream=None):

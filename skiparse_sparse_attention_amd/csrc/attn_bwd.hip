@@ -1,0 +1,624 @@
+// Fused Skiparse attention backward for gfx950 (CDNA4).
+//
+// Gradients through the forward of attn_fwd.hip (3D RoPE on q and k at the original grid
+// positions, Single/Group Skip scopes, softmax attention per scope, scatter back to the
+// original tokens).  Given dO (the loss gradient of the output, original token order), the
+// forward output O and the forward's per-row log2-sum-exp, compute dQ, dK, dV in the original
+// token order.  Per (batch, head, scope), with Z = c q' k'^T (c = 1/sqrt(d); q', k' rotated)
+// and P = softmax(Z) row-wise, the chain rule gives
+//   D   = rowsum(dO * O)                (equal to rowsum(P * dP))
+//   dV  = P^T dO
+//   dP  = dO V^T,  dZ = P * (dP - D)
+//   dq' = c dZ k',  dk' = c dZ^T q'
+// and dq, dk are dq', dk' turned back by the transposed RoPE rotation (each rotate-half pair
+// by -theta).  Wan 2.1 report, section 4.3.1, prices this backward at twice the forward.
+//
+// Two kernels, both recomputing P from the scores and the saved log2-sum-exp:
+//   attn_bwd_dq_kernel: one workgroup per (batch, head, scope, 128-query tile), 4 wavefronts
+//     of 32 queries.  It computes D of its queries (and stores it for the second kernel),
+//     then streams the scope's 64-key K/V tiles: S^T = K Q'^T onto -LSE, P^T = exp2(S^T),
+//     dP^T = V dO^T, dZ^T = P^T * (dP^T - D), dQ'^T += K^T dZ^T, the K^T operands read from
+//     the row-major K tile with the LDS transpose read.
+//   attn_bwd_dkdv_kernel: one workgroup per (batch, head, scope, 128-key tile), 4 wavefronts
+//     of 32 keys holding K'^T and V^T as B operands; streams the scope's 32-query tiles:
+//     S = Q' K'^T onto -LSE, P, dP = dO V^T, dZ, dV^T += dO^T P, dK^T += Q'^T dZ, the dO^T
+//     and Q'^T operands again from transpose reads.
+// Rows are gathered through the scope map on load (q and k rotated while staged into LDS
+// from the banked RoPE table), the transposed rotation is applied in registers in the
+// epilogue, and every gradient row is written straight to its original token.  Keys past the
+// end of a scope start at -inf (weight exactly 0); queries past the end carry an infinite
+// log2-sum-exp (weight 0) and D = 0.
+#include "attn_common.hpp"
+#include "skiparse_device.hpp"
+#include "skiparse_launch.hpp"
+
+namespace skiparse {
+
+using namespace attn;
+
+namespace {
+
+constexpr int kBwdThreads = 256;   // 4 wavefronts, one per SIMD
+constexpr int kBwdRows = 128;      // queries (dq kernel) or keys (dk/dv kernel) per workgroup
+constexpr int kBwdKN = 64;         // keys per K/V tile of the dq kernel
+constexpr int kBwdQN = 32;         // queries per query tile of the dk/dv kernel
+
+template <int D>
+struct BwdLds {
+    static constexpr int kPitch = D * 2 + 16;   // rotated Q/K rows, pair-slot order, one pad granule
+    static constexpr int kVPitch = D * 2;       // V / dO rows, natural order, swizzled granules
+    // dq kernel: two K tiles (the Q staging of 128 rows aliases them), two V tiles, the table
+    static constexpr int kKTile = kBwdKN * kPitch;
+    static constexpr int kVTile = kBwdKN * kVPitch;
+    static constexpr int kDqTab = 2 * kKTile + 2 * kVTile;
+    static_assert(kBwdRows * kPitch <= 2 * kKTile, "Q staging fits the K tiles");
+    // dk/dv kernel: K staging (128 rows), aliased afterwards by two Q and two dO tiles; the
+    // log2-sum-exp and D of two query tiles; the table
+    static constexpr int kQTile = kBwdQN * kPitch;
+    static constexpr int kOTile = kBwdQN * kVPitch;
+    static constexpr int kStage = kBwdRows * kPitch;
+    static constexpr int kLdOff = kStage;
+    static constexpr int kDkvTab = kStage + 2 * 2 * kBwdQN * 4;
+    static_assert(2 * kQTile + 2 * kOTile <= kStage, "query tiles fit the staging area");
+};
+
+// 8 consecutive elements of E as a bf16x8 operand, and as floats (bf16 is exact both ways).
+template <typename E>
+__device__ __forceinline__ bf16x8 load8(__amdgpu_buffer_rsrc_t r, int off, float (&x)[8]) {
+    ChunkRaw<E, 8> raw;
+    buffer_load_dwords(r, off, raw.w);
+    raw_to_f32(raw, x);
+    bf16x8 v;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = (__bf16)x[i];
+    return v;
+}
+
+// Per-lane addresses of the LDS transpose reads that form an A operand from a tile whose rows
+// are the contraction index: within each group of 16 lanes, lane i = 4t + q points at 4
+// consecutive columns of row t; the instruction hands lane j the value at column c0 + j of
+// each of those 4 rows.  Lanes 0-31 take rows {0-3, 8-11} and lanes 32-63 rows {4-7, 12-15}
+// of every 16-row step (the order in which a 32x32 accumulator holds its rows for the B
+// operand of the next product), columns 32 db + lane % 32.  Row 8 h8 + tr_row, granule
+// 4 db + tr_gran (XOR the row swizzle of V/dO tiles), byte tr_byte.
+struct TrLane {
+    int row, gran, byte;
+    __device__ __forceinline__ TrLane(int lane) {
+        const int i = lane & 15;
+        row = (i >> 2) + 4 * (lane >> 5);
+        gran = 2 * ((lane >> 4) & 1) + ((i & 3) >> 1);
+        byte = (i & 1) * 8;
+    }
+};
+
+// A operand (8 bf16) of one 16-row step from two transpose reads at row offsets 0 and 8.
+__device__ __forceinline__ bf16x8 tr_operand(const char* p0, const char* p8) {
+    const i16x4 lo = ds_read_tr16(p0);
+    const i16x4 hi = ds_read_tr16(p8);
+    const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+// Epilogue shared by dQ and dK: acc[db] holds the transposed gradient of one token per lane
+// (column lane % 32) with rows d-slot = 32 db + 8 g + 4 (lane / 32) + jj in the pair-slot order
+// of the Q/K tiles (slot 2 cp: chunk c1 of pair cp, slot 2 cp + 1: its partner c2).  Turns
+// every rotate-half pair back by -theta at the token's grid position, multiplies by `scale`,
+// and stores the row of token n (offsets past the slice are dropped) in natural head_dim order.
+template <int D, typename E>
+__device__ __forceinline__ void store_unrotated(const f32x16 (&acc)[D / 32], float scale, __amdgpu_buffer_rsrc_t out,
+                                                int n, int row_bytes, const Pos& q, const char* tab, int T, int H,
+                                                int phi_mul, int lane) {
+    constexpr int CH = D / 16;
+    constexpr int ES = E::kBytes;
+    constexpr int DB = D / 32;
+    const int hf = lane >> 5;
+    auto entry = [&](int cp, int e) __attribute__((always_inline)) {
+        const RopePair rp = rope_pair(cp);
+        const int pos = rp.axis == 0 ? min(q.t, T - 1) : (rp.axis == 1 ? q.h : q.w);
+        return *reinterpret_cast<const float2*>(tab + rope_tab_offset<D>(T, H, rp.axis, pos, rp.jchunk * CH + e,
+                                                                        rp.axis == 2 ? phi_mul : 0));
+    };
+    auto store4 = [&](int chunk, int e0, const float (&y)[4]) __attribute__((always_inline)) {
+        const int off = n * row_bytes + (chunk * CH + e0) * ES;
+        if constexpr (ES == 2) {
+            const u32x2 v2 = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+            __builtin_amdgcn_raw_buffer_store_b64(v2, out, off, 0, 0);
+        } else {
+            const u32x4 v4 = {__float_as_uint(y[0]), __float_as_uint(y[1]), __float_as_uint(y[2]), __float_as_uint(y[3])};
+            __builtin_amdgcn_raw_buffer_store_b128(v4, out, off, 0, 0);
+        }
+    };
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+        if constexpr (CH == 8) {
+            // granule 4 db + g is slot 4 db + g: g even holds c1 elements, g + 1 their partners
+#pragma unroll
+            for (int g = 0; g < 4; g += 2) {
+                const int cp = 2 * db + g / 2;
+                const RopePair rp = rope_pair(cp);
+                float y1[4], y2[4];
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int e = 4 * hf + jj;
+                    const float2 cs = entry(cp, e);
+                    const float a1 = acc[db][4 * g + jj], a2 = acc[db][4 * (g + 1) + jj];
+                    y1[jj] = (a1 * cs.x + a2 * cs.y) * scale;
+                    y2[jj] = (a2 * cs.x - a1 * cs.y) * scale;
+                }
+                store4(rp.c1, 4 * hf, y1);
+                store4(rp.c2, 4 * hf, y2);
+            }
+        } else {
+            // CH = 4: slot 8 db + 2 g + hf, so a c1 element's partner sits in the lane 32 away
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int cp = 4 * db + g;
+                const RopePair rp = rope_pair(cp);
+                float y[4];
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const float own = acc[db][4 * g + jj];
+                    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(own), __float_as_uint(own), false, false);
+                    const float other = __uint_as_float(hf ? sw[0] : sw[1]);
+                    const float a1 = hf ? other : own, a2 = hf ? own : other;
+                    const float2 cs = entry(cp, jj);
+                    y[jj] = (hf ? (a2 * cs.x - a1 * cs.y) : (a1 * cs.x + a2 * cs.y)) * scale;
+                }
+                store4(hf ? rp.c2 : rp.c1, 0, y);
+            }
+        }
+    }
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------------------------
+// dQ (and D)
+// ---------------------------------------------------------------------------------------------
+template <int D, typename E>
+__global__ void __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+attn_bwd_dq_kernel(AttnBwdParams a) {
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    typedef BwdLds<D> L;
+    constexpr int CH = D / 16;
+    constexpr int KS = D / 16;        // 16-deep k-steps over head_dim
+    constexpr int DB = D / 32;        // 32-row blocks of head_dim
+    constexpr int KB = kBwdKN / 32;   // 32-key blocks per tile
+    constexpr int KK = kBwdKN / 16;   // 16-key steps per tile
+    constexpr int ES = E::kBytes;
+    constexpr int G = D / 8;          // 16-byte granules per V row (bf16)
+    constexpr int kVPer = kBwdKN * G / kBwdThreads;   // V granules per thread per tile
+    char* ktile = lds;
+    char* vtile = lds + 2 * L::kKTile;
+    char* tab = lds + L::kDqTab;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, hf = lane >> 5;
+    const int work = xcd_remap(blockIdx.x, gridDim.x);
+    const int qt = work % a.tiles;
+    const int sc = work / a.tiles;
+    const int s = sc % a.sparse_k;
+    const int bh = sc / a.sparse_k;
+    const int head = bh % a.heads;
+    const int b = bh / a.heads;
+    const int64_t k_ = a.sparse_k;
+    const int row_bytes = a.heads * D * ES;
+    const int64_t slice = ((int64_t)b * a.N * a.heads + head) * D * ES;
+    const int slice_bytes = a.N * row_bytes - head * D * ES;
+    auto rsrc = [&](const void* base) __attribute__((always_inline)) {
+        return __builtin_amdgcn_make_buffer_rsrc((void*)(reinterpret_cast<const char*>(base) + slice), (short)0,
+                                                 slice_bytes, 0x00020000);
+    };
+    const __amdgpu_buffer_rsrc_t qbuf = rsrc(a.q), kbuf = rsrc(a.k), vbuf = rsrc(a.v), obuf = rsrc(a.o),
+                                 dobuf = rsrc(a.dout), dqbuf = rsrc(a.dq);
+    const int64_t vec0 = ((int64_t)b * a.heads + head) * a.N;   // (b, head) row of lse / delta
+    const int HW = a.H * a.W;
+    auto pos_of = [&](int nn) __attribute__((always_inline)) {
+        Pos q;
+        q.t = nn / HW; q.h = (nn / a.W) % a.H; q.w = nn % a.W;
+        return q;
+    };
+
+    build_banked_rope_table<D>(tab, a.T, a.H, a.W, a.phi_mul);
+    const int cp = tid & 7;
+    const RopePair rp = rope_pair(cp);
+    __syncthreads();
+
+    // ---- Q tile: rotated, scaled by log2(e)/sqrt(d), through LDS into B-operand registers ----
+#pragma unroll 2
+    for (int it = 0; it < kBwdRows * 8 / kBwdThreads; ++it) {
+        const int r = (tid >> 3) + it * (kBwdThreads / 8);
+        const int n = (int)scope_token(qt * kBwdRows + r, s, k_, a.mode);   // >= N past the scope end
+        stage_rotated_pair<D, E>(qbuf, n * row_bytes, rp, cp, tab, a.T, a.H, pos_of(n), a.phi_mul, a.scale_log2,
+                                 ktile + r * L::kPitch);
+    }
+    __syncthreads();
+    bf16x8 qreg[KS];
+    {
+        const char* qrow = ktile + (wave * 32 + l32) * L::kPitch;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qreg[ks] = *reinterpret_cast<const bf16x8*>(qrow + (2 * ks + hf) * 16);
+    }
+    __syncthreads();   // the staging rows become K tiles
+
+    // ---- this lane's query: dO as the B operand of dP^T = V dO^T (natural order), D, LSE ----
+    const int pq = qt * kBwdRows + wave * 32 + l32;
+    const int nq = (int)scope_token(pq, s, k_, a.mode);
+    const bool qvalid = pq < a.L;
+    bf16x8 doreg[KS];
+    float dsum = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        const int off = nq * row_bytes + (2 * ks + hf) * 8 * ES;
+        float xd[8], xo[8];
+        doreg[ks] = load8<E>(dobuf, off, xd);
+        load8<E>(obuf, off, xo);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dsum += xd[e] * xo[e];
+    }
+    {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(dsum), __float_as_uint(dsum), false, false);
+        dsum = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    }
+    const float dq_d = qvalid ? dsum : 0.f;
+    if (qvalid && hf == 0) a.delta[vec0 + nq] = dq_d;
+    const float lse_q = qvalid ? a.lse[vec0 + nq] : 0.f;
+
+    // ---- K/V tiles: loaded into registers one tile ahead, staged at the end of a tile ----
+    const int krow = tid >> 3;   // K staging tasks: rows krow and krow + 32, chunk pair cp
+    ChunkRaw<E, CH> kraw[2][2];
+    Pos kpos[2];
+    uint32_t vraw[kVPer][4];
+    auto load_kv = [&](int t) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int n = (int)scope_token(t * kBwdKN + krow + 32 * i, s, k_, a.mode);
+            buffer_load_dwords(kbuf, n * row_bytes + rp.c1 * CH * ES, kraw[i][0].w);
+            buffer_load_dwords(kbuf, n * row_bytes + rp.c2 * CH * ES, kraw[i][1].w);
+            kpos[i] = pos_of(n);
+        }
+#pragma unroll
+        for (int i = 0; i < kVPer; ++i) {
+            const int idx = tid + kBwdThreads * i;
+            const int n = (int)scope_token(t * kBwdKN + idx / G, s, k_, a.mode);
+            buffer_load_8_as_bf16x2<E>(vbuf, n * row_bytes + (idx % G) * 8 * ES, vraw[i]);
+        }
+    };
+    auto store_kv = [&](int buf) __attribute__((always_inline)) {
+        char* kd = ktile + buf * L::kKTile;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            float x1[CH], x2[CH];
+            raw_to_f32(kraw[i][0], x1);
+            raw_to_f32(kraw[i][1], x2);
+            const int pos = rp.axis == 0 ? min(kpos[i].t, a.T - 1) : (rp.axis == 1 ? kpos[i].h : kpos[i].w);
+            const char* row = tab + rope_tab_offset<D>(a.T, a.H, rp.axis, pos, rp.jchunk * CH, rp.axis == 2 ? a.phi_mul : 0);
+            f32x4 cs[CH / 2];
+#pragma unroll
+            for (int j = 0; j < CH / 2; ++j) cs[j] = *reinterpret_cast<const f32x4*>(row + 16 * j);
+            rope_rotate_cs<CH>(x1, x2, cs);
+            char* dst = kd + (krow + 32 * i) * L::kPitch;
+            store_rotated_chunks<CH>(dst + 2 * cp * CH * 2, dst + (2 * cp + 1) * CH * 2, x1, x2);
+        }
+        char* vd = vtile + buf * L::kVTile;
+#pragma unroll
+        for (int i = 0; i < kVPer; ++i) {
+            const int idx = tid + kBwdThreads * i;
+            const int r = idx / G;
+            *reinterpret_cast<u32x4*>(vd + r * L::kVPitch + (((idx % G) ^ vswz<D>(r)) * 16)) =
+                u32x4{vraw[i][0], vraw[i][1], vraw[i][2], vraw[i][3]};
+        }
+    };
+
+    const TrLane tr(lane);
+    f32x16 dqacc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int x = 0; x < 16; ++x) dqacc[db][x] = 0.f;
+    const int nt = (a.L + kBwdKN - 1) / kBwdKN;
+    load_kv(0);
+    store_kv(0);
+    __syncthreads();
+    for (int t = 0; t < nt; ++t) {
+        if (t + 1 < nt) load_kv(t + 1);
+        const char* kc = ktile + (t & 1) * L::kKTile;
+        const char* vc = vtile + (t & 1) * L::kVTile;
+        const int valid = a.L - t * kBwdKN;
+        f32x16 sacc[KB], dpacc[KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int x = 0; x < 16; ++x) {
+                sacc[kb][x] = kb * 32 + 8 * (x >> 2) + 4 * hf + (x & 3) < valid ? -lse_q : -__builtin_inff();
+                dpacc[kb][x] = 0.f;
+            }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const int r = kb * 32 + l32;
+                const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kc + r * L::kPitch + (2 * ks + hf) * 16);
+                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[ks], sacc[kb], 0, 0, 0);
+                const bf16x8 va = *reinterpret_cast<const bf16x8*>(vc + r * L::kVPitch + (((2 * ks + hf) ^ vswz<D>(r)) * 16));
+                dpacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, doreg[ks], dpacc[kb], 0, 0, 0);
+            }
+        // dZ^T = P^T * (dP^T - D), as the bf16 B operand (keys 8 g + 4 hf + jj of block kb sit
+        // in k-step 2 kb + g / 2, slot 4 (g % 2) + jj)
+        bf16x8 dzb[KK];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int x = 4 * g + jj;
+                    const float p = __builtin_amdgcn_exp2f(sacc[kb][x]);
+                    dzb[2 * kb + (g >> 1)][(g & 1) * 4 + jj] = (__bf16)(p * (dpacc[kb][x] - dq_d));
+                }
+        // dQ'^T += K^T dZ^T, K^T from transpose reads of the row-major K tile
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const char* base = kc + (16 * kk + tr.row) * L::kPitch + (4 * db + tr.gran) * 16 + tr.byte;
+                const bf16x8 ka = tr_operand(base, base + 8 * L::kPitch);
+                dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, dzb[kk], dqacc[db], 0, 0, 0);
+            }
+        if (t + 1 < nt) store_kv((t + 1) & 1);
+        wait_vm_loads();
+        __syncthreads();
+    }
+
+    // ---- epilogue: dq = c * (transposed RoPE of dQ'), to the query's token ----
+    if (!qvalid) return;
+    store_unrotated<D, E>(dqacc, a.scale, dqbuf, nq, row_bytes, pos_of(nq), tab, a.T, a.H, a.phi_mul, lane);
+}
+
+// ---------------------------------------------------------------------------------------------
+// dK and dV
+// ---------------------------------------------------------------------------------------------
+template <int D, typename E>
+__global__ void __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+attn_bwd_dkdv_kernel(AttnBwdParams a) {
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    typedef BwdLds<D> L;
+    constexpr int CH = D / 16;
+    constexpr int KS = D / 16;
+    constexpr int DB = D / 32;
+    constexpr int ES = E::kBytes;
+    constexpr int G = D / 8;                           // 16-byte granules per dO row (bf16)
+    constexpr int kOPer = kBwdQN * G / kBwdThreads;    // dO granules per thread per tile
+    char* qtile = lds;
+    char* otile = lds + 2 * L::kQTile;
+    float* ldt = reinterpret_cast<float*>(lds + L::kLdOff);   // [buf][0, 32): LSE, [buf][32, 64): D
+    char* tab = lds + L::kDkvTab;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, hf = lane >> 5;
+    const int work = xcd_remap(blockIdx.x, gridDim.x);
+    const int kt = work % a.tiles;
+    const int sc = work / a.tiles;
+    const int s = sc % a.sparse_k;
+    const int bh = sc / a.sparse_k;
+    const int head = bh % a.heads;
+    const int b = bh / a.heads;
+    const int64_t k_ = a.sparse_k;
+    const int row_bytes = a.heads * D * ES;
+    const int64_t slice = ((int64_t)b * a.N * a.heads + head) * D * ES;
+    const int slice_bytes = a.N * row_bytes - head * D * ES;
+    auto rsrc = [&](const void* base) __attribute__((always_inline)) {
+        return __builtin_amdgcn_make_buffer_rsrc((void*)(reinterpret_cast<const char*>(base) + slice), (short)0,
+                                                 slice_bytes, 0x00020000);
+    };
+    const __amdgpu_buffer_rsrc_t qbuf = rsrc(a.q), kbuf = rsrc(a.k), vbuf = rsrc(a.v), dobuf = rsrc(a.dout),
+                                 dkbuf = rsrc(a.dk), dvbuf = rsrc(a.dv);
+    const int64_t vec0 = ((int64_t)b * a.heads + head) * a.N;
+    const int HW = a.H * a.W;
+    auto pos_of = [&](int nn) __attribute__((always_inline)) {
+        Pos q;
+        q.t = nn / HW; q.h = (nn / a.W) % a.H; q.w = nn % a.W;
+        return q;
+    };
+
+    build_banked_rope_table<D>(tab, a.T, a.H, a.W, a.phi_mul);
+    const int cp = tid & 7;
+    const RopePair rp = rope_pair(cp);
+    __syncthreads();
+
+    // ---- K tile (rotated, unscaled) through LDS into B-operand registers; V of this lane's key ----
+#pragma unroll 2
+    for (int it = 0; it < kBwdRows * 8 / kBwdThreads; ++it) {
+        const int r = (tid >> 3) + it * (kBwdThreads / 8);
+        const int n = (int)scope_token(kt * kBwdRows + r, s, k_, a.mode);
+        stage_rotated_pair<D, E>(kbuf, n * row_bytes, rp, cp, tab, a.T, a.H, pos_of(n), a.phi_mul, 1.0f,
+                                 lds + r * L::kPitch);
+    }
+    __syncthreads();
+    bf16x8 kreg[KS];
+    {
+        const char* krow = lds + (wave * 32 + l32) * L::kPitch;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) kreg[ks] = *reinterpret_cast<const bf16x8*>(krow + (2 * ks + hf) * 16);
+    }
+    const int pk = kt * kBwdRows + wave * 32 + l32;
+    const int nk = (int)scope_token(pk, s, k_, a.mode);
+    bf16x8 vreg[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        float xv[8];
+        vreg[ks] = load8<E>(vbuf, nk * row_bytes + (2 * ks + hf) * 8 * ES, xv);
+    }
+    __syncthreads();   // the staging rows become query tiles
+
+    // ---- query tiles: loaded into registers one tile ahead, staged at the end of a tile ----
+    const int qrow = tid >> 3;   // Q staging task: row qrow, chunk pair cp
+    ChunkRaw<E, CH> qraw[2];
+    Pos qpos;
+    uint32_t oraw[kOPer][4];
+    float ldv = 0.f;
+    auto load_q = [&](int i) __attribute__((always_inline)) {
+        const int n = (int)scope_token(i * kBwdQN + qrow, s, k_, a.mode);
+        buffer_load_dwords(qbuf, n * row_bytes + rp.c1 * CH * ES, qraw[0].w);
+        buffer_load_dwords(qbuf, n * row_bytes + rp.c2 * CH * ES, qraw[1].w);
+        qpos = pos_of(n);
+#pragma unroll
+        for (int j = 0; j < kOPer; ++j) {
+            const int idx = tid + kBwdThreads * j;
+            const int nn = (int)scope_token(i * kBwdQN + idx / G, s, k_, a.mode);
+            buffer_load_8_as_bf16x2<E>(dobuf, nn * row_bytes + (idx % G) * 8 * ES, oraw[j]);
+        }
+        if (tid < 2 * kBwdQN) {
+            const int p = i * kBwdQN + (tid % kBwdQN);
+            const int nn = (int)scope_token(p, s, k_, a.mode);
+            ldv = tid < kBwdQN ? (p < a.L ? a.lse[vec0 + nn] : __builtin_inff())
+                               : (p < a.L ? a.delta[vec0 + nn] : 0.f);
+        }
+    };
+    auto store_q = [&](int buf) __attribute__((always_inline)) {
+        float x1[CH], x2[CH];
+        raw_to_f32(qraw[0], x1);
+        raw_to_f32(qraw[1], x2);
+        const int pos = rp.axis == 0 ? min(qpos.t, a.T - 1) : (rp.axis == 1 ? qpos.h : qpos.w);
+        const char* row = tab + rope_tab_offset<D>(a.T, a.H, rp.axis, pos, rp.jchunk * CH, rp.axis == 2 ? a.phi_mul : 0);
+        f32x4 cs[CH / 2];
+#pragma unroll
+        for (int j = 0; j < CH / 2; ++j) cs[j] = *reinterpret_cast<const f32x4*>(row + 16 * j);
+        rope_rotate_cs<CH>(x1, x2, cs);
+#pragma unroll
+        for (int e = 0; e < CH; ++e) {
+            x1[e] *= a.scale_log2;
+            x2[e] *= a.scale_log2;
+        }
+        char* dst = qtile + buf * L::kQTile + qrow * L::kPitch;
+        store_rotated_chunks<CH>(dst + 2 * cp * CH * 2, dst + (2 * cp + 1) * CH * 2, x1, x2);
+        char* od = otile + buf * L::kOTile;
+#pragma unroll
+        for (int j = 0; j < kOPer; ++j) {
+            const int idx = tid + kBwdThreads * j;
+            const int r = idx / G;
+            *reinterpret_cast<u32x4*>(od + r * L::kVPitch + (((idx % G) ^ vswz<D>(r)) * 16)) =
+                u32x4{oraw[j][0], oraw[j][1], oraw[j][2], oraw[j][3]};
+        }
+        if (tid < 2 * kBwdQN) ldt[buf * 2 * kBwdQN + tid] = ldv;
+    };
+
+    const TrLane tr(lane);
+    f32x16 dvacc[DB], dkacc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int x = 0; x < 16; ++x) {
+            dvacc[db][x] = 0.f;
+            dkacc[db][x] = 0.f;
+        }
+    const int nq = (a.L + kBwdQN - 1) / kBwdQN;
+    load_q(0);
+    store_q(0);
+    __syncthreads();
+    for (int i = 0; i < nq; ++i) {
+        if (i + 1 < nq) load_q(i + 1);
+        const char* qc = qtile + (i & 1) * L::kQTile;
+        const char* oc = otile + (i & 1) * L::kOTile;
+        const float* lc = ldt + (i & 1) * 2 * kBwdQN;
+        // start values -LSE and D of the 16 queries 8 g + 4 hf + jj this lane's accumulator rows hold
+        f32x16 sacc, dpacc;
+        float dd[16];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const f32x4 l4 = *reinterpret_cast<const f32x4*>(lc + 8 * g + 4 * hf);
+            const f32x4 d4 = *reinterpret_cast<const f32x4*>(lc + kBwdQN + 8 * g + 4 * hf);
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                sacc[4 * g + jj] = -l4[jj];
+                dd[4 * g + jj] = d4[jj];
+                dpacc[4 * g + jj] = 0.f;
+            }
+        }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qc + l32 * L::kPitch + (2 * ks + hf) * 16);
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kreg[ks], sacc, 0, 0, 0);
+            const bf16x8 oa = *reinterpret_cast<const bf16x8*>(oc + l32 * L::kVPitch + (((2 * ks + hf) ^ vswz<D>(l32)) * 16));
+            dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vreg[ks], dpacc, 0, 0, 0);
+        }
+        // P and dZ as bf16 B operands (query 8 g + 4 hf + jj in k-step g / 2, slot 4 (g % 2) + jj)
+        bf16x8 pbb[2], dzb[2];
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int x = 4 * g + jj;
+                const float p = __builtin_amdgcn_exp2f(sacc[x]);
+                pbb[g >> 1][(g & 1) * 4 + jj] = (__bf16)p;
+                dzb[g >> 1][(g & 1) * 4 + jj] = (__bf16)(p * (dpacc[x] - dd[x]));
+            }
+        // dV^T += dO^T P and dK^T += Q'^T dZ, both A operands from transpose reads
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const int r0 = 16 * kk + tr.row, r8 = r0 + 8;
+                const bf16x8 oa = tr_operand(oc + r0 * L::kVPitch + (((4 * db + tr.gran) ^ vswz<D>(r0)) * 16) + tr.byte,
+                                             oc + r8 * L::kVPitch + (((4 * db + tr.gran) ^ vswz<D>(r8)) * 16) + tr.byte);
+                dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, pbb[kk], dvacc[db], 0, 0, 0);
+                const char* qb = qc + r0 * L::kPitch + (4 * db + tr.gran) * 16 + tr.byte;
+                const bf16x8 qa = tr_operand(qb, qb + 8 * L::kPitch);
+                dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, dzb[kk], dkacc[db], 0, 0, 0);
+            }
+        if (i + 1 < nq) store_q((i + 1) & 1);
+        wait_vm_loads();
+        __syncthreads();
+    }
+
+    // ---- epilogue: dv rows, and dk = (transposed RoPE of dK') / log2(e), to the key's token ----
+    if (pk >= a.L) return;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int d0 = db * 32 + 8 * g + 4 * hf;
+            const float y0 = dvacc[db][4 * g], y1 = dvacc[db][4 * g + 1];
+            const float y2 = dvacc[db][4 * g + 2], y3 = dvacc[db][4 * g + 3];
+            if constexpr (ES == 2) {
+                const u32x2 v2 = {pack_bf16x2(y0, y1), pack_bf16x2(y2, y3)};
+                __builtin_amdgcn_raw_buffer_store_b64(v2, dvbuf, nk * row_bytes + d0 * 2, 0, 0);
+            } else {
+                const u32x4 v4 = {__float_as_uint(y0), __float_as_uint(y1), __float_as_uint(y2), __float_as_uint(y3)};
+                __builtin_amdgcn_raw_buffer_store_b128(v4, dvbuf, nk * row_bytes + d0 * 4, 0, 0);
+            }
+        }
+    store_unrotated<D, E>(dkacc, 0.69314718055994530942f, dkbuf, nk, row_bytes, pos_of(nk), tab, a.T, a.H, a.phi_mul, lane);
+}
+
+template <int D, typename E>
+static hipError_t launch_bwd_t(const AttnBwdParams& a, hipStream_t stream) {
+    typedef BwdLds<D> L;
+    const size_t table = (size_t)(a.T + a.H + a.W) * 256;
+    const size_t lds_dq = (size_t)L::kDqTab + table, lds_kv = (size_t)L::kDkvTab + table;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bwd_dq_kernel<D, E>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_dq);
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<D, E>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_kv);
+    if (e != hipSuccess) return e;
+    // dq first: it writes D, which the dk/dv kernel reads (same stream, so in order)
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<D, E>), dim3(a.num_work), dim3(kBwdThreads), lds_dq, stream, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, E>), dim3(a.num_work), dim3(kBwdThreads), lds_kv, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_attn_bwd(const AttnBwdParams& a, int head_dim, int dtype, hipStream_t stream) {
+    if (head_dim == 128) return dtype == 0 ? launch_bwd_t<128, BF16>(a, stream) : launch_bwd_t<128, FP32>(a, stream);
+    return dtype == 0 ? launch_bwd_t<64, BF16>(a, stream) : launch_bwd_t<64, FP32>(a, stream);
+}
+
+int attn_bwd_block_rows() { return kBwdRows; }
+
+}  // namespace skiparse

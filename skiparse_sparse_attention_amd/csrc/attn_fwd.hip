@@ -49,6 +49,7 @@
 //     its L2 copy of the scope's K and V.
 #include <type_traits>
 
+#include "attn_common.hpp"
 #include "skiparse_device.hpp"
 #include "skiparse_launch.hpp"
 
@@ -78,191 +79,9 @@ struct Lds {
     static constexpr int kTabRow = 256;                   // bytes per RoPE table row
 };
 
-// Q and K rows in LDS hold RoPE chunk pair cp (first-half chunk c1, partner c2) in chunk slots
-// 2 cp and 2 cp + 1, i.e. each rotate-half pair in one 32-byte span (Q and K use the same order,
-// and Q K^T contracts over head_dim in any order).  With the one-granule row pad, granule g of
-// row r falls in bank group (r + g) mod 16 (D = 128): the MFMA operand reads (one granule of 16
-// consecutive rows per 16 lanes) are conflict-free, and so are the staging writes of a 16-lane
-// group (two consecutive rows times eight pairs), whose first store covers the even slots and
-// whose second store covers the odd ones.
-
-// 3D-RoPE (cos, sin) table of the attention kernel: one 256-byte row per axis position
-// (T t rows, then H h rows, then W w rows); pair j of a row sits at byte 16*off + 8*j.
-// Each staging group of 16 lanes covers two consecutive key rows times the eight chunk
-// pairs, and in instruction i the lanes of one axis read granules off + i + m*CH/2.  The
-// offsets put t, h and the w rows of even and odd "phi" into different granule classes, so
-// those reads never share a bank whenever the two rows share their t and h positions (the
-// common case): t at 0, h at 1 (D = 128) or 4 (D = 64), w at 2 + phi or 9 + phi, where phi
-// is the parity of w div phi_div -- phi_div being the w step between consecutive rows of a
-// scope (k for Single Skip, 1 for Group Skip).  phi only moves data, never changes values.
-template <int D>
-struct RopeBank {
-    static constexpr int kOffH = D == 128 ? 1 : 4;
-    static constexpr int kOffW = D == 128 ? 2 : 9;
-    static_assert(D == 64 || D == 128, "head_dim");
-};
-
-// V rows in LDS: granule g of row r is stored at granule g ^ vswz(r).  The PV operand reads
-// (ds_read_b64_tr_b16) fetch, per 32 lanes, the same four-granule block of four consecutive
-// rows; vswz moves those rows' blocks apart (by r mod 4 at D = 128; at D = 64 the row parity
-// already separates rows r and r + 1 and vswz separates r and r + 2), so the 32 lanes hit
-// distinct banks.  Rows are written whole by 64-lane 1 KiB loads, conflict-free in any order.
-template <int D>
-__device__ __forceinline__ int vswz(int r) {
-    if constexpr (D == 128) return (r & 3) << 2;
-    else return ((r >> 1) & 1) << 2;
-}
-
-__device__ __forceinline__ int rope_phi(int w, int phi_mul) { return ((w * phi_mul) >> 16) & 1; }
-
-template <int D>
-__device__ __forceinline__ void build_banked_rope_table(char* tab, int T, int H, int W, int phi_mul) {
-    constexpr int kT = D / 8;        // pairs per t position
-    constexpr int kHW = 3 * D / 16;  // pairs per h or w position
-    const int nt = T * kT, nh = H * kHW, nw = W * kHW;
-    const int total = nt + nh + nw;
-    for (int e = threadIdx.x; e < total; e += blockDim.x) {
-        int pos, j, da, off;
-        if (e < nt) {
-            pos = e / kT; j = e - pos * kT; da = D / 4;
-            off = pos * 256;
-        } else if (e < nt + nh) {
-            const int r = e - nt; pos = r / kHW; j = r - pos * kHW; da = 3 * D / 8;
-            off = (T + pos) * 256 + RopeBank<D>::kOffH * 16;
-        } else {
-            const int r = e - nt - nh; pos = r / kHW; j = r - pos * kHW; da = 3 * D / 8;
-            off = (T + H + pos) * 256 + (RopeBank<D>::kOffW + rope_phi(pos, phi_mul)) * 16;
-        }
-        const double inv_freq = pow(10000.0, -2.0 * (double)j / (double)da);
-        const double theta = (double)pos * inv_freq;
-        double sn, cs;
-        sincos(theta, &sn, &cs);
-        *reinterpret_cast<float2*>(tab + off + 8 * j) = make_float2((float)cs, (float)sn);
-    }
-}
-
-__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
-    const int q8 = nblocks >> 3, r8 = nblocks & 7;
-    const int xcd = bid & 7, slot = bid >> 3;
-    return xcd * q8 + min(xcd, r8) + slot;
-}
-
-// Raw element storage of one RoPE chunk (CH elements of E) as dwords.
-template <typename E, int CH>
-struct ChunkRaw {
-    static constexpr int kDwords = CH * E::kBytes / 4;
-    uint32_t w[kDwords];
-};
-
-template <typename E, int CH>
-__device__ __forceinline__ void raw_to_f32(const ChunkRaw<E, CH>& r, float (&x)[CH]) {
-    if constexpr (E::kBytes == 2) {
-#pragma unroll
-        for (int i = 0; i < CH / 2; ++i) {
-            x[2 * i] = __uint_as_float(r.w[i] << 16);
-            x[2 * i + 1] = __uint_as_float(r.w[i] & 0xffff0000u);
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < CH; ++i) x[i] = __uint_as_float(r.w[i]);
-    }
-}
-
-// Rotate-half pair rotation with table entries preloaded as f32x4 = two (cos, sin) pairs.
-template <int CH>
-__device__ __forceinline__ void rope_rotate_cs(float (&x1)[CH], float (&x2)[CH], const f32x4 (&cs)[CH / 2]) {
-#pragma unroll
-    for (int e = 0; e < CH; ++e) {
-        const float c = cs[e / 2][2 * (e % 2)], sn = cs[e / 2][2 * (e % 2) + 1];
-        const float a = x1[e], b = x2[e];
-        x1[e] = a * c - b * sn;
-        x2[e] = b * c + a * sn;
-    }
-}
-
-// Buffer load of NDW dwords at a byte offset.
-template <int NDW>
-__device__ __forceinline__ void buffer_load_dwords(__amdgpu_buffer_rsrc_t r, int off, uint32_t (&w)[NDW]) {
-    if constexpr (NDW == 2) {
-        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
-        w[0] = v[0]; w[1] = v[1];
-    } else {
-        static_assert(NDW % 4 == 0, "chunk must be a multiple of 16 bytes");
-#pragma unroll
-        for (int i = 0; i < NDW / 4; ++i) {
-            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16 * i, 0, 0);
-            w[4 * i] = v[0]; w[4 * i + 1] = v[1]; w[4 * i + 2] = v[2]; w[4 * i + 3] = v[3];
-        }
-    }
-}
-
-// 8 consecutive elements of E as 4 dwords of bf16 pairs (fp32 is rounded to bf16).
-template <typename E>
-__device__ __forceinline__ void buffer_load_8_as_bf16x2(__amdgpu_buffer_rsrc_t r, int off, uint32_t (&w)[4]) {
-    if constexpr (E::kBytes == 2) {
-        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-        w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
-    } else {
-        const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-        const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 0);
-        w[0] = pack_bf16x2(__uint_as_float(a[0]), __uint_as_float(a[1]));
-        w[1] = pack_bf16x2(__uint_as_float(a[2]), __uint_as_float(a[3]));
-        w[2] = pack_bf16x2(__uint_as_float(b[0]), __uint_as_float(b[1]));
-        w[3] = pack_bf16x2(__uint_as_float(b[2]), __uint_as_float(b[3]));
-    }
-}
-
-// Round a rotated chunk pair to bf16 and write it to LDS at two byte addresses.
-template <int CH>
-__device__ __forceinline__ void store_rotated_chunks(char* a1, char* a2, const float (&x1)[CH], const float (&x2)[CH]) {
-    uint32_t w1[CH / 2], w2[CH / 2];
-#pragma unroll
-    for (int i = 0; i < CH / 2; ++i) {
-        w1[i] = pack_bf16x2(x1[2 * i], x1[2 * i + 1]);
-        w2[i] = pack_bf16x2(x2[2 * i], x2[2 * i + 1]);
-    }
-    if constexpr (CH == 8) {
-        *reinterpret_cast<u32x4*>(a1) = u32x4{w1[0], w1[1], w1[2], w1[3]};
-        *reinterpret_cast<u32x4*>(a2) = u32x4{w2[0], w2[1], w2[2], w2[3]};
-    } else {
-        *reinterpret_cast<u32x2*>(a1) = u32x2{w1[0], w1[1]};
-        *reinterpret_cast<u32x2*>(a2) = u32x2{w2[0], w2[1]};
-    }
-}
-
-// 16 bytes per lane from a buffer straight into LDS: lane l's bytes land at dst + 16 l (dst
-// must be wave-uniform; out-of-range offsets write zeros).  Issued as inline assembly so the
-// compiler does not treat every later LDS read as a possible reader of this write and wait for
-// all outstanding loads before it; the caller instead waits for the load counter (vmcnt) before
-// the barrier after which the data is read.  The s_nop covers the M0-write hazard.
-__device__ __forceinline__ void buffer_load_to_lds16(__amdgpu_buffer_rsrc_t r, char* dst, int off) {
-    const unsigned lds_addr = (unsigned)(size_t)((__attribute__((address_space(3))) char*)dst);
-    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off), "s"(r), "{m0}"(lds_addr) : "memory");
-}
-
-// Wait until every vector memory load of this wave has completed (including loads into LDS).
-__device__ __forceinline__ void wait_vm_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-// Wait until at most N vector memory instructions of this wave are outstanding: every load
-// issued before the N most recent ones has completed (loads complete in issue order).
-template <int N>
-__device__ __forceinline__ void wait_vm_loads_but() { asm volatile("s_waitcnt vmcnt(%0)" ::"i"(N) : "memory"); }
-
-// LDS transpose read of 4 bf16 (ds_read_b64_tr_b16): within each group of 16 lanes,
-// lane j receives element j % 4 of the 4-element runs addressed by lanes 4t + j / 4,
-// t = 0..3.
-__device__ __forceinline__ i16x4 ds_read_tr16(const char* p) {
-    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
-}
-
-// Grid position of a token, tracked across tiles by adding a fixed token delta
-// decomposed as (dt, dh, dw) with carries.
-struct Pos {
-    int t, h, w;
-};
-
 }  // namespace
+
+using namespace attn;
 
 // KDIV: sparse_k divides kBN, so row p + kBN of a scope is token n(p) + kBN*k in both modes
 // and the load cursors advance by a constant.
@@ -712,9 +531,14 @@ attn_fwd_kernel(AttnParams a) {
     // ---- epilogue: normalise and scatter rows back to their tokens ----
     {
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_part), __float_as_uint(l_part), false, false);
-        const float inv = 1.0f / (__uint_as_float(sw[0]) + __uint_as_float(sw[1]));
+        const float l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+        const float inv = 1.0f / l_tot;
         const int p = qt * kBM + wave * 32 + l32;
-        const int off = (int)scope_token(p, s, k_, a.mode) * row_bytes;   // past the slice when p >= L
+        const int n_tok = (int)scope_token(p, s, k_, a.mode);
+        const int off = n_tok * row_bytes;   // past the slice when p >= L
+        // log2-sum-exp of the row's scaled scores, for the backward pass
+        if (a.lse != nullptr && hf == 0 && p < a.L)
+            a.lse[((int64_t)b * a.heads + head) * a.N + n_tok] = m_ref + log2f(l_tot);
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll

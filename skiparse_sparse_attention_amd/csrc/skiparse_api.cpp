@@ -56,6 +56,12 @@ bool overlaps(const void* a, const void* b, int64_t bytes) {
     return x < y + (uintptr_t)bytes && y < x + (uintptr_t)bytes;
 }
 
+// [a, a + a_bytes) and [b, b + b_bytes) share a byte
+bool ranges_overlap(const void* a, int64_t a_bytes, const void* b, int64_t b_bytes) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + (uintptr_t)b_bytes && y < x + (uintptr_t)a_bytes;
+}
+
 int to_status(hipError_t e) { return e == hipSuccess ? SKIPARSE_OK : SKIPARSE_E_DEVICE; }
 
 int remap_grid(int64_t rows) {
@@ -87,11 +93,11 @@ int skiparse_validate(const void* q, const void* k, const void* v, int B, int T,
     return SKIPARSE_OK;
 }
 
-int skiparse_attn(const void* q, const void* k, const void* v, int B, int T, int H, int W,
-                  int heads, int head_dim, int sparse_k, int mode, int dtype, void* out,
-                  void* stream) {
-    const int st = skiparse_validate(q, k, v, B, T, H, W, heads, head_dim, sparse_k, mode, dtype, out);
-    if (st != SKIPARSE_OK) return st;
+namespace {
+
+// The forward launch shared by skiparse_attn and skiparse_attn_lse (lse may be NULL).
+int attn_forward(const void* q, const void* k, const void* v, int B, int T, int H, int W, int heads,
+                 int head_dim, int sparse_k, int mode, int dtype, void* out, float* lse, void* stream) {
     Dims d;
     check_dims(B, T, H, W, heads, head_dim, sparse_k, mode, dtype, &d);
     skiparse::AttnParams a;
@@ -106,10 +112,87 @@ int skiparse_attn(const void* q, const void* k, const void* v, int B, int T, int
     a.num_work = (int)work;
     a.k_divides_bn = (bn % sparse_k) == 0;
     a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)head_dim));
+    a.lse = lse;
     // consecutive rows of a scope step w by k (Single Skip) or by 1 (Group Skip)
     const int phi_div = mode == SKIPARSE_SINGLE ? sparse_k : 1;
     a.phi_mul = phi_div > 65536 ? 0 : (65536 + phi_div - 1) / phi_div;
     return to_status(skiparse::launch_attn(a, head_dim, dtype, static_cast<hipStream_t>(stream)));
+}
+
+int phi_mul_of(int mode, int sparse_k) {
+    const int phi_div = mode == SKIPARSE_SINGLE ? sparse_k : 1;
+    return phi_div > 65536 ? 0 : (65536 + phi_div - 1) / phi_div;
+}
+
+}  // namespace
+
+int skiparse_attn(const void* q, const void* k, const void* v, int B, int T, int H, int W,
+                  int heads, int head_dim, int sparse_k, int mode, int dtype, void* out,
+                  void* stream) {
+    const int st = skiparse_validate(q, k, v, B, T, H, W, heads, head_dim, sparse_k, mode, dtype, out);
+    if (st != SKIPARSE_OK) return st;
+    return attn_forward(q, k, v, B, T, H, W, heads, head_dim, sparse_k, mode, dtype, out, nullptr, stream);
+}
+
+int skiparse_attn_lse(const void* q, const void* k, const void* v, int B, int T, int H, int W,
+                      int heads, int head_dim, int sparse_k, int mode, int dtype, void* out,
+                      float* lse, void* stream) {
+    if (!lse) return SKIPARSE_E_NULL;
+    const int st = skiparse_validate(q, k, v, B, T, H, W, heads, head_dim, sparse_k, mode, dtype, out);
+    if (st != SKIPARSE_OK) return st;
+    Dims d;
+    check_dims(B, T, H, W, heads, head_dim, sparse_k, mode, dtype, &d);
+    const int64_t lse_bytes = (int64_t)B * heads * d.N * 4;
+    if (ranges_overlap(lse, lse_bytes, q, d.bytes) || ranges_overlap(lse, lse_bytes, k, d.bytes) ||
+        ranges_overlap(lse, lse_bytes, v, d.bytes) || ranges_overlap(lse, lse_bytes, out, d.bytes))
+        return SKIPARSE_E_ALIAS;
+    return attn_forward(q, k, v, B, T, H, W, heads, head_dim, sparse_k, mode, dtype, out, lse, stream);
+}
+
+int skiparse_attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                      const float* lse, int B, int T, int H, int W, int heads, int head_dim,
+                      int sparse_k, int mode, int dtype, void* dq, void* dk, void* dv, float* delta,
+                      void* stream) {
+    if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv || !delta) return SKIPARSE_E_NULL;
+    const int st = skiparse_validate(q, k, v, B, T, H, W, heads, head_dim, sparse_k, mode, dtype, out);
+    if (st != SKIPARSE_OK) return st;
+    Dims d;
+    check_dims(B, T, H, W, heads, head_dim, sparse_k, mode, dtype, &d);
+    const int64_t vec_bytes = (int64_t)B * heads * d.N * 4;
+    // outputs: dq, dk, dv (tensor-sized) and delta (vector-sized) must not overlap any input or
+    // each other
+    const void* ins[5] = {q, k, v, out, dout};
+    void* outs[3] = {dq, dk, dv};
+    for (int i = 0; i < 3; ++i) {
+        for (int j = 0; j < 5; ++j)
+            if (overlaps(outs[i], ins[j], d.bytes)) return SKIPARSE_E_ALIAS;
+        for (int j = i + 1; j < 3; ++j)
+            if (overlaps(outs[i], outs[j], d.bytes)) return SKIPARSE_E_ALIAS;
+        if (ranges_overlap(outs[i], d.bytes, lse, vec_bytes) || ranges_overlap(outs[i], d.bytes, delta, vec_bytes))
+            return SKIPARSE_E_ALIAS;
+    }
+    for (int j = 0; j < 5; ++j)
+        if (ranges_overlap(delta, vec_bytes, ins[j], d.bytes)) return SKIPARSE_E_ALIAS;
+    if (overlaps(delta, lse, vec_bytes)) return SKIPARSE_E_ALIAS;
+    skiparse::AttnBwdParams a;
+    a.q = q; a.k = k; a.v = v; a.o = out; a.dout = dout; a.lse = lse; a.delta = delta;
+    a.dq = dq; a.dk = dk; a.dv = dv;
+    a.B = B; a.T = T; a.H = H; a.W = W; a.heads = heads; a.sparse_k = sparse_k; a.mode = mode;
+    a.N = (int)d.N; a.L = (int)d.L;
+    const int rows = skiparse::attn_bwd_block_rows();
+    a.tiles = (int)((d.L + rows - 1) / rows);
+    const int64_t work = (int64_t)B * heads * sparse_k * a.tiles;
+    if (work > kI32Max) return SKIPARSE_E_SHAPE;
+    a.num_work = (int)work;
+    a.scale = (float)(1.0 / std::sqrt((double)head_dim));
+    a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)head_dim));
+    a.phi_mul = phi_mul_of(mode, sparse_k);
+    return to_status(skiparse::launch_attn_bwd(a, head_dim, dtype, static_cast<hipStream_t>(stream)));
+}
+
+double skiparse_attn_bwd_flops(int B, int T, int H, int W, int heads, int head_dim, int sparse_k) {
+    const double f = skiparse_attn_flops(B, T, H, W, heads, head_dim, sparse_k);
+    return f < 0 ? f : 2.0 * f;
 }
 
 int skiparse_rope_remap(const void* q, const void* k, const void* v, int B, int T, int H, int W,

@@ -34,13 +34,36 @@ struct AttnParams {
     int num_work;    // B*heads*sparse_k*q_tiles workgroups
     int k_divides_bn;  // sparse_k divides the key-tile height
     float scale_log2;  // log2(e) / sqrt(head_dim)
+    float* lse;        // optional (B, heads, N) fp32: log2 of each row's softmax denominator,
+                       // in the units of the scores scaled by scale_log2
     int phi_mul;       // ceil(2^16 / phi_div), phi_div = w step between consecutive scope rows
+};
+
+struct AttnBwdParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* o;       // forward output
+    const void* dout;    // gradient of the loss with respect to the output
+    const float* lse;    // (B, heads, N): the forward's log2-sum-exp of each row
+    float* delta;        // (B, heads, N) workspace: rowsum(dout * o), written by the dq kernel
+    void* dq;
+    void* dk;
+    void* dv;
+    int B, T, H, W, heads, sparse_k, mode, N, L;
+    int tiles;           // ceil(L / 128): query tiles of the dq kernel, key tiles of the dk/dv kernel
+    int num_work;        // B*heads*sparse_k*tiles workgroups per kernel
+    float scale_log2;    // log2(e) / sqrt(head_dim)
+    float scale;         // 1 / sqrt(head_dim)
+    int phi_mul;
 };
 
 hipError_t launch_rope_remap(const RemapParams& a, int head_dim, int dtype, hipStream_t stream, int grid);
 hipError_t launch_reverse(const ReverseParams& a, hipStream_t stream, int grid);
 hipError_t launch_attn(const AttnParams& a, int head_dim, int dtype, hipStream_t stream);
+hipError_t launch_attn_bwd(const AttnBwdParams& a, int head_dim, int dtype, hipStream_t stream);
 int attn_block_rows();  // query rows per attention workgroup
+int attn_bwd_block_rows();  // queries / keys per backward workgroup
 int attn_tile_keys();   // keys per attention K/V tile
 
 }  // namespace skiparse

@@ -86,3 +86,15 @@ def make_inputs(w: Workload, seed: int = 0, device="cpu"):
             x = x.to(torch.bfloat16)
         out.append(x.to(device))
     return tuple(out)
+
+
+def make_output_grad(w: Workload, seed: int = 1, device="cpu"):
+    """A synthetic gradient of the loss with respect to the attention output, shape
+    (B, N, heads, head_dim): torch CPU generator seeded with ``seed``, randn in float32,
+    cast like the inputs (bfloat16 unless the workload is fp32), moved to ``device``."""
+    import torch
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    x = torch.randn((w.B, w.N, w.heads, w.head_dim), generator=g, dtype=torch.float32)
+    if w.dtype == "bf16":
+        x = x.to(torch.bfloat16)
+    return x.to(device)

@@ -29,7 +29,8 @@ def test_header_declares_the_boundary():
     names = _declared_functions()
     for want in ("skiparse_attn", "skiparse_rope_remap", "skiparse_rearrange", "skiparse_reverse",
                  "skiparse_validate", "skiparse_scope_table", "skiparse_attn_flops",
-                 "skiparse_status_string", "skiparse_version"):
+                 "skiparse_status_string", "skiparse_version", "skiparse_attn_lse",
+                 "skiparse_attn_bwd", "skiparse_attn_bwd_flops"):
         assert want in names
 
 
@@ -118,3 +119,37 @@ def test_attn_flops_matches_definition():
     assert sk.attn_flops(1, (24, 22, 40), 24, 128, 4) == oracle.skiparse_flops(1, 21120, 24, 128, 4)
     assert sk.attn_flops(2, (20, 48, 48), 24, 128, 8) == oracle.skiparse_flops(2, 46080, 24, 128, 8)
     assert sk.attn_flops(0, (1, 1, 1), 1, 64, 1) < 0
+
+
+def test_attn_flops_backward_is_twice_the_forward():
+    assert sk.attn_bwd_flops(1, (24, 22, 40), 24, 128, 4) == oracle.skiparse_backward_flops(1, 21120, 24, 128, 4)
+    assert sk.attn_bwd_flops(2, (20, 48, 48), 24, 128, 8) == oracle.skiparse_backward_flops(2, 46080, 24, 128, 8)
+    assert sk.attn_bwd_flops(1, (0, 1, 1), 1, 64, 1) < 0
+
+
+LSE, DO, DQ, DK, DV, DELTA = 5 << 40, 6 << 40, 7 << 40, 8 << 40, 9 << 40, 10 << 40
+
+
+def _bwd(**kw):
+    a = dict(q=Q, k=K, v=V, out=OUT, dout=DO, lse=LSE, dq=DQ, dk=DK, dv=DV, delta=DELTA)
+    a.update({x: kw.pop(x) for x in list(kw) if x in a})
+    g = dict(GOOD)
+    g.update(kw)
+    return sk.lib().skiparse_attn_bwd(a["q"], a["k"], a["v"], a["out"], a["dout"], a["lse"], g["B"], g["T"],
+                                      g["H"], g["W"], g["heads"], g["head_dim"], g["sparse_k"], g["mode"],
+                                      g["dtype"], a["dq"], a["dk"], a["dv"], a["delta"], None)
+
+
+def test_backward_and_lse_reject_before_any_device_call():
+    L = sk.lib()
+    assert L.skiparse_attn_lse(Q, K, V, 1, 4, 8, 8, 2, 64, 2, 0, 1, OUT, None, None) == sk.E_NULL
+    assert L.skiparse_attn_lse(Q, K, V, 1, 4, 8, 8, 2, 64, 2, 0, 1, OUT, Q, None) == sk.E_ALIAS
+    assert L.skiparse_attn_lse(Q, K, V, 1, 4, 8, 8, 2, 64, 3, 0, 1, OUT, LSE, None) == sk.E_DIVISIBILITY
+    assert _bwd(delta=None) == sk.E_NULL
+    assert _bwd(lse=None) == sk.E_NULL
+    assert _bwd(dq=K) == sk.E_ALIAS            # a gradient over an input
+    assert _bwd(dv=DK) == sk.E_ALIAS           # two gradients in one buffer
+    assert _bwd(delta=DO) == sk.E_ALIAS        # the workspace over an input
+    assert _bwd(delta=LSE) == sk.E_ALIAS       # the workspace over the log2-sum-exp
+    assert _bwd(sparse_k=3) == sk.E_DIVISIBILITY
+    assert _bwd(head_dim=96) == sk.E_UNSUPPORTED
