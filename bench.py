@@ -27,7 +27,8 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_osp_24x22x40_traffic.md")
-ATTN_SOURCE = os.path.join(ROOT, "skiparse_sparse_attention_amd", "csrc", "attn_fwd.hip")
+ATTN_SOURCES = [os.path.join(ROOT, "skiparse_sparse_attention_amd", "csrc", f)
+                for f in ("attn_fwd.hip", "attn_common.hpp")]
 
 
 def parse_args():
@@ -40,14 +41,19 @@ def parse_args():
     ap.add_argument("--no-remap", action="store_true", help="skip the standalone RoPE+remap pass")
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the per-workload attention timings (other grids, k in {1,2,4,8})")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass timing")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (counter calibration)")
     return ap.parse_args()
 
 
 def source_digest():
-    with open(ATTN_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Digest of the forward attention kernel's sources (the traffic figures go stale with it)."""
+    h = hashlib.sha256()
+    for path in ATTN_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(per_launch_flops):
@@ -135,6 +141,40 @@ def sweep(sk, wl, stream, reps=3):
         del out
     cache.clear()
     return res
+
+
+def backward(sk, wl, q, k, v, stream, reps=10):
+    """skiparse_attn_bwd (dq kernel, then dk/dv kernel) on the 24x22x40 workload, both modes:
+    median of `reps` calls after warm-up, HIP events on the launch stream.  FLOPs counted as
+    twice the forward's (the backward price of Wan 2.1 report section 4.3.1)."""
+    import torch
+    res = {}
+    ws = wl.OSP_SINGLE
+    do = wl.make_output_grad(ws, seed=1, device="cuda")
+    grads = tuple(torch.empty_like(q) for _ in range(3))
+    for w in (wl.OSP_SINGLE, wl.OSP_GROUP):
+        out, lse = sk.attn_lse(q, k, v, w.grid, w.sparse_k, w.mode, stream=stream)
+        delta = torch.empty_like(lse)
+        def call():
+            sk.attn_bwd(q, k, v, out, do, lse, w.grid, w.sparse_k, w.mode, grads=grads, delta=delta, stream=stream)
+        for _ in range(3):
+            call()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev[0].record(stream)
+        for i in range(reps):
+            call()
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        ms = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(reps))[reps // 2]
+        flops = sk.attn_bwd_flops(w.B, w.grid, w.heads, w.head_dim, w.sparse_k)
+        tf = flops / (ms * 1e-3) / 1e12
+        res["single" if w.mode == 0 else "group"] = {"ms": round(ms, 4), "tflops": round(tf, 1)}
+    avg_ms = 0.5 * (res["single"]["ms"] + res["group"]["ms"])
+    tf = sk.attn_bwd_flops(ws.B, ws.grid, ws.heads, ws.head_dim, ws.sparse_k) / (avg_ms * 1e-3) / 1e12
+    return {"kernels": "attn_bwd_dq_kernel<128, bf16> + attn_bwd_dkdv_kernel<128, bf16>",
+            "bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tf / PEAK_BF16_TFLOPS, 4), "flop_per_call": sk.attn_bwd_flops(ws.B, ws.grid, ws.heads, ws.head_dim, ws.sparse_k),
+            "per_mode": res}
 
 
 def main():
@@ -272,6 +312,9 @@ def main():
             "device_copy_same_bytes_gbs": round(copy_gbs, 1),
         }
         del rq, rk, rv
+
+    if not args.no_backward:
+        result["backward"] = backward(sk, wl, qg, kg, vg, stream)
 
     if not args.no_sweep:
         result["sweep"] = sweep(sk, wl, stream)

@@ -84,8 +84,9 @@ struct Lds {
 using namespace attn;
 
 // KDIV: sparse_k divides kBN, so row p + kBN of a scope is token n(p) + kBN*k in both modes
-// and the load cursors advance by a constant.
-template <int D, typename E, bool KDIV>
+// and the load cursors advance by a constant.  LSE: also write each row's log2-sum-exp (a
+// separate instantiation, so the plain forward carries none of its code).
+template <int D, typename E, bool KDIV, bool LSE>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kThreads / 256, kThreads / 256)))
 attn_fwd_kernel(AttnParams a) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
@@ -537,7 +538,7 @@ attn_fwd_kernel(AttnParams a) {
         const int n_tok = (int)scope_token(p, s, k_, a.mode);
         const int off = n_tok * row_bytes;   // past the slice when p >= L
         // log2-sum-exp of the row's scaled scores, for the backward pass
-        if (a.lse != nullptr && hf == 0 && p < a.L)
+        if (LSE && hf == 0 && p < a.L)
             a.lse[((int64_t)b * a.heads + head) * a.N + n_tok] = m_ref + log2f(l_tot);
 #pragma unroll
         for (int db = 0; db < DB; ++db)
@@ -557,20 +558,25 @@ attn_fwd_kernel(AttnParams a) {
     }
 }
 
-template <int D, typename E, bool KDIV>
+template <int D, typename E, bool KDIV, bool LSE>
 static hipError_t launch_attn_k(const AttnParams& a, hipStream_t stream) {
     typedef Lds<D> L;
     const size_t lds = (size_t)L::kTabOff + (size_t)(a.T + a.H + a.W) * L::kTabRow;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_kernel<D, E, KDIV>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_kernel<D, E, KDIV, LSE>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((attn_fwd_kernel<D, E, KDIV>), dim3(a.num_work), dim3(kThreads), lds, stream, a);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, E, KDIV, LSE>), dim3(a.num_work), dim3(kThreads), lds, stream, a);
     return hipGetLastError();
+}
+
+template <int D, typename E, bool LSE>
+static hipError_t launch_attn_l(const AttnParams& a, hipStream_t stream) {
+    return a.k_divides_bn ? launch_attn_k<D, E, true, LSE>(a, stream) : launch_attn_k<D, E, false, LSE>(a, stream);
 }
 
 template <int D, typename E>
 static hipError_t launch_attn_t(const AttnParams& a, hipStream_t stream) {
-    return a.k_divides_bn ? launch_attn_k<D, E, true>(a, stream) : launch_attn_k<D, E, false>(a, stream);
+    return a.lse != nullptr ? launch_attn_l<D, E, true>(a, stream) : launch_attn_l<D, E, false>(a, stream);
 }
 
 hipError_t launch_attn(const AttnParams& a, int head_dim, int dtype, hipStream_t stream) {

@@ -34,9 +34,9 @@ struct AttnParams {
     int num_work;    // B*heads*sparse_k*q_tiles workgroups
     int k_divides_bn;  // sparse_k divides the key-tile height
     float scale_log2;  // log2(e) / sqrt(head_dim)
+    int phi_mul;       // ceil(2^16 / phi_div), phi_div = w step between consecutive scope rows
     float* lse;        // optional (B, heads, N) fp32: log2 of each row's softmax denominator,
                        // in the units of the scores scaled by scale_log2
-    int phi_mul;       // ceil(2^16 / phi_div), phi_div = w step between consecutive scope rows
 };
 
 struct AttnBwdParams {
