@@ -5,6 +5,7 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 the oracle imports nothing from the product package.
 """
 
+from . import skiparse_oracle8  # noqa: F401  (8-bit Skiparse attention)
 from .skiparse_oracle import (  # noqa: F401
     GROUP,
     ROPE_BASE,
