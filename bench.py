@@ -26,6 +26,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PEAK_8BIT_TOPS = 5000.0     # MI355X dense int8 (TOP/s) and fp8 (TFLOP/s) MFMA
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_osp_24x22x40_traffic.md")
 ATTN_SOURCES = [os.path.join(ROOT, "skiparse_sparse_attention_amd", "csrc", f)
                 for f in ("attn_fwd.hip", "attn_common.hpp")]
@@ -42,6 +43,7 @@ def parse_args():
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the per-workload attention timings (other grids, k in {1,2,4,8})")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass timing")
+    ap.add_argument("--no-8bit", action="store_true", help="skip the 8-bit attention timing")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -175,6 +177,48 @@ def backward(sk, wl, q, k, v, stream, reps=10):
             "bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(tf / PEAK_BF16_TFLOPS, 4), "flop_per_call": sk.attn_bwd_flops(ws.B, ws.grid, ws.heads, ws.head_dim, ws.sparse_k),
             "per_mode": res}
+
+
+def eight_bit(sk, wl, q, k, v, stream, reps=20):
+    """8-bit Skiparse attention on the 24x22x40 workload, both modes: skiparse_quant8 (three
+    launches, HBM-bound) and skiparse_attn8 (one launch), each the median of `reps` calls
+    timed with HIP events on the launch stream.  FLOPs as for the bf16 kernel; the peak is
+    the int8 / fp8 one (the QK products are int8, the PV products fp8)."""
+    import torch
+    res = {}
+    ws = wl.OSP_SINGLE
+    flops = sk.attn_flops(ws.B, ws.grid, ws.heads, ws.head_dim, ws.sparse_k)
+
+    def timed(fn):
+        for _ in range(5):
+            fn()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev[0].record(stream)
+        for i in range(reps):
+            fn()
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        return sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(reps))[reps // 2]
+
+    nbytes_el = q.numel()                       # elements of one tensor
+    for w in (wl.OSP_SINGLE, wl.OSP_GROUP):
+        qz = sk.quant8(q, k, v, w.grid, w.sparse_k, w.mode, stream=stream)
+        out = torch.empty_like(q)
+        q_ms = timed(lambda: sk.quant8(q, k, v, w.grid, w.sparse_k, w.mode, outs=qz, stream=stream))
+        a_ms = timed(lambda: sk.attn8(qz, w.grid, w.sparse_k, w.mode, out=out, stream=stream))
+        # quant8 algorithmic bytes: the statistics pass reads k and v; the quantisation pass
+        # reads q, k, v and writes the int8 / E4M3 codes and q_amax
+        vt_bytes = qz["vt8"].numel()
+        qbytes = 2 * 2 * nbytes_el + 3 * 2 * nbytes_el + 2 * nbytes_el + vt_bytes + qz["q_amax"].numel() * 4
+        res["single" if w.mode == 0 else "group"] = {
+            "attn8_ms": round(a_ms, 4), "attn8_tflops": round(flops / (a_ms * 1e-3) / 1e12, 1),
+            "quant8_ms": round(q_ms, 4), "quant8_gbs": round(qbytes / (q_ms * 1e-3) / 1e9, 1),
+            "both_tflops": round(flops / ((a_ms + q_ms) * 1e-3) / 1e12, 1)}
+    a_ms = 0.5 * (res["single"]["attn8_ms"] + res["group"]["attn8_ms"])
+    tf = flops / (a_ms * 1e-3) / 1e12
+    return {"kernel": "attn8_fwd_kernel (int8 QK, E4M3 PV)", "bound": "mfma", "achieved": round(tf, 1),
+            "peak": PEAK_8BIT_TOPS, "unit": "TFLOP/s", "frac": round(tf / PEAK_8BIT_TOPS, 4),
+            "flop_per_call": flops, "per_mode": res}
 
 
 def main():
@@ -315,6 +359,9 @@ def main():
 
     if not args.no_backward:
         result["backward"] = backward(sk, wl, qg, kg, vg, stream)
+
+    if not args.no_8bit:
+        result["attn8"] = eight_bit(sk, wl, qg, kg, vg, stream)
 
     if not args.no_sweep:
         result["sweep"] = sweep(sk, wl, stream)

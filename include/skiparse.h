@@ -150,6 +150,66 @@ double skiparse_attn_bwd_flops(int B, int T, int H, int W, int heads, int head_d
                                int sparse_k);
 
 /*
+ * 8-bit Skiparse attention (Wan 2.1 report, section 4.4.3 "Quantization",
+ * paragraph "8-Bit FlashAttention": Int8 operands for S = Q K^T, FP8 (E4M3)
+ * operands for O = P V, float32 accumulation across key blocks).  Two calls:
+ * skiparse_quant8 turns bf16/fp32 q, k, v into the 8-bit operands, and
+ * skiparse_attn8 runs the attention on them.  head_dim 128 only; sparse_k must
+ * divide 64; B*heads at most 65535 (SKIPARSE_E_UNSUPPORTED otherwise).
+ *
+ * Operand layouts (all device memory, caller-owned, N = T*H*W, L = N/sparse_k,
+ * Lp = skiparse_q8_scope_pitch(T, H, W, sparse_k) = L rounded up to 64):
+ *   q8, k8 : int8 (B, N, heads, 128), original token order, codes of q' and k'
+ *            (q, k after the same 3D RoPE as skiparse_attn, in float32);
+ *   q_amax : float32 (B, N, heads), max |q'| over each head row;
+ *   k_amax : float32 (B, heads), max |k'| over every token and channel;
+ *   vt8    : uint8 E4M3 codes (B, heads, sparse_k, 128, Lp): entry
+ *            [b, head, s, c, p] encodes v[b, n(s, p), head, c] * (448 / v_amax),
+ *            n(s, p) the token at position p of scope s; positions p >= L hold 0;
+ *   v_amax : float32 (B, heads, 128), max |v| over the tokens of each channel.
+ * Codes: round-half-even(x * (127 / amax)) for int8, E4M3 round-to-nearest-even
+ * for V; the reciprocal and the product are float32 operations rounded once
+ * each, and a zero amax gives zero codes.
+ */
+
+/*
+ * skiparse_q8_scope_pitch -- Lp, the channel-row pitch (in keys) of vt8: L
+ * rounded up to a multiple of 64.  Host only; negative status for invalid
+ * sizes.
+ */
+int skiparse_q8_scope_pitch(int T, int H, int W, int sparse_k);
+
+/*
+ * skiparse_quant8 -- the 8-bit operands of q, k, v (layouts above).
+ * q, k, v : (B, N, heads, head_dim) in `dtype` (SKIPARSE_BF16 or SKIPARSE_FP32).
+ * Outputs q8, q_amax, k8, k_amax, vt8, v_amax must not overlap any input or
+ * each other.  Three kernel launches on `stream`: a fill of k_amax and v_amax
+ * with zeros, a pass folding |k'| and |v| maxima into them with atomic maxima,
+ * and the quantisation pass.  Returns SKIPARSE_OK or an error code.
+ */
+int skiparse_quant8(const void* q, const void* k, const void* v,
+                    int B, int T, int H, int W, int heads, int head_dim,
+                    int sparse_k, int mode, int dtype,
+                    void* q8, float* q_amax, void* k8, float* k_amax,
+                    void* vt8, float* v_amax, void* stream);
+
+/*
+ * skiparse_attn8 -- 8-bit Skiparse attention of skiparse_quant8's operands.
+ * For query token i of scope s and the scope's keys j:
+ *   z_ij = (q8_i . k8_j) * (q_amax_i/127) * (k_amax/127) * log2(e) / sqrt(128)
+ *   M_i  = ceil(max_j z_ij),  P_ij = 2^(z_ij - M_i + 8)
+ *   out_i = (sum_j E4M3(P_ij) * V~_j) * (v_amax / 448) / sum_j P_ij
+ * (V~ the decoded vt8 codes), written to token i's row of out.
+ * out : (B, N, heads, 128) in `out_dtype` (SKIPARSE_BF16 or SKIPARSE_FP32),
+ *       must not overlap any operand.  One kernel launch.  Same size limits as
+ *       skiparse_attn.  Returns SKIPARSE_OK or an error code.
+ */
+int skiparse_attn8(const void* q8, const float* q_amax, const void* k8,
+                   const float* k_amax, const void* vt8, const float* v_amax,
+                   int B, int T, int H, int W, int heads, int head_dim,
+                   int sparse_k, int mode, int out_dtype, void* out, void* stream);
+
+/*
  * skiparse_rope_remap -- the materialised RoPE + rearrange of q, k and v in
  * one pass (the page's add_rope + *_skip_rearrange calls, before attention).
  *

@@ -22,11 +22,14 @@ from ._lib import (  # noqa: F401
     SINGLE,
     SkiparseError,
     attn,
+    attn8,
     attn_bwd,
     attn_bwd_flops,
     attn_flops,
     attn_lse,
     lib,
+    q8_scope_pitch,
+    quant8,
     rearrange,
     reverse,
     rope_remap,

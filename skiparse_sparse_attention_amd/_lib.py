@@ -68,6 +68,12 @@ def lib():
         L.skiparse_attn_bwd.restype = i
         L.skiparse_attn_bwd_flops.argtypes = [i] * 7
         L.skiparse_attn_bwd_flops.restype = ctypes.c_double
+        L.skiparse_q8_scope_pitch.argtypes = [i] * 4
+        L.skiparse_q8_scope_pitch.restype = i
+        L.skiparse_quant8.argtypes = [vp, vp, vp] + dims + [i, i, i] + [vp] * 7
+        L.skiparse_quant8.restype = i
+        L.skiparse_attn8.argtypes = [vp] * 6 + dims + [i, i, i, vp, vp]
+        L.skiparse_attn8.restype = i
         L.skiparse_status_string.argtypes = [i]
         L.skiparse_status_string.restype = ctypes.c_char_p
         L.skiparse_version.argtypes = []
@@ -177,6 +183,59 @@ def attn_bwd(q, k, v, out, dout, lse, grid, sparse_k, mode, grads=None, delta=No
 def attn_bwd_flops(B, grid, heads, head_dim, sparse_k):
     T, H, W = (int(g) for g in grid)
     return float(lib().skiparse_attn_bwd_flops(int(B), T, H, W, int(heads), int(head_dim), int(sparse_k)))
+
+
+Q8_KEYS = ("q8", "q_amax", "k8", "k_amax", "vt8", "v_amax")
+
+
+def q8_scope_pitch(grid, sparse_k):
+    """Lp: the channel-row pitch (keys) of vt8, L rounded up to a multiple of 64."""
+    T, H, W = (int(g) for g in grid)
+    lp = lib().skiparse_q8_scope_pitch(T, H, W, int(sparse_k))
+    if lp < 0:
+        raise SkiparseError(-lp, "skiparse_q8_scope_pitch")
+    return lp
+
+
+def quant8(q, k, v, grid, sparse_k, mode, outs=None, stream=None):
+    """8-bit operands of q, k, v for :func:`attn8`: a dict with q8 (int8), q_amax, k8 (int8),
+    k_amax, vt8 (uint8 E4M3 codes) and v_amax (float32), in the layouts of include/skiparse.h."""
+    import torch
+    B, T, H, W, heads, d = _dims(q, grid)
+    for t in (k, v):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
+            raise ValueError("q, k, v must share shape, dtype and be contiguous")
+    N = T * H * W
+    if outs is None:
+        lp = q8_scope_pitch(grid, sparse_k)
+        dev = q.device
+        outs = {"q8": torch.empty((B, N, heads, d), dtype=torch.int8, device=dev),
+                "q_amax": torch.empty((B, N, heads), dtype=torch.float32, device=dev),
+                "k8": torch.empty((B, N, heads, d), dtype=torch.int8, device=dev),
+                "k_amax": torch.empty((B, heads), dtype=torch.float32, device=dev),
+                "vt8": torch.empty((B, heads, int(sparse_k), d, lp), dtype=torch.uint8, device=dev),
+                "v_amax": torch.empty((B, heads, d), dtype=torch.float32, device=dev)}
+    _check(lib().skiparse_quant8(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, T, H, W, heads, d,
+                                 int(sparse_k), int(mode), _dtype_code(q),
+                                 *(outs[key].data_ptr() for key in Q8_KEYS), _stream_ptr(stream)),
+           "skiparse_quant8")
+    return outs
+
+
+def attn8(qz, grid, sparse_k, mode, out_dtype=None, out=None, stream=None):
+    """8-bit Skiparse attention of :func:`quant8`'s operands -> (B, N, heads, d) bf16 (or fp32)."""
+    import torch
+    q8 = qz["q8"]
+    B, T, H, W, heads, d = _dims(q8, grid)
+    for key in Q8_KEYS:
+        if not qz[key].is_contiguous():
+            raise ValueError(f"{key} must be contiguous")
+    if out is None:
+        out = torch.empty(q8.shape, dtype=out_dtype or torch.bfloat16, device=q8.device)
+    _check(lib().skiparse_attn8(*(qz[key].data_ptr() for key in Q8_KEYS), B, T, H, W, heads, d,
+                                int(sparse_k), int(mode), _dtype_code(out), out.data_ptr(),
+                                _stream_ptr(stream)), "skiparse_attn8")
+    return out
 
 
 def rope_remap(q, k, v, grid, sparse_k, mode, outs=None, stream=None):

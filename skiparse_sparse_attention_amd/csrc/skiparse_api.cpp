@@ -195,6 +195,86 @@ double skiparse_attn_bwd_flops(int B, int T, int H, int W, int heads, int head_d
     return f < 0 ? f : 2.0 * f;
 }
 
+int skiparse_q8_scope_pitch(int T, int H, int W, int sparse_k) {
+    if (T < 1 || H < 1 || W < 1 || sparse_k < 1) return -SKIPARSE_E_SHAPE;
+    const int64_t N = (int64_t)T * H * W;
+    if (N > kI32Max || N % sparse_k) return -SKIPARSE_E_DIVISIBILITY;
+    return skiparse::q8_scope_pitch((int)(N / sparse_k));
+}
+
+namespace {
+
+// Checks shared by the 8-bit calls: the attention's size limits, head_dim 128, sparse_k | 64.
+int check_q8(int B, int T, int H, int W, int heads, int head_dim, int sparse_k, int mode, int dtype,
+             Dims* d, int64_t* lp) {
+    const int st = check_dims(B, T, H, W, heads, head_dim, sparse_k, mode, dtype, d);
+    if (st != SKIPARSE_OK) return st;
+    if (head_dim != 128 || 64 % sparse_k != 0) return SKIPARSE_E_UNSUPPORTED;
+    if ((int64_t)B * heads > 65535) return SKIPARSE_E_UNSUPPORTED;   // grid y of the statistics pass
+    const int64_t row_bytes = (int64_t)heads * head_dim * d->esize;
+    if ((d->N + 256 * (int64_t)sparse_k + (int64_t)sparse_k * sparse_k) * row_bytes + 4096 > kI32Max)
+        return SKIPARSE_E_UNSUPPORTED;
+    *lp = skiparse::q8_scope_pitch((int)d->L);
+    if ((int64_t)head_dim * *lp > kI32Max) return SKIPARSE_E_UNSUPPORTED;
+    return SKIPARSE_OK;
+}
+
+}  // namespace
+
+int skiparse_quant8(const void* q, const void* k, const void* v, int B, int T, int H, int W, int heads,
+                    int head_dim, int sparse_k, int mode, int dtype, void* q8, float* q_amax, void* k8,
+                    float* k_amax, void* vt8, float* v_amax, void* stream) {
+    if (!q || !k || !v || !q8 || !q_amax || !k8 || !k_amax || !vt8 || !v_amax) return SKIPARSE_E_NULL;
+    Dims d;
+    int64_t lp = 0;
+    const int st = check_q8(B, T, H, W, heads, head_dim, sparse_k, mode, dtype, &d, &lp);
+    if (st != SKIPARSE_OK) return st;
+    const int64_t codes = (int64_t)B * d.N * heads * head_dim;
+    const int64_t sizes[6] = {codes, (int64_t)B * d.N * heads * 4, codes, (int64_t)B * heads * 4,
+                              (int64_t)B * heads * sparse_k * head_dim * lp, (int64_t)B * heads * head_dim * 4};
+    const void* outs[6] = {q8, q_amax, k8, k_amax, vt8, v_amax};
+    const void* ins[3] = {q, k, v};
+    for (int i = 0; i < 6; ++i) {
+        for (int j = 0; j < 3; ++j)
+            if (ranges_overlap(outs[i], sizes[i], ins[j], d.bytes)) return SKIPARSE_E_ALIAS;
+        for (int j = i + 1; j < 6; ++j)
+            if (ranges_overlap(outs[i], sizes[i], outs[j], sizes[j])) return SKIPARSE_E_ALIAS;
+    }
+    skiparse::Q8Params a;
+    a.q = q; a.k = k; a.v = v; a.q8 = q8; a.k8 = k8; a.vt8 = vt8;
+    a.q_amax = q_amax; a.k_amax = k_amax; a.v_amax = v_amax;
+    a.B = B; a.T = T; a.H = H; a.W = W; a.heads = heads; a.sparse_k = sparse_k; a.mode = mode;
+    a.N = (int)d.N; a.Lp = (int)lp;
+    return to_status(skiparse::launch_quant8(a, head_dim, dtype, static_cast<hipStream_t>(stream)));
+}
+
+int skiparse_attn8(const void* q8, const float* q_amax, const void* k8, const float* k_amax, const void* vt8,
+                   const float* v_amax, int B, int T, int H, int W, int heads, int head_dim, int sparse_k,
+                   int mode, int out_dtype, void* out, void* stream) {
+    if (!q8 || !q_amax || !k8 || !k_amax || !vt8 || !v_amax || !out) return SKIPARSE_E_NULL;
+    Dims d;
+    int64_t lp = 0;
+    const int st = check_q8(B, T, H, W, heads, head_dim, sparse_k, mode, out_dtype, &d, &lp);
+    if (st != SKIPARSE_OK) return st;
+    const int64_t codes = (int64_t)B * d.N * heads * head_dim;
+    const int64_t sizes[6] = {codes, (int64_t)B * d.N * heads * 4, codes, (int64_t)B * heads * 4,
+                              (int64_t)B * heads * sparse_k * head_dim * lp, (int64_t)B * heads * head_dim * 4};
+    const void* ins[6] = {q8, q_amax, k8, k_amax, vt8, v_amax};
+    for (int j = 0; j < 6; ++j)
+        if (ranges_overlap(out, d.bytes, ins[j], sizes[j])) return SKIPARSE_E_ALIAS;
+    skiparse::Attn8Params a;
+    a.q8 = q8; a.k8 = k8; a.vt8 = vt8; a.q_amax = q_amax; a.k_amax = k_amax; a.v_amax = v_amax; a.out = out;
+    a.B = B; a.T = T; a.H = H; a.W = W; a.heads = heads; a.sparse_k = sparse_k; a.mode = mode;
+    a.N = (int)d.N; a.L = (int)d.L; a.Lp = (int)lp;
+    const int rows = skiparse::attn8_block_rows();
+    a.q_tiles = (int)((d.L + rows - 1) / rows);
+    const int64_t work = (int64_t)B * heads * sparse_k * a.q_tiles;
+    if (work > kI32Max) return SKIPARSE_E_SHAPE;
+    a.num_work = (int)work;
+    a.out_bytes = d.esize;
+    return to_status(skiparse::launch_attn8(a, static_cast<hipStream_t>(stream)));
+}
+
 int skiparse_rope_remap(const void* q, const void* k, const void* v, int B, int T, int H, int W,
                         int heads, int head_dim, int sparse_k, int mode, int dtype, void* rq,
                         void* rk, void* rv, void* stream) {

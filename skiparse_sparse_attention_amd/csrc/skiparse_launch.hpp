@@ -58,6 +58,36 @@ struct AttnBwdParams {
     int phi_mul;
 };
 
+// 8-bit operands (quant8.hip): q8, k8 int8 (B, N, heads, d); vt8 E4M3 (B, heads, k, d, Lp)
+struct Q8Params {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* q8;
+    void* k8;
+    void* vt8;
+    float* q_amax;       // (B, N, heads)
+    float* k_amax;       // (B, heads)
+    float* v_amax;       // (B, heads, d)
+    int B, T, H, W, heads, sparse_k, mode, N;
+    int Lp;              // L rounded up to a multiple of 64: the channel-row pitch of vt8
+};
+
+// 8-bit attention (attn8_fwd.hip), operands from quant8.hip
+struct Attn8Params {
+    const void* q8;
+    const void* k8;
+    const void* vt8;
+    const float* q_amax;
+    const float* k_amax;
+    const float* v_amax;
+    void* out;
+    int B, T, H, W, heads, sparse_k, mode, N, L, Lp;
+    int q_tiles;         // ceil(L / 256)
+    int num_work;        // B*heads*sparse_k*q_tiles workgroups
+    int out_bytes;       // 2 (bf16) or 4 (fp32)
+};
+
 hipError_t launch_rope_remap(const RemapParams& a, int head_dim, int dtype, hipStream_t stream, int grid);
 hipError_t launch_reverse(const ReverseParams& a, hipStream_t stream, int grid);
 hipError_t launch_attn(const AttnParams& a, int head_dim, int dtype, hipStream_t stream);
@@ -65,5 +95,9 @@ hipError_t launch_attn_bwd(const AttnBwdParams& a, int head_dim, int dtype, hipS
 int attn_block_rows();  // query rows per attention workgroup
 int attn_bwd_block_rows();  // queries / keys per backward workgroup
 int attn_tile_keys();   // keys per attention K/V tile
+hipError_t launch_quant8(const Q8Params& a, int head_dim, int dtype, hipStream_t stream);
+hipError_t launch_attn8(const Attn8Params& a, hipStream_t stream);
+int q8_scope_pitch(int L);  // Lp of the vt8 layout
+int attn8_block_rows();     // query rows per 8-bit attention workgroup
 
 }  // namespace skiparse

@@ -30,7 +30,8 @@ def test_header_declares_the_boundary():
     for want in ("skiparse_attn", "skiparse_rope_remap", "skiparse_rearrange", "skiparse_reverse",
                  "skiparse_validate", "skiparse_scope_table", "skiparse_attn_flops",
                  "skiparse_status_string", "skiparse_version", "skiparse_attn_lse",
-                 "skiparse_attn_bwd", "skiparse_attn_bwd_flops"):
+                 "skiparse_attn_bwd", "skiparse_attn_bwd_flops", "skiparse_quant8", "skiparse_attn8",
+                 "skiparse_q8_scope_pitch"):
         assert want in names
 
 
@@ -153,3 +154,45 @@ def test_backward_and_lse_reject_before_any_device_call():
     assert _bwd(delta=LSE) == sk.E_ALIAS       # the workspace over the log2-sum-exp
     assert _bwd(sparse_k=3) == sk.E_DIVISIBILITY
     assert _bwd(head_dim=96) == sk.E_UNSUPPORTED
+
+
+def test_q8_scope_pitch():
+    L = sk.lib()
+    assert L.skiparse_q8_scope_pitch(24, 22, 40, 4) == 5312       # L = 5280 rounded up to 64
+    assert L.skiparse_q8_scope_pitch(4, 8, 16, 4) == 128           # L = 128 already a multiple
+    assert L.skiparse_q8_scope_pitch(1, 1, 3, 1) == 64
+    assert L.skiparse_q8_scope_pitch(2, 2, 5, 3) < 0               # N not divisible by k
+
+
+def _q8(**kw):
+    a = dict(q=Q, k=K, v=V, q8=DQ, qa=DK, k8=DV, ka=DELTA, vt8=DO, va=LSE)
+    a.update({x: kw.pop(x) for x in list(kw) if x in a})
+    g = dict(B=1, T=4, H=8, W=16, heads=2, head_dim=128, sparse_k=4, mode=0, dtype=0)
+    g.update(kw)
+    return sk.lib().skiparse_quant8(a["q"], a["k"], a["v"], g["B"], g["T"], g["H"], g["W"], g["heads"],
+                                    g["head_dim"], g["sparse_k"], g["mode"], g["dtype"], a["q8"], a["qa"],
+                                    a["k8"], a["ka"], a["vt8"], a["va"], None)
+
+
+def _a8(**kw):
+    a = dict(q8=DQ, qa=DK, k8=DV, ka=DELTA, vt8=DO, va=LSE, out=OUT)
+    a.update({x: kw.pop(x) for x in list(kw) if x in a})
+    g = dict(B=1, T=4, H=8, W=16, heads=2, head_dim=128, sparse_k=4, mode=0, dtype=0)
+    g.update(kw)
+    return sk.lib().skiparse_attn8(a["q8"], a["qa"], a["k8"], a["ka"], a["vt8"], a["va"], g["B"], g["T"],
+                                   g["H"], g["W"], g["heads"], g["head_dim"], g["sparse_k"], g["mode"],
+                                   g["dtype"], a["out"], None)
+
+
+def test_8bit_calls_reject_before_any_device_call():
+    assert _q8(vt8=None) == sk.E_NULL
+    assert _q8(head_dim=64) == sk.E_UNSUPPORTED       # the 8-bit path is head_dim 128 only
+    assert _q8(T=3, H=8, W=8, sparse_k=3) == sk.E_UNSUPPORTED     # 3 does not divide 64
+    assert _q8(sparse_k=3) == sk.E_DIVISIBILITY
+    assert _q8(q8=Q) == sk.E_ALIAS                     # an output over an input
+    assert _q8(ka=DELTA, va=DELTA) == sk.E_ALIAS       # two outputs in one buffer
+    assert _q8(B=3000, heads=30) == sk.E_UNSUPPORTED   # B*heads beyond the statistics grid
+    assert _a8(out=None) == sk.E_NULL
+    assert _a8(head_dim=64) == sk.E_UNSUPPORTED
+    assert _a8(out=DV) == sk.E_ALIAS                   # the output over an operand
+    assert _a8(dtype=2) == sk.E_UNSUPPORTED
