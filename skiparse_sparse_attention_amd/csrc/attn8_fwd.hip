@@ -29,6 +29,8 @@
 //     scales), and the A operand, V^T, is read from the transposed vt8 tile as 32 consecutive
 //     keys of one channel per lane, two 16-byte LDS reads;
 //   * both tiles are XOR-swizzled per row so every LDS operand read is bank-conflict-free.
+#include <type_traits>
+
 #include "attn_common.hpp"
 #include "skiparse_device.hpp"
 #include "skiparse_launch.hpp"
@@ -177,11 +179,13 @@ attn8_fwd_kernel(Attn8Params a) {
         __builtin_amdgcn_s_setprio(0);
     };
 
-    auto softmax = [&](int j) __attribute__((always_inline)) {
-        const bool ragged = j == nt - 1 && (a.L % kBN8) != 0;
+    // `masked`: the last tile of the scope, whose keys past the end of the scope are excluded
+    // from the maximum and weighted 0.  Only the peeled last iteration of each schedule loop
+    // instantiates it, so the loop body carries none of the masking.
+    auto softmax = [&](int j, auto masked) __attribute__((always_inline)) {
+        constexpr bool ragged = decltype(masked)::value;
         const int valid = a.L - j * kBN8;
-        // keys past the end of the scope: excluded from the maximum (and weighted 0 below)
-        if (ragged) {
+        if constexpr (ragged) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -217,7 +221,8 @@ attn8_fwd_kernel(Attn8Params a) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     float t = __builtin_fmaf((float)sacc[kb][4 * g + r], cq, bias);
-                    if (ragged && 32 * hf + 16 * kb + 4 * g + r >= valid) t = -__builtin_inff();
+                    if constexpr (ragged)
+                        if (32 * hf + 16 * kb + 4 * g + r >= valid) t = -__builtin_inff();
                     p[r] = __builtin_amdgcn_exp2f(t);
                     lsum[r & 1] += p[r];
                 }
@@ -261,29 +266,45 @@ attn8_fwd_kernel(Attn8Params a) {
         if (m >= 1) pv(opaque((m - 1) % 3));
         if (m < nt) qk(opaque(m % 3));
     };
-    auto valu_block = [&](int m, int sm) __attribute__((always_inline)) {
+    auto valu_block = [&](int m, int sm, auto masked) __attribute__((always_inline)) {
         int issued = 0;
         if (m + 1 < nt) { load_v(opaque((m + 1) % 3)); ++issued; }
         if (m + 2 < nt) { load_k(opaque((m + 2) % 3)); ++issued; }
-        if (sm >= 0 && sm < nt) softmax(sm);
+        if (sm >= 0 && sm < nt) softmax(sm, masked);
         if (issued == 2) wait_vm_loads_but<2>();
         else if (issued == 1) wait_vm_loads_but<1>();
         else wait_vm_loads();
     };
+    // softmax(nt - 1), the only one that may need masking, runs in group 0's VALU block
+    // m = nt - 1 and in group 1's VALU block m = nt: those iterations are peeled
+    const std::false_type plain;
+    const std::true_type last;
     if (grp == 0) {
-        for (int m = 0; m <= nt; ++m) {
+        for (int m = 0; m < nt - 1; ++m) {
             mfma_block(m);
             __syncthreads();
-            valu_block(m, m);
+            valu_block(m, m, plain);
             __syncthreads();
         }
+        mfma_block(nt - 1);
+        __syncthreads();
+        valu_block(nt - 1, nt - 1, last);
+        __syncthreads();
+        mfma_block(nt);
+        __syncthreads();
+        valu_block(nt, nt, plain);   // no loads and no softmax left: the final wait only
+        __syncthreads();
     } else {
-        for (int m = 0; m <= nt; ++m) {
-            valu_block(m, m - 1);
+        for (int m = 0; m < nt; ++m) {
+            valu_block(m, m - 1, plain);
             __syncthreads();
             mfma_block(m);
             __syncthreads();
         }
+        valu_block(nt, nt - 1, last);
+        __syncthreads();
+        mfma_block(nt);
+        __syncthreads();
     }
 
     // ---- epilogue: O / l * v_amax / 448, scattered back to the query's token row ----
