@@ -33,62 +33,69 @@ using namespace attn;
 
 namespace {
 
+constexpr int kD = 128;                // head_dim of the 8-bit path
+constexpr int kCH = kD / 16;           // elements per RoPE chunk (rope_pair's chunk layout)
 constexpr int kQ8Threads = 256;        // 4 wavefronts
 constexpr int kQ8Tile = 64;            // scope positions per quantisation task
 constexpr int kStatTokens = 512;       // tokens per statistics workgroup
 constexpr int kQ8MaxGrid = 1024;       // quantisation workgroups (each builds the table once)
+constexpr int kVtPitch = kQ8Tile + 16; // bytes per transposed LDS row of the V codes
 
-// Pair i of a head row (i < D/2): the RoPE axis, its frequency index j and the offsets of the
-// two rotate-half elements (axis chunks t, h, w of D/4, 3D/8, 3D/8 elements).
-template <int D>
-struct PairSlot {
-    int axis, j, e1, e2;
-    __device__ __forceinline__ explicit PairSlot(int i) {
-        constexpr int ht = D / 8, hh = 3 * D / 16;
-        if (i < ht) {
-            axis = 0; j = i; e1 = i; e2 = i + ht;
-        } else if (i < ht + hh) {
-            axis = 1; j = i - ht; e1 = D / 4 + j; e2 = e1 + hh;
-        } else {
-            axis = 2; j = i - ht - hh; e1 = 5 * D / 8 + j; e2 = e1 + hh;
-        }
-    }
-};
+typedef float f32x8 __attribute__((ext_vector_type(8)));
 
 // x1' = x1 c - x2 s, x2' = x2 c + x1 s with every product and sum rounded to float32
-__device__ __forceinline__ void rotate_rn(float x1, float x2, float2 cs, float& y1, float& y2) {
+__device__ __forceinline__ void rotate_rn(float x1, float x2, float c, float s, float& y1, float& y2) {
 #pragma clang fp contract(off)
-    y1 = x1 * cs.x - x2 * cs.y;
-    y2 = x2 * cs.x + x1 * cs.y;
+    y1 = x1 * c - x2 * s;
+    y2 = x2 * c + x1 * s;
 }
 
-template <typename E>
-__device__ __forceinline__ float load_elem(__amdgpu_buffer_rsrc_t r, int off) {
-    if constexpr (E::kBytes == 2)
-        return __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0) << 16);
-    else
-        return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
-}
-
-// int8 code of x * r (r = 127 / amax), both float32 operations rounded to nearest even
-__device__ __forceinline__ int int8_code(float x, float r) {
+// int8 code of x * r (r = 127 / amax), the product rounded to float32, then to nearest even
+__device__ __forceinline__ uint32_t int8_code(float x, float r) {
 #pragma clang fp contract(off)
     const float y = __builtin_rintf(x * r);
-    return (int)fminf(fmaxf(y, -127.f), 127.f);
+    return (uint32_t)(int)fminf(fmaxf(y, -127.f), 127.f) & 0xffu;
 }
 
-__device__ __forceinline__ float wave_max(float x) {
+// kCH elements of E at byte offset `off` as floats (16-byte loads)
+template <typename E>
+__device__ __forceinline__ void load_chunk(__amdgpu_buffer_rsrc_t r, int off, float (&x)[kCH]) {
+    ChunkRaw<E, kCH> raw;
+    buffer_load_dwords(r, off, raw.w);
+    raw_to_f32(raw, x);
+}
+
+// The rotated chunk pair cp of the head row at `off` (token n at grid position q): x1 gets
+// chunk rp.c1, x2 its rotate-half partner rp.c2, both turned by RoPE at q.
+template <typename E>
+__device__ __forceinline__ void rotated_pair(__amdgpu_buffer_rsrc_t r, int off, const RopePair& rp, const char* tab,
+                                             int T, int H, const Pos& q, float (&x1)[kCH], float (&x2)[kCH]) {
+    load_chunk<E>(r, off + rp.c1 * kCH * E::kBytes, x1);
+    load_chunk<E>(r, off + rp.c2 * kCH * E::kBytes, x2);
+    const int pos = rp.axis == 0 ? q.t : (rp.axis == 1 ? q.h : q.w);
+    const float* cs = reinterpret_cast<const float*>(tab + rope_tab_offset<kD>(T, H, rp.axis, pos, rp.jchunk * kCH, 0));
+    float c[2 * kCH];
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m));
-    return x;
+    for (int i = 0; i < kCH / 2; ++i) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(cs + 4 * i);
+        c[4 * i] = v[0]; c[4 * i + 1] = v[1]; c[4 * i + 2] = v[2]; c[4 * i + 3] = v[3];
+    }
+#pragma unroll
+    for (int e = 0; e < kCH; ++e) rotate_rn(x1[e], x2[e], c[2 * e], c[2 * e + 1], x1[e], x2[e]);
 }
 
-// Grid position of token n and the table offset of pair `ps` at it.
-template <int D>
-__device__ __forceinline__ const float2* pair_cs(const char* tab, const Q8Params& a, const PairSlot<D>& ps, int n) {
-    const int HW = a.H * a.W;
-    const int pos = ps.axis == 0 ? n / HW : (ps.axis == 1 ? (n / a.W) % a.H : n % a.W);
-    return reinterpret_cast<const float2*>(tab + rope_tab_offset<D>(a.T, a.H, ps.axis, pos, ps.j, 0));
+__device__ __forceinline__ Pos grid_pos(int n, int H, int W) {
+    Pos q;
+    q.t = n / (H * W); q.h = (n / W) % H; q.w = n % W;
+    return q;
+}
+
+// kCH int8 codes packed little-endian into two dwords
+__device__ __forceinline__ u32x2 pack_codes(const float (&x)[kCH], float r) {
+    u32x2 w = {0u, 0u};
+#pragma unroll
+    for (int e = 0; e < kCH; ++e) w[e / 4] |= int8_code(x[e], r) << (8 * (e % 4));
+    return w;
 }
 
 __global__ void __launch_bounds__(kQ8Threads) q8_fill_kernel(float* k_amax, float* v_amax, int nk, int nv) {
@@ -98,173 +105,189 @@ __global__ void __launch_bounds__(kQ8Threads) q8_fill_kernel(float* k_amax, floa
     }
 }
 
-// Statistics: workgroup (token chunk, batch * heads + head).  Lane l of a row group handles
-// RoPE pair l of k and channels 2l, 2l + 1 of v; a wavefront covers 128 / D token rows per
-// step.
-template <int D, typename E>
+// Statistics: workgroup (token chunk, batch * heads + head).  k: 8 lanes per token row, one
+// RoPE chunk pair each; v: 16 lanes per token row, one 8-channel chunk each.  Partial maxima
+// meet in LDS, then one atomic maximum per channel (and one for k) per workgroup.
+template <typename E>
 __global__ void __launch_bounds__(kQ8Threads) q8_stats_kernel(Q8Params a) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
-    constexpr int LPR = D / 2;              // lanes per token row
-    constexpr int RPW = 64 / LPR;           // token rows per wavefront step
     constexpr int ES = E::kBytes;
     char* tab = lds;
-    float* red = reinterpret_cast<float*>(lds + (a.T + a.H + a.W) * 256);   // [4 waves][RPW][D + 1]
+    float* red = reinterpret_cast<float*>(lds + (a.T + a.H + a.W) * 256);   // [kQ8Threads / 16][kD], then k
     const int bh = blockIdx.y, b = bh / a.heads, head = bh % a.heads;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int sub = lane / LPR, li = lane % LPR;
-    const int row_bytes = a.heads * D * ES;
-    const int64_t slice = ((int64_t)b * a.N * a.heads + head) * D * ES;
-    const int slice_bytes = a.N * row_bytes - head * D * ES;
+    const int tid = threadIdx.x;
+    const int row_bytes = a.heads * kD * ES;
+    const int64_t slice = ((int64_t)b * a.N * a.heads + head) * kD * ES;
+    const int slice_bytes = a.N * row_bytes - head * kD * ES;
     const __amdgpu_buffer_rsrc_t kbuf = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(reinterpret_cast<const char*>(a.k) + slice), (short)0, slice_bytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t vbuf = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(reinterpret_cast<const char*>(a.v) + slice), (short)0, slice_bytes, 0x00020000);
-    build_banked_rope_table<D>(tab, a.T, a.H, a.W, 0);
+    build_banked_rope_table<kD>(tab, a.T, a.H, a.W, 0);
     __syncthreads();
-    const PairSlot<D> ps(li);
-    float km = 0.f, vm0 = 0.f, vm1 = 0.f;
     const int n0 = blockIdx.x * kStatTokens;
     const int n1 = min(n0 + kStatTokens, a.N);
-    for (int n = n0 + wave * RPW + sub; n < n1; n += 4 * RPW) {
-        const int off = n * row_bytes;
-        float y1, y2;
-        rotate_rn(load_elem<E>(kbuf, off + ps.e1 * ES), load_elem<E>(kbuf, off + ps.e2 * ES),
-                  *pair_cs<D>(tab, a, ps, n), y1, y2);
-        km = fmaxf(km, fmaxf(fabsf(y1), fabsf(y2)));
-        vm0 = fmaxf(vm0, fabsf(load_elem<E>(vbuf, off + 2 * li * ES)));
-        vm1 = fmaxf(vm1, fabsf(load_elem<E>(vbuf, off + (2 * li + 1) * ES)));
+    // k: row tid / 8 of each 32-row step, chunk pair tid % 8
+    const RopePair rp = rope_pair(tid & 7);
+    float km = 0.f;
+    for (int n = n0 + (tid >> 3); n < n1; n += kQ8Threads / 8) {
+        float x1[kCH], x2[kCH];
+        rotated_pair<E>(kbuf, n * row_bytes, rp, tab, a.T, a.H, grid_pos(n, a.H, a.W), x1, x2);
+#pragma unroll
+        for (int e = 0; e < kCH; ++e) km = fmaxf(km, fmaxf(fabsf(x1[e]), fabsf(x2[e])));
     }
-    km = wave_max(km);
-    float* wr = red + (wave * RPW + sub) * (D + 1);
-    wr[2 * li] = vm0;
-    wr[2 * li + 1] = vm1;
-    if (lane == 0) wr[D] = km;
+    // v: row tid / 16 of each 16-row step, channels 8 (tid % 16) + [0, 8)
+    const int vc = tid & 15;
+    float vm[kCH];
+#pragma unroll
+    for (int e = 0; e < kCH; ++e) vm[e] = 0.f;
+    for (int n = n0 + (tid >> 4); n < n1; n += kQ8Threads / 16) {
+        float x[kCH];
+        load_chunk<E>(vbuf, n * row_bytes + vc * kCH * ES, x);
+#pragma unroll
+        for (int e = 0; e < kCH; ++e) vm[e] = fmaxf(vm[e], fabsf(x[e]));
+    }
+    float* wr = red + (tid >> 4) * kD + vc * kCH;
+#pragma unroll
+    for (int e = 0; e < kCH; ++e) wr[e] = vm[e];
+    float* kred = red + (kQ8Threads / 16) * kD;
+    {
+        float m = km;
+#pragma unroll
+        for (int x = 32; x >= 1; x >>= 1) m = fmaxf(m, __shfl_xor(m, x));
+        if ((tid & 63) == 0) kred[tid >> 6] = m;
+    }
     __syncthreads();
-    for (int c = tid; c <= D; c += kQ8Threads) {
+    if (tid < kD) {
         float m = 0.f;
-        for (int r = 0; r < 4 * RPW; ++r) m = fmaxf(m, red[r * (D + 1) + c]);
-        unsigned* dst = c < D ? reinterpret_cast<unsigned*>(a.v_amax) + (int64_t)bh * D + c
-                              : reinterpret_cast<unsigned*>(a.k_amax) + bh;
-        atomicMax(dst, __float_as_uint(m));
+        for (int r = 0; r < kQ8Threads / 16; ++r) m = fmaxf(m, red[r * kD + tid]);
+        atomicMax(reinterpret_cast<unsigned*>(a.v_amax) + (int64_t)bh * kD + tid, __float_as_uint(m));
+    } else if (tid == kD) {
+        float m = 0.f;
+        for (int r = 0; r < kQ8Threads / 64; ++r) m = fmaxf(m, kred[r]);
+        atomicMax(reinterpret_cast<unsigned*>(a.k_amax) + bh, __float_as_uint(m));
     }
 }
 
-// Quantisation: task (batch, head, scope, tile of 64 scope positions).  Each wavefront takes
-// 16 positions: q and k rows by RoPE pair per lane (codes stored straight to their original
-// token rows), v by channel pair per lane into a transposed LDS tile, which the workgroup
-// then writes as 64-byte rows of vt8.
-template <int D, typename E>
+// Quantisation: task (batch, head, scope, tile of 64 scope positions).  q and k: 8 lanes per
+// row, one RoPE chunk pair each (the q row's amax across the 8 lanes), codes stored as two
+// 8-byte pieces straight to the token's row; v: 16 lanes per row, 8 channels each, codes
+// transposed through LDS and written as 64-byte rows of vt8.
+template <typename E>
 __global__ void __launch_bounds__(kQ8Threads) q8_quant_kernel(Q8Params a) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
-    constexpr int LPR = D / 2;
-    constexpr int RPW = 64 / LPR;
     constexpr int ES = E::kBytes;
-    constexpr int kVtPitch = kQ8Tile + 4;                       // bytes per transposed LDS row
     char* tab = lds;
     unsigned char* vt = reinterpret_cast<unsigned char*>(lds + (a.T + a.H + a.W) * 256);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int sub = lane / LPR, li = lane % LPR;
-    const int row_bytes = a.heads * D * ES;
-    const int row8 = a.heads * D;                               // bytes per token of q8 / k8
+    const int tid = threadIdx.x;
+    const int row_bytes = a.heads * kD * ES;
+    const int row8 = a.heads * kD;                              // bytes per token of q8 / k8
     const int L = a.N / a.sparse_k;
     const int tiles = a.Lp / kQ8Tile;
     const int tasks = a.B * a.heads * a.sparse_k * tiles;
-    build_banked_rope_table<D>(tab, a.T, a.H, a.W, 0);
+    build_banked_rope_table<kD>(tab, a.T, a.H, a.W, 0);
     __syncthreads();
-    const PairSlot<D> ps(li);
+    const int cp = tid & 7;
+    const RopePair rp = rope_pair(cp);
+    const int vc = tid & 15;
     for (int task = blockIdx.x; task < tasks; task += gridDim.x) {
         const int pt = task % tiles;
         const int s = (task / tiles) % a.sparse_k;
         const int bh = task / (tiles * a.sparse_k);
         const int b = bh / a.heads, head = bh % a.heads;
-        const int64_t slice = ((int64_t)b * a.N * a.heads + head) * D * ES;
-        const int slice_bytes = a.N * row_bytes - head * D * ES;
+        const int64_t slice = ((int64_t)b * a.N * a.heads + head) * kD * ES;
+        const int slice_bytes = a.N * row_bytes - head * kD * ES;
         const __amdgpu_buffer_rsrc_t qbuf = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(reinterpret_cast<const char*>(a.q) + slice), (short)0, slice_bytes, 0x00020000);
         const __amdgpu_buffer_rsrc_t kbuf = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(reinterpret_cast<const char*>(a.k) + slice), (short)0, slice_bytes, 0x00020000);
         const __amdgpu_buffer_rsrc_t vbuf = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(reinterpret_cast<const char*>(a.v) + slice), (short)0, slice_bytes, 0x00020000);
-        const int64_t slice8 = ((int64_t)b * a.N * a.heads + head) * D;
-        const int slice8_bytes = a.N * row8 - head * D;
+        const int64_t slice8 = ((int64_t)b * a.N * a.heads + head) * kD;
+        const int slice8_bytes = a.N * row8 - head * kD;
         const __amdgpu_buffer_rsrc_t q8buf = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(reinterpret_cast<char*>(a.q8) + slice8), (short)0, slice8_bytes, 0x00020000);
         const __amdgpu_buffer_rsrc_t k8buf = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(reinterpret_cast<char*>(a.k8) + slice8), (short)0, slice8_bytes, 0x00020000);
         const float k_amax = a.k_amax[bh];
         const float k_r = k_amax > 0.f ? __fdiv_rn(127.f, k_amax) : 0.f;
-        const float* va = a.v_amax + (int64_t)bh * D;
-        const float vam0 = va[2 * li], vam1 = va[2 * li + 1];
-        const float v_r0 = vam0 > 0.f ? __fdiv_rn(448.f, vam0) : 0.f;
-        const float v_r1 = vam1 > 0.f ? __fdiv_rn(448.f, vam1) : 0.f;
-        for (int rr = wave * RPW + sub; rr < kQ8Tile; rr += 4 * RPW) {
+        // q and k rows: rows tid / 8 + 32 i of the tile
+        for (int rr = tid >> 3; rr < kQ8Tile; rr += kQ8Threads / 8) {
             const int p = pt * kQ8Tile + rr;
-            const int n = p < L ? (int)scope_token(p, s, a.sparse_k, a.mode) : a.N;   // a.N: reads 0
-            const int off = n * row_bytes;
-            const float2 cs = n < a.N ? *pair_cs<D>(tab, a, ps, n) : make_float2(1.f, 0.f);
-            // q: per-row amax across the LPR lanes of the row
-            float q1, q2;
-            rotate_rn(load_elem<E>(qbuf, off + ps.e1 * ES), load_elem<E>(qbuf, off + ps.e2 * ES), cs, q1, q2);
-            float qm = fmaxf(fabsf(q1), fabsf(q2));
+            if (p >= L) break;                                   // uniform per group of 8 lanes
+            const int n = (int)scope_token(p, s, a.sparse_k, a.mode);
+            const Pos q = grid_pos(n, a.H, a.W);
+            float x1[kCH], x2[kCH];
+            rotated_pair<E>(qbuf, n * row_bytes, rp, tab, a.T, a.H, q, x1, x2);
+            float qm = 0.f;
 #pragma unroll
-            for (int m = LPR / 2; m >= 1; m >>= 1) qm = fmaxf(qm, __shfl_xor(qm, m));
+            for (int e = 0; e < kCH; ++e) qm = fmaxf(qm, fmaxf(fabsf(x1[e]), fabsf(x2[e])));
+            qm = fmaxf(qm, __shfl_xor(qm, 1));
+            qm = fmaxf(qm, __shfl_xor(qm, 2));
+            qm = fmaxf(qm, __shfl_xor(qm, 4));
             const float q_r = qm > 0.f ? __fdiv_rn(127.f, qm) : 0.f;
-            float k1, k2;
-            rotate_rn(load_elem<E>(kbuf, off + ps.e1 * ES), load_elem<E>(kbuf, off + ps.e2 * ES), cs, k1, k2);
-            if (n < a.N) {
-                const int o8 = n * row8;
-                __builtin_amdgcn_raw_buffer_store_b8((unsigned char)int8_code(q1, q_r), q8buf, o8 + ps.e1, 0, 0);
-                __builtin_amdgcn_raw_buffer_store_b8((unsigned char)int8_code(q2, q_r), q8buf, o8 + ps.e2, 0, 0);
-                __builtin_amdgcn_raw_buffer_store_b8((unsigned char)int8_code(k1, k_r), k8buf, o8 + ps.e1, 0, 0);
-                __builtin_amdgcn_raw_buffer_store_b8((unsigned char)int8_code(k2, k_r), k8buf, o8 + ps.e2, 0, 0);
-                if (li == 0) a.q_amax[((int64_t)b * a.N + n) * a.heads + head] = qm;
-            }
-            // v: E4M3 codes of channels 2 li, 2 li + 1 into the transposed tile (zero past L)
-            const float x0 = load_elem<E>(vbuf, off + 2 * li * ES), x1 = load_elem<E>(vbuf, off + (2 * li + 1) * ES);
-            float y0, y1;
-            {
+            const int o8 = n * row8;
+            __builtin_amdgcn_raw_buffer_store_b64(pack_codes(x1, q_r), q8buf, o8 + rp.c1 * kCH, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b64(pack_codes(x2, q_r), q8buf, o8 + rp.c2 * kCH, 0, 0);
+            if (cp == 0) a.q_amax[((int64_t)b * a.N + n) * a.heads + head] = qm;
+            rotated_pair<E>(kbuf, n * row_bytes, rp, tab, a.T, a.H, q, x1, x2);
+            __builtin_amdgcn_raw_buffer_store_b64(pack_codes(x1, k_r), k8buf, o8 + rp.c1 * kCH, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b64(pack_codes(x2, k_r), k8buf, o8 + rp.c2 * kCH, 0, 0);
+        }
+        // v rows: rows tid / 16 + 16 i of the tile, channels 8 vc + [0, 8); zero past L
+        {
+            const f32x8 vam = *reinterpret_cast<const f32x8*>(a.v_amax + (int64_t)bh * kD + vc * kCH);
+            float vr[kCH];
+#pragma unroll
+            for (int e = 0; e < kCH; ++e) vr[e] = vam[e] > 0.f ? __fdiv_rn(448.f, vam[e]) : 0.f;
+            for (int rr = tid >> 4; rr < kQ8Tile; rr += kQ8Threads / 16) {
+                const int p = pt * kQ8Tile + rr;
+                const int n = p < L ? (int)scope_token(p, s, a.sparse_k, a.mode) : a.N;   // a.N reads 0
+                float x[kCH];
+                load_chunk<E>(vbuf, n * row_bytes + vc * kCH * ES, x);
+#pragma unroll
+                for (int e = 0; e < kCH; e += 2) {
+                    float y0, y1;
+                    {
 #pragma clang fp contract(off)
-                y0 = x0 * v_r0;
-                y1 = x1 * v_r1;
+                        y0 = x[e] * vr[e];
+                        y1 = x[e + 1] * vr[e + 1];
+                    }
+                    const unsigned pk = (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
+                    vt[(vc * kCH + e) * kVtPitch + rr] = (unsigned char)(pk & 0xff);
+                    vt[(vc * kCH + e + 1) * kVtPitch + rr] = (unsigned char)((pk >> 8) & 0xff);
+                }
             }
-            const unsigned pk = (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
-            vt[(2 * li) * kVtPitch + rr] = (unsigned char)(pk & 0xff);
-            vt[(2 * li + 1) * kVtPitch + rr] = (unsigned char)((pk >> 8) & 0xff);
         }
         __syncthreads();
-        // vt8 rows: D channel rows of 64 bytes, 16 bytes per thread step
-        unsigned char* dst = reinterpret_cast<unsigned char*>(a.vt8) + (((int64_t)bh * a.sparse_k + s) * D) * a.Lp +
+        // vt8 rows: kD channel rows of 64 bytes, one 16-byte piece per thread step
+        unsigned char* dst = reinterpret_cast<unsigned char*>(a.vt8) + (((int64_t)bh * a.sparse_k + s) * kD) * a.Lp +
                              (int64_t)pt * kQ8Tile;
-        for (int i = tid; i < D * (kQ8Tile / 16); i += kQ8Threads) {
+        for (int i = tid; i < kD * (kQ8Tile / 16); i += kQ8Threads) {
             const int c = i / (kQ8Tile / 16), g = i % (kQ8Tile / 16);
-            const unsigned char* src = vt + c * kVtPitch + 16 * g;
-            u32x4 w;
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                w[e] = (uint32_t)src[4 * e] | ((uint32_t)src[4 * e + 1] << 8) | ((uint32_t)src[4 * e + 2] << 16) |
-                       ((uint32_t)src[4 * e + 3] << 24);
-            *reinterpret_cast<u32x4*>(dst + (int64_t)c * a.Lp + 16 * g) = w;
+            *reinterpret_cast<u32x4*>(dst + (int64_t)c * a.Lp + 16 * g) =
+                *reinterpret_cast<const u32x4*>(vt + c * kVtPitch + 16 * g);
         }
         __syncthreads();
     }
 }
 
-template <int D, typename E>
+template <typename E>
 hipError_t launch_q8_t(const Q8Params& a, hipStream_t stream) {
     const size_t tab = (size_t)(a.T + a.H + a.W) * 256;
-    const int nk = a.B * a.heads, nv = a.B * a.heads * D;
+    const int nk = a.B * a.heads, nv = a.B * a.heads * kD;
     hipLaunchKernelGGL(q8_fill_kernel, dim3((nk + nv + kQ8Threads - 1) / kQ8Threads), dim3(kQ8Threads), 0, stream,
                        a.k_amax, a.v_amax, nk, nv);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const size_t lds_stats = tab + (size_t)4 * (64 / (D / 2)) * (D + 1) * 4;
-    hipLaunchKernelGGL((q8_stats_kernel<D, E>), dim3((a.N + kStatTokens - 1) / kStatTokens, a.B * a.heads),
+    const size_t lds_stats = tab + (size_t)((kQ8Threads / 16) * kD + kQ8Threads / 64) * 4;
+    hipLaunchKernelGGL((q8_stats_kernel<E>), dim3((a.N + kStatTokens - 1) / kStatTokens, a.B * a.heads),
                        dim3(kQ8Threads), lds_stats, stream, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int tasks = a.B * a.heads * a.sparse_k * (a.Lp / kQ8Tile);
-    const size_t lds_q = tab + (size_t)D * (kQ8Tile + 4);
-    hipLaunchKernelGGL((q8_quant_kernel<D, E>), dim3(tasks < kQ8MaxGrid ? tasks : kQ8MaxGrid), dim3(kQ8Threads),
+    const size_t lds_q = tab + (size_t)kD * kVtPitch;
+    hipLaunchKernelGGL((q8_quant_kernel<E>), dim3(tasks < kQ8MaxGrid ? tasks : kQ8MaxGrid), dim3(kQ8Threads),
                        lds_q, stream, a);
     return hipGetLastError();
 }
@@ -272,8 +295,8 @@ hipError_t launch_q8_t(const Q8Params& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_quant8(const Q8Params& a, int head_dim, int dtype, hipStream_t stream) {
-    if (head_dim == 128) return dtype == 0 ? launch_q8_t<128, BF16>(a, stream) : launch_q8_t<128, FP32>(a, stream);
-    return dtype == 0 ? launch_q8_t<64, BF16>(a, stream) : launch_q8_t<64, FP32>(a, stream);
+    if (head_dim != kD) return hipErrorInvalidValue;
+    return dtype == 0 ? launch_q8_t<BF16>(a, stream) : launch_q8_t<FP32>(a, stream);
 }
 
 int q8_scope_pitch(int L) { return (L + kQ8Tile - 1) / kQ8Tile * kQ8Tile; }
