@@ -44,6 +44,7 @@ def parse_args():
                     help="skip the per-workload attention timings (other grids, k in {1,2,4,8})")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass timing")
     ap.add_argument("--no-8bit", action="store_true", help="skip the 8-bit attention timing")
+    ap.add_argument("--no-schedule", action="store_true", help="skip the per-layer schedule timing")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -221,6 +222,45 @@ def eight_bit(sk, wl, q, k, v, stream, reps=20):
             "flop_per_call": flops, "per_mode": res}
 
 
+def schedule(sk, wl, q, k, v, stream, reps=5):
+    """An 8-layer U-shaped (sparse_k, mode) schedule on the 24x22x40 workload (k = 1, 2, 4, 8,
+    8, 4, 2, 1, modes alternating): one skiparse_attn_schedule call, and the same call
+    captured once in a HIP graph and replayed.  Counted FLOPs: the sum of the layers'."""
+    import torch
+    ws = wl.OSP_SINGLE
+    sched = sk.u_schedule(8, 8)
+    outs = [torch.empty_like(q) for _ in sched]
+    layers = [(q, k, v, o, kk, mode) for o, (kk, mode) in zip(outs, sched)]
+    flops = sum(sk.attn_flops(ws.B, ws.grid, ws.heads, ws.head_dim, kk) for kk, _ in sched)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev[0].record(stream)
+        for i in range(reps):
+            fn()
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        return sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(reps))[reps // 2]
+
+    eager_ms = timed(lambda: sk.attn_schedule(layers, ws.grid, stream=stream))
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        sk.attn_schedule(layers, ws.grid)
+    stream.wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        sk.attn_schedule(layers, ws.grid)
+    torch.cuda.synchronize()
+    graph_ms = timed(g.replay)
+    return {"layers": [{"sparse_k": kk, "mode": "single" if mode == 0 else "group"} for kk, mode in sched],
+            "flop_per_schedule": flops, "eager_ms": round(eager_ms, 3),
+            "eager_tflops": round(flops / (eager_ms * 1e-3) / 1e12, 1), "graph_ms": round(graph_ms, 3),
+            "graph_tflops": round(flops / (graph_ms * 1e-3) / 1e12, 1)}
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -362,6 +402,9 @@ def main():
 
     if not args.no_8bit:
         result["attn8"] = eight_bit(sk, wl, qg, kg, vg, stream)
+
+    if not args.no_schedule:
+        result["schedule"] = schedule(sk, wl, qg, kg, vg, stream)
 
     if not args.no_sweep:
         result["sweep"] = sweep(sk, wl, stream)

@@ -210,6 +210,35 @@ int skiparse_attn8(const void* q8, const float* q_amax, const void* k8,
                    int sparse_k, int mode, int out_dtype, void* out, void* stream);
 
 /*
+ * A per-layer schedule of Skiparse attention calls.  Open-Sora Plan's feature
+ * list describes SUV as a U-shaped sparse structure over the transformer's
+ * layers without giving the per-layer sparsity; a schedule is the knob that
+ * expresses one: every layer may use its own sparse_k and mode.
+ */
+typedef struct skiparse_layer {
+    const void* q;     /* (B, N, heads, head_dim) in the schedule's dtype */
+    const void* k;
+    const void* v;
+    void* out;         /* same layout; must not overlap this layer's q, k, v */
+    int sparse_k;
+    int mode;          /* SKIPARSE_SINGLE or SKIPARSE_GROUP */
+} skiparse_layer;
+
+/*
+ * skiparse_attn_schedule -- run n_layers skiparse_attn calls, layers[i] with
+ * its own buffers, sparse_k and mode, all on `stream` in order.  Every layer
+ * is validated first (same rules as skiparse_attn); if any is invalid nothing
+ * is launched and the status of the first invalid layer is returned.  Each
+ * layer is one kernel launch with no host synchronisation between them; the
+ * call allocates nothing and issues no memset, so a caller may capture it in a
+ * HIP graph and replay the whole schedule.  Results equal those of separate
+ * skiparse_attn calls bit for bit.  n_layers in [1, 4096].
+ */
+int skiparse_attn_schedule(const skiparse_layer* layers, int n_layers,
+                           int B, int T, int H, int W, int heads, int head_dim,
+                           int dtype, void* stream);
+
+/*
  * skiparse_rope_remap -- the materialised RoPE + rearrange of q, k and v in
  * one pass (the page's add_rope + *_skip_rearrange calls, before attention).
  *

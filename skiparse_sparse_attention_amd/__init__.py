@@ -17,6 +17,7 @@ from ._lib import (  # noqa: F401
     FP32,
     GROUP,
     LIB_PATH,
+    Layer,
     MAX_GRID_SUM,
     OK,
     SINGLE,
@@ -24,6 +25,7 @@ from ._lib import (  # noqa: F401
     attn,
     attn8,
     attn_bwd,
+    attn_schedule,
     attn_bwd_flops,
     attn_flops,
     attn_lse,
@@ -35,5 +37,6 @@ from ._lib import (  # noqa: F401
     rope_remap,
     scope_table,
     status_string,
+    u_schedule,
     version,
 )

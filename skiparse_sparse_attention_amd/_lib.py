@@ -32,6 +32,12 @@ MAX_GRID_SUM = 192
 _lib = None
 
 
+class Layer(ctypes.Structure):
+    """One entry of a schedule (the C struct skiparse_layer)."""
+    _fields_ = [("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("out", ctypes.c_void_p), ("sparse_k", ctypes.c_int), ("mode", ctypes.c_int)]
+
+
 class SkiparseError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
@@ -74,6 +80,8 @@ def lib():
         L.skiparse_quant8.restype = i
         L.skiparse_attn8.argtypes = [vp] * 6 + dims + [i, i, i, vp, vp]
         L.skiparse_attn8.restype = i
+        L.skiparse_attn_schedule.argtypes = [ctypes.POINTER(Layer), i] + dims + [i, vp]
+        L.skiparse_attn_schedule.restype = i
         L.skiparse_status_string.argtypes = [i]
         L.skiparse_status_string.restype = ctypes.c_char_p
         L.skiparse_version.argtypes = []
@@ -135,6 +143,35 @@ def attn(q, k, v, grid, sparse_k, mode, out=None, stream=None):
                                int(sparse_k), int(mode), _dtype_code(q), out.data_ptr(),
                                _stream_ptr(stream)), "skiparse_attn")
     return out
+
+
+def u_schedule(n_layers, k_max, modes=(SINGLE, GROUP)):
+    """A U-shaped per-layer (sparse_k, mode) list: dense (k = 1) at both ends, doubling towards
+    the middle up to k_max, modes alternating -- one example of the knob, not numbers from
+    the pages."""
+    out = []
+    for i in range(int(n_layers)):
+        depth = min(i, n_layers - 1 - i)
+        out.append((min(1 << depth, int(k_max)), modes[i % len(modes)]))
+    return out
+
+
+def attn_schedule(layers, grid, stream=None):
+    """Run a schedule: `layers` is a list of (q, k, v, out, sparse_k, mode); all layers share
+    shape and dtype.  One validation pass, then one launch per layer on one stream."""
+    if not layers:
+        raise ValueError("empty schedule")
+    q0 = layers[0][0]
+    B, T, H, W, heads, d = _dims(q0, grid)
+    arr = (Layer * len(layers))()
+    for i, (q, k, v, out, sk_, mode) in enumerate(layers):
+        for t in (q, k, v, out):
+            if t.shape != q0.shape or t.dtype != q0.dtype or not t.is_contiguous():
+                raise ValueError("every layer's q, k, v, out must share shape, dtype and be contiguous")
+        arr[i] = Layer(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), int(sk_), int(mode))
+    _check(lib().skiparse_attn_schedule(arr, len(layers), B, T, H, W, heads, d, _dtype_code(q0),
+                                        _stream_ptr(stream)), "skiparse_attn_schedule")
+    return [layer[3] for layer in layers]
 
 
 def attn_lse(q, k, v, grid, sparse_k, mode, out=None, lse=None, stream=None):

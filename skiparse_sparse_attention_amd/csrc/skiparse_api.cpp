@@ -134,6 +134,24 @@ int skiparse_attn(const void* q, const void* k, const void* v, int B, int T, int
     return attn_forward(q, k, v, B, T, H, W, heads, head_dim, sparse_k, mode, dtype, out, nullptr, stream);
 }
 
+int skiparse_attn_schedule(const skiparse_layer* layers, int n_layers, int B, int T, int H, int W, int heads,
+                           int head_dim, int dtype, void* stream) {
+    if (!layers) return SKIPARSE_E_NULL;
+    if (n_layers < 1 || n_layers > 4096) return SKIPARSE_E_SHAPE;
+    for (int i = 0; i < n_layers; ++i) {
+        const skiparse_layer& l = layers[i];
+        const int st = skiparse_validate(l.q, l.k, l.v, B, T, H, W, heads, head_dim, l.sparse_k, l.mode, dtype, l.out);
+        if (st != SKIPARSE_OK) return st;
+    }
+    for (int i = 0; i < n_layers; ++i) {
+        const skiparse_layer& l = layers[i];
+        const int st = attn_forward(l.q, l.k, l.v, B, T, H, W, heads, head_dim, l.sparse_k, l.mode, dtype, l.out,
+                                    nullptr, stream);
+        if (st != SKIPARSE_OK) return st;
+    }
+    return SKIPARSE_OK;
+}
+
 int skiparse_attn_lse(const void* q, const void* k, const void* v, int B, int T, int H, int W,
                       int heads, int head_dim, int sparse_k, int mode, int dtype, void* out,
                       float* lse, void* stream) {

@@ -31,7 +31,7 @@ def test_header_declares_the_boundary():
                  "skiparse_validate", "skiparse_scope_table", "skiparse_attn_flops",
                  "skiparse_status_string", "skiparse_version", "skiparse_attn_lse",
                  "skiparse_attn_bwd", "skiparse_attn_bwd_flops", "skiparse_quant8", "skiparse_attn8",
-                 "skiparse_q8_scope_pitch"):
+                 "skiparse_q8_scope_pitch", "skiparse_attn_schedule"):
         assert want in names
 
 
@@ -196,3 +196,23 @@ def test_8bit_calls_reject_before_any_device_call():
     assert _a8(head_dim=64) == sk.E_UNSUPPORTED
     assert _a8(out=DV) == sk.E_ALIAS                   # the output over an operand
     assert _a8(dtype=2) == sk.E_UNSUPPORTED
+
+
+def test_schedule_rejects_before_any_device_call():
+    L = sk.lib()
+    good = sk.Layer(Q, K, V, OUT, 2, 0)
+    bad_k = sk.Layer(Q, K, V, OUT, 3, 0)          # N = 256 is not divisible by 3
+    alias = sk.Layer(Q, K, V, Q, 2, 0)            # out over q
+    arr = (sk.Layer * 3)(good, bad_k, good)
+    args = (1, 4, 8, 8, 2, 64, 1, None)           # B, T, H, W, heads, head_dim, dtype, stream
+    assert L.skiparse_attn_schedule(arr, 3, *args) == sk.E_DIVISIBILITY
+    assert L.skiparse_attn_schedule((sk.Layer * 2)(good, alias), 2, *args) == sk.E_ALIAS
+    assert L.skiparse_attn_schedule(None, 1, *args) == sk.E_NULL
+    assert L.skiparse_attn_schedule(arr, 0, *args) == sk.E_SHAPE
+    assert L.skiparse_attn_schedule(arr, 5000, *args) == sk.E_SHAPE
+
+
+def test_u_schedule_shape():
+    assert sk.u_schedule(8, 8) == [(1, 0), (2, 1), (4, 0), (8, 1), (8, 0), (4, 1), (2, 0), (1, 1)]
+    ks = [k for k, _ in sk.u_schedule(9, 4)]
+    assert ks == ks[::-1] and ks[0] == 1 and max(ks) == 4
