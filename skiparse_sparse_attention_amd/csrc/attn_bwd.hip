@@ -28,6 +28,8 @@
 // epilogue, and every gradient row is written straight to its original token.  Keys past the
 // end of a scope start at -inf (weight exactly 0); queries past the end carry an infinite
 // log2-sum-exp (weight 0) and D = 0.
+#include <type_traits>
+
 #include "attn_common.hpp"
 #include "skiparse_device.hpp"
 #include "skiparse_launch.hpp"
@@ -175,7 +177,9 @@ __device__ __forceinline__ void store_unrotated(const f32x16 (&acc)[D / 32], flo
 // ---------------------------------------------------------------------------------------------
 // dQ (and D)
 // ---------------------------------------------------------------------------------------------
-template <int D, typename E>
+// KDIV: sparse_k divides the tile height, so row r + tile of a scope is token n(r) + tile * k
+// in both modes and the load cursors and grid positions advance by constants.
+template <int D, typename E, bool KDIV>
 __global__ void __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 attn_bwd_dq_kernel(AttnBwdParams a) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
@@ -271,20 +275,48 @@ attn_bwd_dq_kernel(AttnBwdParams a) {
     ChunkRaw<E, CH> kraw[2][2];
     Pos kpos[2];
     uint32_t vraw[kVPer][4];
-    auto load_kv = [&](int t) __attribute__((always_inline)) {
+    // cursors: token rows of this thread's K and V rows in the tile being loaded (KDIV: advanced
+    // by a constant per tile, grid positions with carries)
+    int kn[2], vn[kVPer];
+    const int tile_dn = kBwdKN * a.sparse_k;
+    const int dt = tile_dn / HW, drem = tile_dn % HW;
+    const int dh = drem / a.W, dw = drem % a.W;
+    auto set_rows = [&](int t) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            const int n = (int)scope_token(t * kBwdKN + krow + 32 * i, s, k_, a.mode);
-            buffer_load_dwords(kbuf, n * row_bytes + rp.c1 * CH * ES, kraw[i][0].w);
-            buffer_load_dwords(kbuf, n * row_bytes + rp.c2 * CH * ES, kraw[i][1].w);
-            kpos[i] = pos_of(n);
+            kn[i] = (int)scope_token(t * kBwdKN + krow + 32 * i, s, k_, a.mode);
+            kpos[i] = pos_of(kn[i]);
         }
 #pragma unroll
-        for (int i = 0; i < kVPer; ++i) {
-            const int idx = tid + kBwdThreads * i;
-            const int n = (int)scope_token(t * kBwdKN + idx / G, s, k_, a.mode);
-            buffer_load_8_as_bf16x2<E>(vbuf, n * row_bytes + (idx % G) * 8 * ES, vraw[i]);
+        for (int i = 0; i < kVPer; ++i) vn[i] = (int)scope_token(t * kBwdKN + (tid + kBwdThreads * i) / G, s, k_, a.mode);
+    };
+    auto advance_rows = [&](int t) __attribute__((always_inline)) {   // to tile t, from t - 1
+        if constexpr (KDIV) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                kn[i] += tile_dn;
+                int w = kpos[i].w + dw, c = w >= a.W;
+                kpos[i].w = w - (c ? a.W : 0);
+                int h = kpos[i].h + dh + c;
+                c = h >= a.H;
+                kpos[i].h = h - (c ? a.H : 0);
+                kpos[i].t += dt + c;
+            }
+#pragma unroll
+            for (int i = 0; i < kVPer; ++i) vn[i] += tile_dn;
+        } else {
+            set_rows(t);
         }
+    };
+    auto load_kv = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            buffer_load_dwords(kbuf, kn[i] * row_bytes + rp.c1 * CH * ES, kraw[i][0].w);
+            buffer_load_dwords(kbuf, kn[i] * row_bytes + rp.c2 * CH * ES, kraw[i][1].w);
+        }
+#pragma unroll
+        for (int i = 0; i < kVPer; ++i)
+            buffer_load_8_as_bf16x2<E>(vbuf, vn[i] * row_bytes + ((tid + kBwdThreads * i) % G) * 8 * ES, vraw[i]);
     };
     auto store_kv = [&](int buf) __attribute__((always_inline)) {
         char* kd = ktile + buf * L::kKTile;
@@ -319,11 +351,17 @@ attn_bwd_dq_kernel(AttnBwdParams a) {
 #pragma unroll
         for (int x = 0; x < 16; ++x) dqacc[db][x] = 0.f;
     const int nt = (a.L + kBwdKN - 1) / kBwdKN;
-    load_kv(0);
+    set_rows(0);
+    load_kv();
     store_kv(0);
     __syncthreads();
-    for (int t = 0; t < nt; ++t) {
-        if (t + 1 < nt) load_kv(t + 1);
+    // one key tile; `masked`: the last tile, whose keys past the end of the scope start at -inf
+    // (a separate instantiation, peeled out of the loop, so the other tiles carry no masking)
+    auto tile = [&](int t, auto masked) __attribute__((always_inline)) {
+        if (t + 1 < nt) {
+            advance_rows(t + 1);
+            load_kv();
+        }
         const char* kc = ktile + (t & 1) * L::kKTile;
         const char* vc = vtile + (t & 1) * L::kVTile;
         const int valid = a.L - t * kBwdKN;
@@ -332,7 +370,10 @@ attn_bwd_dq_kernel(AttnBwdParams a) {
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
             for (int x = 0; x < 16; ++x) {
-                sacc[kb][x] = kb * 32 + 8 * (x >> 2) + 4 * hf + (x & 3) < valid ? -lse_q : -__builtin_inff();
+                if constexpr (decltype(masked)::value)
+                    sacc[kb][x] = kb * 32 + 8 * (x >> 2) + 4 * hf + (x & 3) < valid ? -lse_q : -__builtin_inff();
+                else
+                    sacc[kb][x] = -lse_q;
                 dpacc[kb][x] = 0.f;
             }
 #pragma unroll
@@ -370,7 +411,9 @@ attn_bwd_dq_kernel(AttnBwdParams a) {
         if (t + 1 < nt) store_kv((t + 1) & 1);
         wait_vm_loads();
         __syncthreads();
-    }
+    };
+    for (int t = 0; t < nt - 1; ++t) tile(t, std::false_type{});
+    tile(nt - 1, std::true_type{});
 
     // ---- epilogue: dq = c * (transposed RoPE of dQ'), to the query's token ----
     if (!qvalid) return;
@@ -380,7 +423,8 @@ attn_bwd_dq_kernel(AttnBwdParams a) {
 // ---------------------------------------------------------------------------------------------
 // dK and dV
 // ---------------------------------------------------------------------------------------------
-template <int D, typename E>
+// KDIV: sparse_k divides the query-tile height (cursors advance by constants, as in the dq kernel)
+template <int D, typename E, bool KDIV>
 __global__ void __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 attn_bwd_dkdv_kernel(AttnBwdParams a) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
@@ -461,22 +505,44 @@ attn_bwd_dkdv_kernel(AttnBwdParams a) {
     Pos qpos;
     uint32_t oraw[kOPer][4];
     float ldv = 0.f;
-    auto load_q = [&](int i) __attribute__((always_inline)) {
-        const int n = (int)scope_token(i * kBwdQN + qrow, s, k_, a.mode);
-        buffer_load_dwords(qbuf, n * row_bytes + rp.c1 * CH * ES, qraw[0].w);
-        buffer_load_dwords(qbuf, n * row_bytes + rp.c2 * CH * ES, qraw[1].w);
-        qpos = pos_of(n);
+    // cursors of the tile being loaded: the Q row, the dO rows, the lse / D row (threads < 64)
+    int qn, on[kOPer], ln;
+    const int tile_dn = kBwdQN * a.sparse_k;
+    const int dt = tile_dn / HW, drem = tile_dn % HW;
+    const int dh = drem / a.W, dw = drem % a.W;
+    auto set_rows = [&](int i) __attribute__((always_inline)) {
+        qn = (int)scope_token(i * kBwdQN + qrow, s, k_, a.mode);
+        qpos = pos_of(qn);
 #pragma unroll
-        for (int j = 0; j < kOPer; ++j) {
-            const int idx = tid + kBwdThreads * j;
-            const int nn = (int)scope_token(i * kBwdQN + idx / G, s, k_, a.mode);
-            buffer_load_8_as_bf16x2<E>(dobuf, nn * row_bytes + (idx % G) * 8 * ES, oraw[j]);
+        for (int j = 0; j < kOPer; ++j) on[j] = (int)scope_token(i * kBwdQN + (tid + kBwdThreads * j) / G, s, k_, a.mode);
+        ln = (int)scope_token(i * kBwdQN + (tid % kBwdQN), s, k_, a.mode);
+    };
+    auto advance_rows = [&](int i) __attribute__((always_inline)) {   // to tile i, from i - 1
+        if constexpr (KDIV) {
+            qn += tile_dn;
+            int w = qpos.w + dw, c = w >= a.W;
+            qpos.w = w - (c ? a.W : 0);
+            int h = qpos.h + dh + c;
+            c = h >= a.H;
+            qpos.h = h - (c ? a.H : 0);
+            qpos.t += dt + c;
+#pragma unroll
+            for (int j = 0; j < kOPer; ++j) on[j] += tile_dn;
+            ln += tile_dn;
+        } else {
+            set_rows(i);
         }
+    };
+    auto load_q = [&](int i) __attribute__((always_inline)) {
+        buffer_load_dwords(qbuf, qn * row_bytes + rp.c1 * CH * ES, qraw[0].w);
+        buffer_load_dwords(qbuf, qn * row_bytes + rp.c2 * CH * ES, qraw[1].w);
+#pragma unroll
+        for (int j = 0; j < kOPer; ++j)
+            buffer_load_8_as_bf16x2<E>(dobuf, on[j] * row_bytes + ((tid + kBwdThreads * j) % G) * 8 * ES, oraw[j]);
         if (tid < 2 * kBwdQN) {
             const int p = i * kBwdQN + (tid % kBwdQN);
-            const int nn = (int)scope_token(p, s, k_, a.mode);
-            ldv = tid < kBwdQN ? (p < a.L ? a.lse[vec0 + nn] : __builtin_inff())
-                               : (p < a.L ? a.delta[vec0 + nn] : 0.f);
+            ldv = tid < kBwdQN ? (p < a.L ? a.lse[vec0 + ln] : __builtin_inff())
+                               : (p < a.L ? a.delta[vec0 + ln] : 0.f);
         }
     };
     auto store_q = [&](int buf) __attribute__((always_inline)) {
@@ -517,11 +583,15 @@ attn_bwd_dkdv_kernel(AttnBwdParams a) {
             dkacc[db][x] = 0.f;
         }
     const int nq = (a.L + kBwdQN - 1) / kBwdQN;
+    set_rows(0);
     load_q(0);
     store_q(0);
     __syncthreads();
     for (int i = 0; i < nq; ++i) {
-        if (i + 1 < nq) load_q(i + 1);
+        if (i + 1 < nq) {
+            advance_rows(i + 1);
+            load_q(i + 1);
+        }
         const char* qc = qtile + (i & 1) * L::kQTile;
         const char* oc = otile + (i & 1) * L::kOTile;
         const float* lc = ldt + (i & 1) * 2 * kBwdQN;
@@ -595,23 +665,31 @@ attn_bwd_dkdv_kernel(AttnBwdParams a) {
     store_unrotated<D, E>(dkacc, 0.69314718055994530942f, dkbuf, nk, row_bytes, pos_of(nk), tab, a.T, a.H, a.phi_mul, lane);
 }
 
-template <int D, typename E>
-static hipError_t launch_bwd_t(const AttnBwdParams& a, hipStream_t stream) {
+template <int D, typename E, bool KDQ, bool KKV>
+static hipError_t launch_bwd_k(const AttnBwdParams& a, hipStream_t stream) {
     typedef BwdLds<D> L;
     const size_t table = (size_t)(a.T + a.H + a.W) * 256;
     const size_t lds_dq = (size_t)L::kDqTab + table, lds_kv = (size_t)L::kDkvTab + table;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bwd_dq_kernel<D, E>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bwd_dq_kernel<D, E, KDQ>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_dq);
     if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<D, E>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<D, E, KKV>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_kv);
     if (e != hipSuccess) return e;
     // dq first: it writes D, which the dk/dv kernel reads (same stream, so in order)
-    hipLaunchKernelGGL((attn_bwd_dq_kernel<D, E>), dim3(a.num_work), dim3(kBwdThreads), lds_dq, stream, a);
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<D, E, KDQ>), dim3(a.num_work), dim3(kBwdThreads), lds_dq, stream, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, E>), dim3(a.num_work), dim3(kBwdThreads), lds_kv, stream, a);
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, E, KKV>), dim3(a.num_work), dim3(kBwdThreads), lds_kv, stream, a);
     return hipGetLastError();
+}
+
+template <int D, typename E>
+static hipError_t launch_bwd_t(const AttnBwdParams& a, hipStream_t stream) {
+    // sparse_k dividing 32 divides 64 too; otherwise both kernels take the general cursors
+    if (kBwdQN % a.sparse_k == 0) return launch_bwd_k<D, E, true, true>(a, stream);
+    if (kBwdKN % a.sparse_k == 0) return launch_bwd_k<D, E, true, false>(a, stream);
+    return launch_bwd_k<D, E, false, false>(a, stream);
 }
 
 hipError_t launch_attn_bwd(const AttnBwdParams& a, int head_dim, int dtype, hipStream_t stream) {
