@@ -43,7 +43,8 @@ namespace {
 constexpr int kBwdThreads = 256;   // 4 wavefronts, one per SIMD
 constexpr int kBwdRows = 128;      // queries (dq kernel) or keys (dk/dv kernel) per workgroup
 constexpr int kBwdKN = 64;         // keys per K/V tile of the dq kernel
-constexpr int kBwdQN = 32;         // queries per query tile of the dk/dv kernel
+constexpr int kBwdQN = 64;         // queries per query tile of the dk/dv kernel
+constexpr int kBwdQB = kBwdQN / 32; // 32-query blocks per query tile
 
 template <int D>
 struct BwdLds {
@@ -59,9 +60,9 @@ struct BwdLds {
     static constexpr int kQTile = kBwdQN * kPitch;
     static constexpr int kOTile = kBwdQN * kVPitch;
     static constexpr int kStage = kBwdRows * kPitch;
-    static constexpr int kLdOff = kStage;
-    static constexpr int kDkvTab = kStage + 2 * 2 * kBwdQN * 4;
-    static_assert(2 * kQTile + 2 * kOTile <= kStage, "query tiles fit the staging area");
+    static constexpr int kQTiles = 2 * kQTile + 2 * kOTile;
+    static constexpr int kLdOff = kStage > kQTiles ? kStage : kQTiles;
+    static constexpr int kDkvTab = kLdOff + 2 * 2 * kBwdQN * 4;
 };
 
 // 8 consecutive elements of E as a bf16x8 operand, and as floats (bf16 is exact both ways).
@@ -437,7 +438,7 @@ attn_bwd_dkdv_kernel(AttnBwdParams a) {
     constexpr int kOPer = kBwdQN * G / kBwdThreads;    // dO granules per thread per tile
     char* qtile = lds;
     char* otile = lds + 2 * L::kQTile;
-    float* ldt = reinterpret_cast<float*>(lds + L::kLdOff);   // [buf][0, 32): LSE, [buf][32, 64): D
+    float* ldt = reinterpret_cast<float*>(lds + L::kLdOff);   // [buf][0, QN): LSE, [buf][QN, 2 QN): D
     char* tab = lds + L::kDkvTab;
 
     const int tid = threadIdx.x;
@@ -500,32 +501,39 @@ attn_bwd_dkdv_kernel(AttnBwdParams a) {
     __syncthreads();   // the staging rows become query tiles
 
     // ---- query tiles: loaded into registers one tile ahead, staged at the end of a tile ----
-    const int qrow = tid >> 3;   // Q staging task: row qrow, chunk pair cp
-    ChunkRaw<E, CH> qraw[2];
-    Pos qpos;
+    constexpr int kQPer = kBwdQN * 8 / kBwdThreads;   // Q staging tasks per thread per tile
+    const int qrow = tid >> 3;   // Q staging tasks: rows qrow + 32 j, chunk pair cp
+    ChunkRaw<E, CH> qraw[kQPer][2];
+    Pos qpos[kQPer];
     uint32_t oraw[kOPer][4];
     float ldv = 0.f;
-    // cursors of the tile being loaded: the Q row, the dO rows, the lse / D row (threads < 64)
-    int qn, on[kOPer], ln;
+    // cursors of the tile being loaded: the Q rows, the dO rows, the lse / D row (threads < 2 QN)
+    int qn[kQPer], on[kOPer], ln;
     const int tile_dn = kBwdQN * a.sparse_k;
     const int dt = tile_dn / HW, drem = tile_dn % HW;
     const int dh = drem / a.W, dw = drem % a.W;
     auto set_rows = [&](int i) __attribute__((always_inline)) {
-        qn = (int)scope_token(i * kBwdQN + qrow, s, k_, a.mode);
-        qpos = pos_of(qn);
+#pragma unroll
+        for (int j = 0; j < kQPer; ++j) {
+            qn[j] = (int)scope_token(i * kBwdQN + qrow + 32 * j, s, k_, a.mode);
+            qpos[j] = pos_of(qn[j]);
+        }
 #pragma unroll
         for (int j = 0; j < kOPer; ++j) on[j] = (int)scope_token(i * kBwdQN + (tid + kBwdThreads * j) / G, s, k_, a.mode);
         ln = (int)scope_token(i * kBwdQN + (tid % kBwdQN), s, k_, a.mode);
     };
     auto advance_rows = [&](int i) __attribute__((always_inline)) {   // to tile i, from i - 1
         if constexpr (KDIV) {
-            qn += tile_dn;
-            int w = qpos.w + dw, c = w >= a.W;
-            qpos.w = w - (c ? a.W : 0);
-            int h = qpos.h + dh + c;
-            c = h >= a.H;
-            qpos.h = h - (c ? a.H : 0);
-            qpos.t += dt + c;
+#pragma unroll
+            for (int j = 0; j < kQPer; ++j) {
+                qn[j] += tile_dn;
+                int w = qpos[j].w + dw, c = w >= a.W;
+                qpos[j].w = w - (c ? a.W : 0);
+                int h = qpos[j].h + dh + c;
+                c = h >= a.H;
+                qpos[j].h = h - (c ? a.H : 0);
+                qpos[j].t += dt + c;
+            }
 #pragma unroll
             for (int j = 0; j < kOPer; ++j) on[j] += tile_dn;
             ln += tile_dn;
@@ -534,8 +542,11 @@ attn_bwd_dkdv_kernel(AttnBwdParams a) {
         }
     };
     auto load_q = [&](int i) __attribute__((always_inline)) {
-        buffer_load_dwords(qbuf, qn * row_bytes + rp.c1 * CH * ES, qraw[0].w);
-        buffer_load_dwords(qbuf, qn * row_bytes + rp.c2 * CH * ES, qraw[1].w);
+#pragma unroll
+        for (int j = 0; j < kQPer; ++j) {
+            buffer_load_dwords(qbuf, qn[j] * row_bytes + rp.c1 * CH * ES, qraw[j][0].w);
+            buffer_load_dwords(qbuf, qn[j] * row_bytes + rp.c2 * CH * ES, qraw[j][1].w);
+        }
 #pragma unroll
         for (int j = 0; j < kOPer; ++j)
             buffer_load_8_as_bf16x2<E>(dobuf, on[j] * row_bytes + ((tid + kBwdThreads * j) % G) * 8 * ES, oraw[j]);
@@ -546,22 +557,25 @@ attn_bwd_dkdv_kernel(AttnBwdParams a) {
         }
     };
     auto store_q = [&](int buf) __attribute__((always_inline)) {
-        float x1[CH], x2[CH];
-        raw_to_f32(qraw[0], x1);
-        raw_to_f32(qraw[1], x2);
-        const int pos = rp.axis == 0 ? min(qpos.t, a.T - 1) : (rp.axis == 1 ? qpos.h : qpos.w);
-        const char* row = tab + rope_tab_offset<D>(a.T, a.H, rp.axis, pos, rp.jchunk * CH, rp.axis == 2 ? a.phi_mul : 0);
-        f32x4 cs[CH / 2];
 #pragma unroll
-        for (int j = 0; j < CH / 2; ++j) cs[j] = *reinterpret_cast<const f32x4*>(row + 16 * j);
-        rope_rotate_cs<CH>(x1, x2, cs);
+        for (int jq = 0; jq < kQPer; ++jq) {
+            float x1[CH], x2[CH];
+            raw_to_f32(qraw[jq][0], x1);
+            raw_to_f32(qraw[jq][1], x2);
+            const int pos = rp.axis == 0 ? min(qpos[jq].t, a.T - 1) : (rp.axis == 1 ? qpos[jq].h : qpos[jq].w);
+            const char* row = tab + rope_tab_offset<D>(a.T, a.H, rp.axis, pos, rp.jchunk * CH, rp.axis == 2 ? a.phi_mul : 0);
+            f32x4 cs[CH / 2];
 #pragma unroll
-        for (int e = 0; e < CH; ++e) {
-            x1[e] *= a.scale_log2;
-            x2[e] *= a.scale_log2;
+            for (int j = 0; j < CH / 2; ++j) cs[j] = *reinterpret_cast<const f32x4*>(row + 16 * j);
+            rope_rotate_cs<CH>(x1, x2, cs);
+#pragma unroll
+            for (int e = 0; e < CH; ++e) {
+                x1[e] *= a.scale_log2;
+                x2[e] *= a.scale_log2;
+            }
+            char* dst = qtile + buf * L::kQTile + (qrow + 32 * jq) * L::kPitch;
+            store_rotated_chunks<CH>(dst + 2 * cp * CH * 2, dst + (2 * cp + 1) * CH * 2, x1, x2);
         }
-        char* dst = qtile + buf * L::kQTile + qrow * L::kPitch;
-        store_rotated_chunks<CH>(dst + 2 * cp * CH * 2, dst + (2 * cp + 1) * CH * 2, x1, x2);
         char* od = otile + buf * L::kOTile;
 #pragma unroll
         for (int j = 0; j < kOPer; ++j) {
@@ -595,41 +609,49 @@ attn_bwd_dkdv_kernel(AttnBwdParams a) {
         const char* qc = qtile + (i & 1) * L::kQTile;
         const char* oc = otile + (i & 1) * L::kOTile;
         const float* lc = ldt + (i & 1) * 2 * kBwdQN;
-        // start values -LSE and D of the 16 queries 8 g + 4 hf + jj this lane's accumulator rows hold
-        f32x16 sacc, dpacc;
-        float dd[16];
+        // start values -LSE and D of the queries 32 qb + 8 g + 4 hf + jj this lane's accumulator rows hold
+        f32x16 sacc[kBwdQB], dpacc[kBwdQB];
+        float dd[kBwdQB][16];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const f32x4 l4 = *reinterpret_cast<const f32x4*>(lc + 8 * g + 4 * hf);
-            const f32x4 d4 = *reinterpret_cast<const f32x4*>(lc + kBwdQN + 8 * g + 4 * hf);
+        for (int qb = 0; qb < kBwdQB; ++qb)
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                sacc[4 * g + jj] = -l4[jj];
-                dd[4 * g + jj] = d4[jj];
-                dpacc[4 * g + jj] = 0.f;
+            for (int g = 0; g < 4; ++g) {
+                const f32x4 l4 = *reinterpret_cast<const f32x4*>(lc + 32 * qb + 8 * g + 4 * hf);
+                const f32x4 d4 = *reinterpret_cast<const f32x4*>(lc + kBwdQN + 32 * qb + 8 * g + 4 * hf);
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    sacc[qb][4 * g + jj] = -l4[jj];
+                    dd[qb][4 * g + jj] = d4[jj];
+                    dpacc[qb][4 * g + jj] = 0.f;
+                }
             }
-        }
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qc + l32 * L::kPitch + (2 * ks + hf) * 16);
-            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kreg[ks], sacc, 0, 0, 0);
-            const bf16x8 oa = *reinterpret_cast<const bf16x8*>(oc + l32 * L::kVPitch + (((2 * ks + hf) ^ vswz<D>(l32)) * 16));
-            dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vreg[ks], dpacc, 0, 0, 0);
-        }
-        // P and dZ as bf16 B operands (query 8 g + 4 hf + jj in k-step g / 2, slot 4 (g % 2) + jj)
-        bf16x8 pbb[2], dzb[2];
+        for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int x = 4 * g + jj;
-                const float p = __builtin_amdgcn_exp2f(sacc[x]);
-                pbb[g >> 1][(g & 1) * 4 + jj] = (__bf16)p;
-                dzb[g >> 1][(g & 1) * 4 + jj] = (__bf16)(p * (dpacc[x] - dd[x]));
+            for (int qb = 0; qb < kBwdQB; ++qb) {
+                const int r = 32 * qb + l32;
+                const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qc + r * L::kPitch + (2 * ks + hf) * 16);
+                sacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kreg[ks], sacc[qb], 0, 0, 0);
+                const bf16x8 oa = *reinterpret_cast<const bf16x8*>(oc + r * L::kVPitch + (((2 * ks + hf) ^ vswz<D>(r)) * 16));
+                dpacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vreg[ks], dpacc[qb], 0, 0, 0);
             }
+        // P and dZ as bf16 B operands (query 32 qb + 8 g + 4 hf + jj in k-step 2 qb + g / 2, slot
+        // 4 (g % 2) + jj)
+        bf16x8 pbb[2 * kBwdQB], dzb[2 * kBwdQB];
+#pragma unroll
+        for (int qb = 0; qb < kBwdQB; ++qb)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int x = 4 * g + jj;
+                    const float p = __builtin_amdgcn_exp2f(sacc[qb][x]);
+                    pbb[2 * qb + (g >> 1)][(g & 1) * 4 + jj] = (__bf16)p;
+                    dzb[2 * qb + (g >> 1)][(g & 1) * 4 + jj] = (__bf16)(p * (dpacc[qb][x] - dd[qb][x]));
+                }
         // dV^T += dO^T P and dK^T += Q'^T dZ, both A operands from transpose reads
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
+        for (int kk = 0; kk < 2 * kBwdQB; ++kk)
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
                 const int r0 = 16 * kk + tr.row, r8 = r0 + 8;
@@ -686,9 +708,8 @@ static hipError_t launch_bwd_k(const AttnBwdParams& a, hipStream_t stream) {
 
 template <int D, typename E>
 static hipError_t launch_bwd_t(const AttnBwdParams& a, hipStream_t stream) {
-    // sparse_k dividing 32 divides 64 too; otherwise both kernels take the general cursors
-    if (kBwdQN % a.sparse_k == 0) return launch_bwd_k<D, E, true, true>(a, stream);
-    if (kBwdKN % a.sparse_k == 0) return launch_bwd_k<D, E, true, false>(a, stream);
+    static_assert(kBwdQN == kBwdKN, "one divisibility test covers both tile heights");
+    if (kBwdKN % a.sparse_k == 0) return launch_bwd_k<D, E, true, true>(a, stream);
     return launch_bwd_k<D, E, false, false>(a, stream);
 }
 
