@@ -45,6 +45,7 @@ constexpr int kBwdRows = 128;      // queries (dq kernel) or keys (dk/dv kernel)
 constexpr int kBwdKN = 64;         // keys per K/V tile of the dq kernel
 constexpr int kBwdQN = 64;         // queries per query tile of the dk/dv kernel
 constexpr int kBwdQB = kBwdQN / 32; // 32-query blocks per query tile
+constexpr int kRing = 4;            // depth of the MFMA operand register rings
 
 template <int D>
 struct BwdLds {
@@ -377,16 +378,41 @@ attn_bwd_dq_kernel(AttnBwdParams a) {
                     sacc[kb][x] = -lse_q;
                 dpacc[kb][x] = 0.f;
             }
+        // S^T = K Q'^T and dP^T = V dO^T in (ks, kb) steps; the K and V operands come from a
+        // 4-deep register ring read 3 steps ahead, so the LDS latency overlaps the MFMAs
+        {
+            constexpr int NST = KS * KB;
+            auto kop = [&](int st) __attribute__((always_inline)) {
+                const int r = (st % KB) * 32 + l32;
+                return *reinterpret_cast<const bf16x8*>(kc + r * L::kPitch + (2 * (st / KB) + hf) * 16);
+            };
+            auto vop = [&](int st) __attribute__((always_inline)) {
+                const int r = (st % KB) * 32 + l32;
+                return *reinterpret_cast<const bf16x8*>(vc + r * L::kVPitch + (((2 * (st / KB) + hf) ^ vswz<D>(r)) * 16));
+            };
+            bf16x8 ka[kRing], va[kRing];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-                const int r = kb * 32 + l32;
-                const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kc + r * L::kPitch + (2 * ks + hf) * 16);
-                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[ks], sacc[kb], 0, 0, 0);
-                const bf16x8 va = *reinterpret_cast<const bf16x8*>(vc + r * L::kVPitch + (((2 * ks + hf) ^ vswz<D>(r)) * 16));
-                dpacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, doreg[ks], dpacc[kb], 0, 0, 0);
+            for (int st = 0; st < kRing - 1; ++st) {
+                ka[st] = kop(st);
+                va[st] = vop(st);
             }
+#pragma unroll
+            for (int st = 0; st < NST; ++st) {
+                if (st + kRing - 1 < NST) {
+                    ka[(st + kRing - 1) % kRing] = kop(st + kRing - 1);
+                    va[(st + kRing - 1) % kRing] = vop(st + kRing - 1);
+                }
+                sacc[st % KB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[st % kRing], qreg[st / KB], sacc[st % KB], 0, 0, 0);
+                dpacc[st % KB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[st % kRing], doreg[st / KB], dpacc[st % KB], 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * (kRing - 1), 0);
+#pragma unroll
+            for (int i = 0; i < NST - (kRing - 1); ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 2 * (kRing - 1), 0);
+        }
         // dZ^T = P^T * (dP^T - D), as the bf16 B operand (keys 8 g + 4 hf + jj of block kb sit
         // in k-step 2 kb + g / 2, slot 4 (g % 2) + jj)
         bf16x8 dzb[KK];
@@ -400,15 +426,29 @@ attn_bwd_dq_kernel(AttnBwdParams a) {
                     const float p = __builtin_amdgcn_exp2f(sacc[kb][x]);
                     dzb[2 * kb + (g >> 1)][(g & 1) * 4 + jj] = (__bf16)(p * (dpacc[kb][x] - dq_d));
                 }
-        // dQ'^T += K^T dZ^T, K^T from transpose reads of the row-major K tile
+        // dQ'^T += K^T dZ^T, K^T from transpose reads of the row-major K tile (ring as above)
+        {
+            constexpr int NST = KK * DB;
+            auto top = [&](int st) __attribute__((always_inline)) {
+                const char* base = kc + (16 * (st / DB) + tr.row) * L::kPitch + (4 * (st % DB) + tr.gran) * 16 + tr.byte;
+                return tr_operand(base, base + 8 * L::kPitch);
+            };
+            bf16x8 ta[kRing];
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk)
+            for (int st = 0; st < kRing - 1; ++st) ta[st] = top(st);
 #pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                const char* base = kc + (16 * kk + tr.row) * L::kPitch + (4 * db + tr.gran) * 16 + tr.byte;
-                const bf16x8 ka = tr_operand(base, base + 8 * L::kPitch);
-                dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, dzb[kk], dqacc[db], 0, 0, 0);
+            for (int st = 0; st < NST; ++st) {
+                if (st + kRing - 1 < NST) ta[(st + kRing - 1) % kRing] = top(st + kRing - 1);
+                dqacc[st % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[st % kRing], dzb[st / DB], dqacc[st % DB], 0, 0, 0);
             }
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * (kRing - 1), 0);
+#pragma unroll
+            for (int i = 0; i < NST - (kRing - 1); ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, kRing - 1, 0);
+        }
         if (t + 1 < nt) store_kv((t + 1) & 1);
         wait_vm_loads();
         __syncthreads();
@@ -625,16 +665,40 @@ attn_bwd_dkdv_kernel(AttnBwdParams a) {
                     dpacc[qb][4 * g + jj] = 0.f;
                 }
             }
+        // S = Q' K'^T and dP = dO V^T in (ks, qb) steps, operands through a 4-deep register ring
+        {
+            constexpr int NST = KS * kBwdQB;
+            auto qop = [&](int st) __attribute__((always_inline)) {
+                const int r = 32 * (st % kBwdQB) + l32;
+                return *reinterpret_cast<const bf16x8*>(qc + r * L::kPitch + (2 * (st / kBwdQB) + hf) * 16);
+            };
+            auto oop = [&](int st) __attribute__((always_inline)) {
+                const int r = 32 * (st % kBwdQB) + l32;
+                return *reinterpret_cast<const bf16x8*>(oc + r * L::kVPitch + (((2 * (st / kBwdQB) + hf) ^ vswz<D>(r)) * 16));
+            };
+            bf16x8 qa[kRing], oa[kRing];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-            for (int qb = 0; qb < kBwdQB; ++qb) {
-                const int r = 32 * qb + l32;
-                const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qc + r * L::kPitch + (2 * ks + hf) * 16);
-                sacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kreg[ks], sacc[qb], 0, 0, 0);
-                const bf16x8 oa = *reinterpret_cast<const bf16x8*>(oc + r * L::kVPitch + (((2 * ks + hf) ^ vswz<D>(r)) * 16));
-                dpacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vreg[ks], dpacc[qb], 0, 0, 0);
+            for (int st = 0; st < kRing - 1; ++st) {
+                qa[st] = qop(st);
+                oa[st] = oop(st);
             }
+#pragma unroll
+            for (int st = 0; st < NST; ++st) {
+                if (st + kRing - 1 < NST) {
+                    qa[(st + kRing - 1) % kRing] = qop(st + kRing - 1);
+                    oa[(st + kRing - 1) % kRing] = oop(st + kRing - 1);
+                }
+                sacc[st % kBwdQB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[st % kRing], kreg[st / kBwdQB], sacc[st % kBwdQB], 0, 0, 0);
+                dpacc[st % kBwdQB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[st % kRing], vreg[st / kBwdQB], dpacc[st % kBwdQB], 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * (kRing - 1), 0);
+#pragma unroll
+            for (int i = 0; i < NST - (kRing - 1); ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 2 * (kRing - 1), 0);
+        }
         // P and dZ as bf16 B operands (query 32 qb + 8 g + 4 hf + jj in k-step 2 qb + g / 2, slot
         // 4 (g % 2) + jj)
         bf16x8 pbb[2 * kBwdQB], dzb[2 * kBwdQB];
@@ -649,19 +713,43 @@ attn_bwd_dkdv_kernel(AttnBwdParams a) {
                     pbb[2 * qb + (g >> 1)][(g & 1) * 4 + jj] = (__bf16)p;
                     dzb[2 * qb + (g >> 1)][(g & 1) * 4 + jj] = (__bf16)(p * (dpacc[qb][x] - dd[qb][x]));
                 }
-        // dV^T += dO^T P and dK^T += Q'^T dZ, both A operands from transpose reads
-#pragma unroll
-        for (int kk = 0; kk < 2 * kBwdQB; ++kk)
-#pragma unroll
-            for (int db = 0; db < DB; ++db) {
+        // dV^T += dO^T P and dK^T += Q'^T dZ, both A operands from transpose reads (ring as above)
+        {
+            constexpr int NST = 2 * kBwdQB * DB;
+            auto dop = [&](int st) __attribute__((always_inline)) {
+                const int kk = st / DB, db = st % DB;
                 const int r0 = 16 * kk + tr.row, r8 = r0 + 8;
-                const bf16x8 oa = tr_operand(oc + r0 * L::kVPitch + (((4 * db + tr.gran) ^ vswz<D>(r0)) * 16) + tr.byte,
-                                             oc + r8 * L::kVPitch + (((4 * db + tr.gran) ^ vswz<D>(r8)) * 16) + tr.byte);
-                dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, pbb[kk], dvacc[db], 0, 0, 0);
-                const char* qb = qc + r0 * L::kPitch + (4 * db + tr.gran) * 16 + tr.byte;
-                const bf16x8 qa = tr_operand(qb, qb + 8 * L::kPitch);
-                dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, dzb[kk], dkacc[db], 0, 0, 0);
+                return tr_operand(oc + r0 * L::kVPitch + (((4 * db + tr.gran) ^ vswz<D>(r0)) * 16) + tr.byte,
+                                  oc + r8 * L::kVPitch + (((4 * db + tr.gran) ^ vswz<D>(r8)) * 16) + tr.byte);
+            };
+            auto kop2 = [&](int st) __attribute__((always_inline)) {
+                const int kk = st / DB, db = st % DB;
+                const char* qb = qc + (16 * kk + tr.row) * L::kPitch + (4 * db + tr.gran) * 16 + tr.byte;
+                return tr_operand(qb, qb + 8 * L::kPitch);
+            };
+            bf16x8 da[kRing], ka2[kRing];
+#pragma unroll
+            for (int st = 0; st < kRing - 1; ++st) {
+                da[st] = dop(st);
+                ka2[st] = kop2(st);
             }
+#pragma unroll
+            for (int st = 0; st < NST; ++st) {
+                if (st + kRing - 1 < NST) {
+                    da[(st + kRing - 1) % kRing] = dop(st + kRing - 1);
+                    ka2[(st + kRing - 1) % kRing] = kop2(st + kRing - 1);
+                }
+                dvacc[st % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[st % kRing], pbb[st / DB], dvacc[st % DB], 0, 0, 0);
+                dkacc[st % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka2[st % kRing], dzb[st / DB], dkacc[st % DB], 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x100, 4 * (kRing - 1), 0);
+#pragma unroll
+            for (int i = 0; i < NST - (kRing - 1); ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 2 * (kRing - 1), 0);
+        }
         if (i + 1 < nq) store_q((i + 1) & 1);
         wait_vm_loads();
         __syncthreads();
