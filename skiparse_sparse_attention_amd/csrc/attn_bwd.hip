@@ -40,7 +40,9 @@ using namespace attn;
 
 namespace {
 
-constexpr int kBwdThreads = 256;   // 4 wavefronts, one per SIMD
+constexpr int kBwdThreads = 256;   // dk/dv kernel: 4 wavefronts, one per SIMD
+constexpr int kDqThreads = 512;    // dq kernel: 8 wavefronts, two per SIMD
+constexpr int kDqRows = 256;       // queries per dq workgroup
 constexpr int kBwdRows = 128;      // queries (dq kernel) or keys (dk/dv kernel) per workgroup
 constexpr int kBwdKN = 64;         // keys per K/V tile of the dq kernel
 constexpr int kBwdQN = 64;         // queries per query tile of the dk/dv kernel
@@ -51,11 +53,11 @@ template <int D>
 struct BwdLds {
     static constexpr int kPitch = D * 2 + 16;   // rotated Q/K rows, pair-slot order, one pad granule
     static constexpr int kVPitch = D * 2;       // V / dO rows, natural order, swizzled granules
-    // dq kernel: two K tiles (the Q staging of 128 rows aliases them), two V tiles, the table
+    // dq kernel: two K tiles and two V tiles (aliased first by the Q staging of 256 rows), the table
     static constexpr int kKTile = kBwdKN * kPitch;
     static constexpr int kVTile = kBwdKN * kVPitch;
-    static constexpr int kDqTab = 2 * kKTile + 2 * kVTile;
-    static_assert(kBwdRows * kPitch <= 2 * kKTile, "Q staging fits the K tiles");
+    static constexpr int kDqTiles = 2 * kKTile + 2 * kVTile;
+    static constexpr int kDqTab = kDqTiles > kDqRows * kPitch ? kDqTiles : kDqRows * kPitch;
     // dk/dv kernel: K staging (128 rows), aliased afterwards by two Q and two dO tiles; the
     // log2-sum-exp and D of two query tiles; the table
     static constexpr int kQTile = kBwdQN * kPitch;
@@ -181,8 +183,14 @@ __device__ __forceinline__ void store_unrotated(const f32x16 (&acc)[D / 32], flo
 // ---------------------------------------------------------------------------------------------
 // KDIV: sparse_k divides the tile height, so row r + tile of a scope is token n(r) + tile * k
 // in both modes and the load cursors and grid positions advance by constants.
+//
+// 8 wavefronts (two per SIMD) of 32 queries.  Each 64-key tile is processed one 32-key block
+// at a time (S^T and dP^T of the block, its dZ^T, its two 16-key steps of dQ'^T), so only one
+// block's score accumulators are live and a wavefront fits in 256 VGPRs: the MFMAs take their
+// accumulators in VGPRs (no AGPR copies) and the two wavefronts of a SIMD hide each other's
+// LDS and dependency latency.
 template <int D, typename E, bool KDIV>
-__global__ void __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(kDqThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_bwd_dq_kernel(AttnBwdParams a) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     typedef BwdLds<D> L;
@@ -190,10 +198,10 @@ attn_bwd_dq_kernel(AttnBwdParams a) {
     constexpr int KS = D / 16;        // 16-deep k-steps over head_dim
     constexpr int DB = D / 32;        // 32-row blocks of head_dim
     constexpr int KB = kBwdKN / 32;   // 32-key blocks per tile
-    constexpr int KK = kBwdKN / 16;   // 16-key steps per tile
     constexpr int ES = E::kBytes;
     constexpr int G = D / 8;          // 16-byte granules per V row (bf16)
-    constexpr int kVPer = kBwdKN * G / kBwdThreads;   // V granules per thread per tile
+    constexpr int kVPer = kBwdKN * G / kDqThreads;    // V granules per thread per tile
+    static_assert(kBwdKN * 8 == kDqThreads, "one K staging task per thread per tile");
     char* ktile = lds;
     char* vtile = lds + 2 * L::kKTile;
     char* tab = lds + L::kDqTab;
@@ -203,8 +211,8 @@ attn_bwd_dq_kernel(AttnBwdParams a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, hf = lane >> 5;
     const int work = xcd_remap(blockIdx.x, gridDim.x);
-    const int qt = work % a.tiles;
-    const int sc = work / a.tiles;
+    const int qt = work % a.dq_tiles;
+    const int sc = work / a.dq_tiles;
     const int s = sc % a.sparse_k;
     const int bh = sc / a.sparse_k;
     const int head = bh % a.heads;
@@ -234,9 +242,9 @@ attn_bwd_dq_kernel(AttnBwdParams a) {
 
     // ---- Q tile: rotated, scaled by log2(e)/sqrt(d), through LDS into B-operand registers ----
 #pragma unroll 2
-    for (int it = 0; it < kBwdRows * 8 / kBwdThreads; ++it) {
-        const int r = (tid >> 3) + it * (kBwdThreads / 8);
-        const int n = (int)scope_token(qt * kBwdRows + r, s, k_, a.mode);   // >= N past the scope end
+    for (int it = 0; it < kDqRows * 8 / kDqThreads; ++it) {
+        const int r = (tid >> 3) + it * (kDqThreads / 8);
+        const int n = (int)scope_token(qt * kDqRows + r, s, k_, a.mode);   // >= N past the scope end
         stage_rotated_pair<D, E>(qbuf, n * row_bytes, rp, cp, tab, a.T, a.H, pos_of(n), a.phi_mul, a.scale_log2,
                                  ktile + r * L::kPitch);
     }
@@ -250,7 +258,7 @@ attn_bwd_dq_kernel(AttnBwdParams a) {
     __syncthreads();   // the staging rows become K tiles
 
     // ---- this lane's query: dO as the B operand of dP^T = V dO^T (natural order), D, LSE ----
-    const int pq = qt * kBwdRows + wave * 32 + l32;
+    const int pq = qt * kDqRows + wave * 32 + l32;
     const int nq = (int)scope_token(pq, s, k_, a.mode);
     const bool qvalid = pq < a.L;
     bf16x8 doreg[KS];
@@ -273,37 +281,31 @@ attn_bwd_dq_kernel(AttnBwdParams a) {
     const float lse_q = qvalid ? a.lse[vec0 + nq] : 0.f;
 
     // ---- K/V tiles: loaded into registers one tile ahead, staged at the end of a tile ----
-    const int krow = tid >> 3;   // K staging tasks: rows krow and krow + 32, chunk pair cp
-    ChunkRaw<E, CH> kraw[2][2];
-    Pos kpos[2];
+    const int krow = tid >> 3;   // K staging task: row krow, chunk pair cp
+    ChunkRaw<E, CH> kraw[2];
+    Pos kpos;
     uint32_t vraw[kVPer][4];
     // cursors: token rows of this thread's K and V rows in the tile being loaded (KDIV: advanced
     // by a constant per tile, grid positions with carries)
-    int kn[2], vn[kVPer];
+    int kn, vn[kVPer];
     const int tile_dn = kBwdKN * a.sparse_k;
     const int dt = tile_dn / HW, drem = tile_dn % HW;
     const int dh = drem / a.W, dw = drem % a.W;
     auto set_rows = [&](int t) __attribute__((always_inline)) {
+        kn = (int)scope_token(t * kBwdKN + krow, s, k_, a.mode);
+        kpos = pos_of(kn);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            kn[i] = (int)scope_token(t * kBwdKN + krow + 32 * i, s, k_, a.mode);
-            kpos[i] = pos_of(kn[i]);
-        }
-#pragma unroll
-        for (int i = 0; i < kVPer; ++i) vn[i] = (int)scope_token(t * kBwdKN + (tid + kBwdThreads * i) / G, s, k_, a.mode);
+        for (int i = 0; i < kVPer; ++i) vn[i] = (int)scope_token(t * kBwdKN + (tid + kDqThreads * i) / G, s, k_, a.mode);
     };
     auto advance_rows = [&](int t) __attribute__((always_inline)) {   // to tile t, from t - 1
         if constexpr (KDIV) {
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                kn[i] += tile_dn;
-                int w = kpos[i].w + dw, c = w >= a.W;
-                kpos[i].w = w - (c ? a.W : 0);
-                int h = kpos[i].h + dh + c;
-                c = h >= a.H;
-                kpos[i].h = h - (c ? a.H : 0);
-                kpos[i].t += dt + c;
-            }
+            kn += tile_dn;
+            int w = kpos.w + dw, c = w >= a.W;
+            kpos.w = w - (c ? a.W : 0);
+            int h = kpos.h + dh + c;
+            c = h >= a.H;
+            kpos.h = h - (c ? a.H : 0);
+            kpos.t += dt + c;
 #pragma unroll
             for (int i = 0; i < kVPer; ++i) vn[i] += tile_dn;
         } else {
@@ -311,35 +313,29 @@ attn_bwd_dq_kernel(AttnBwdParams a) {
         }
     };
     auto load_kv = [&]() __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            buffer_load_dwords(kbuf, kn[i] * row_bytes + rp.c1 * CH * ES, kraw[i][0].w);
-            buffer_load_dwords(kbuf, kn[i] * row_bytes + rp.c2 * CH * ES, kraw[i][1].w);
-        }
+        buffer_load_dwords(kbuf, kn * row_bytes + rp.c1 * CH * ES, kraw[0].w);
+        buffer_load_dwords(kbuf, kn * row_bytes + rp.c2 * CH * ES, kraw[1].w);
 #pragma unroll
         for (int i = 0; i < kVPer; ++i)
-            buffer_load_8_as_bf16x2<E>(vbuf, vn[i] * row_bytes + ((tid + kBwdThreads * i) % G) * 8 * ES, vraw[i]);
+            buffer_load_8_as_bf16x2<E>(vbuf, vn[i] * row_bytes + ((tid + kDqThreads * i) % G) * 8 * ES, vraw[i]);
     };
     auto store_kv = [&](int buf) __attribute__((always_inline)) {
         char* kd = ktile + buf * L::kKTile;
+        float x1[CH], x2[CH];
+        raw_to_f32(kraw[0], x1);
+        raw_to_f32(kraw[1], x2);
+        const int pos = rp.axis == 0 ? min(kpos.t, a.T - 1) : (rp.axis == 1 ? kpos.h : kpos.w);
+        const char* row = tab + rope_tab_offset<D>(a.T, a.H, rp.axis, pos, rp.jchunk * CH, rp.axis == 2 ? a.phi_mul : 0);
+        f32x4 cs[CH / 2];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            float x1[CH], x2[CH];
-            raw_to_f32(kraw[i][0], x1);
-            raw_to_f32(kraw[i][1], x2);
-            const int pos = rp.axis == 0 ? min(kpos[i].t, a.T - 1) : (rp.axis == 1 ? kpos[i].h : kpos[i].w);
-            const char* row = tab + rope_tab_offset<D>(a.T, a.H, rp.axis, pos, rp.jchunk * CH, rp.axis == 2 ? a.phi_mul : 0);
-            f32x4 cs[CH / 2];
-#pragma unroll
-            for (int j = 0; j < CH / 2; ++j) cs[j] = *reinterpret_cast<const f32x4*>(row + 16 * j);
-            rope_rotate_cs<CH>(x1, x2, cs);
-            char* dst = kd + (krow + 32 * i) * L::kPitch;
-            store_rotated_chunks<CH>(dst + 2 * cp * CH * 2, dst + (2 * cp + 1) * CH * 2, x1, x2);
-        }
+        for (int j = 0; j < CH / 2; ++j) cs[j] = *reinterpret_cast<const f32x4*>(row + 16 * j);
+        rope_rotate_cs<CH>(x1, x2, cs);
+        char* dst = kd + krow * L::kPitch;
+        store_rotated_chunks<CH>(dst + 2 * cp * CH * 2, dst + (2 * cp + 1) * CH * 2, x1, x2);
         char* vd = vtile + buf * L::kVTile;
 #pragma unroll
         for (int i = 0; i < kVPer; ++i) {
-            const int idx = tid + kBwdThreads * i;
+            const int idx = tid + kDqThreads * i;
             const int r = idx / G;
             *reinterpret_cast<u32x4*>(vd + r * L::kVPitch + (((idx % G) ^ vswz<D>(r)) * 16)) =
                 u32x4{vraw[i][0], vraw[i][1], vraw[i][2], vraw[i][3]};
@@ -357,6 +353,7 @@ attn_bwd_dq_kernel(AttnBwdParams a) {
     load_kv();
     store_kv(0);
     __syncthreads();
+    constexpr int kR = 3;   // depth of the operand rings
     // one key tile; `masked`: the last tile, whose keys past the end of the scope start at -inf
     // (a separate instantiation, peeled out of the loop, so the other tiles carry no masking)
     auto tile = [&](int t, auto masked) __attribute__((always_inline)) {
@@ -367,87 +364,69 @@ attn_bwd_dq_kernel(AttnBwdParams a) {
         const char* kc = ktile + (t & 1) * L::kKTile;
         const char* vc = vtile + (t & 1) * L::kVTile;
         const int valid = a.L - t * kBwdKN;
-        f32x16 sacc[KB], dpacc[KB];
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
+        for (int kb = 0; kb < KB; ++kb) {
+            // S^T = K Q'^T and dP^T = V dO^T of the 32-key block, operands through rings
+            f32x16 sacc, dpacc;
 #pragma unroll
             for (int x = 0; x < 16; ++x) {
                 if constexpr (decltype(masked)::value)
-                    sacc[kb][x] = kb * 32 + 8 * (x >> 2) + 4 * hf + (x & 3) < valid ? -lse_q : -__builtin_inff();
+                    sacc[x] = kb * 32 + 8 * (x >> 2) + 4 * hf + (x & 3) < valid ? -lse_q : -__builtin_inff();
                 else
-                    sacc[kb][x] = -lse_q;
-                dpacc[kb][x] = 0.f;
+                    sacc[x] = -lse_q;
+                dpacc[x] = 0.f;
             }
-        // S^T = K Q'^T and dP^T = V dO^T in (ks, kb) steps; the K and V operands come from a
-        // 4-deep register ring read 3 steps ahead, so the LDS latency overlaps the MFMAs
-        {
-            constexpr int NST = KS * KB;
-            auto kop = [&](int st) __attribute__((always_inline)) {
-                const int r = (st % KB) * 32 + l32;
-                return *reinterpret_cast<const bf16x8*>(kc + r * L::kPitch + (2 * (st / KB) + hf) * 16);
-            };
-            auto vop = [&](int st) __attribute__((always_inline)) {
-                const int r = (st % KB) * 32 + l32;
-                return *reinterpret_cast<const bf16x8*>(vc + r * L::kVPitch + (((2 * (st / KB) + hf) ^ vswz<D>(r)) * 16));
-            };
-            bf16x8 ka[kRing], va[kRing];
+            {
+                const int r = kb * 32 + l32;
+                auto kop = [&](int ks) __attribute__((always_inline)) {
+                    return *reinterpret_cast<const bf16x8*>(kc + r * L::kPitch + (2 * ks + hf) * 16);
+                };
+                auto vop = [&](int ks) __attribute__((always_inline)) {
+                    return *reinterpret_cast<const bf16x8*>(vc + r * L::kVPitch + (((2 * ks + hf) ^ vswz<D>(r)) * 16));
+                };
+                bf16x8 ka[kR], va[kR];
 #pragma unroll
-            for (int st = 0; st < kRing - 1; ++st) {
-                ka[st] = kop(st);
-                va[st] = vop(st);
-            }
-#pragma unroll
-            for (int st = 0; st < NST; ++st) {
-                if (st + kRing - 1 < NST) {
-                    ka[(st + kRing - 1) % kRing] = kop(st + kRing - 1);
-                    va[(st + kRing - 1) % kRing] = vop(st + kRing - 1);
+                for (int ks = 0; ks < kR - 1; ++ks) {
+                    ka[ks] = kop(ks);
+                    va[ks] = vop(ks);
                 }
-                sacc[st % KB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[st % kRing], qreg[st / KB], sacc[st % KB], 0, 0, 0);
-                dpacc[st % KB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[st % kRing], doreg[st / KB], dpacc[st % KB], 0, 0, 0);
-            }
-            __builtin_amdgcn_sched_group_barrier(0x100, 2 * (kRing - 1), 0);
 #pragma unroll
-            for (int i = 0; i < NST - (kRing - 1); ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                for (int ks = 0; ks < KS; ++ks) {
+                    if (ks + kR - 1 < KS) {
+                        ka[(ks + kR - 1) % kR] = kop(ks + kR - 1);
+                        va[(ks + kR - 1) % kR] = vop(ks + kR - 1);
+                    }
+                    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks % kR], qreg[ks], sacc, 0, 0, 0);
+                    dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[ks % kR], doreg[ks], dpacc, 0, 0, 0);
+                }
             }
-            __builtin_amdgcn_sched_group_barrier(0x008, 2 * (kRing - 1), 0);
-        }
-        // dZ^T = P^T * (dP^T - D), as the bf16 B operand (keys 8 g + 4 hf + jj of block kb sit
-        // in k-step 2 kb + g / 2, slot 4 (g % 2) + jj)
-        bf16x8 dzb[KK];
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
+            // dZ^T = P^T * (dP^T - D) of the block as two bf16 B operands (keys 8 g + 4 hf + jj
+            // sit in 16-key step g / 2, slot 4 (g % 2) + jj)
+            bf16x8 dzb[2];
 #pragma unroll
             for (int g = 0; g < 4; ++g)
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {
                     const int x = 4 * g + jj;
-                    const float p = __builtin_amdgcn_exp2f(sacc[kb][x]);
-                    dzb[2 * kb + (g >> 1)][(g & 1) * 4 + jj] = (__bf16)(p * (dpacc[kb][x] - dq_d));
+                    const float p = __builtin_amdgcn_exp2f(sacc[x]);
+                    dzb[g >> 1][(g & 1) * 4 + jj] = (__bf16)(p * (dpacc[x] - dq_d));
                 }
-        // dQ'^T += K^T dZ^T, K^T from transpose reads of the row-major K tile (ring as above)
-        {
-            constexpr int NST = KK * DB;
-            auto top = [&](int st) __attribute__((always_inline)) {
-                const char* base = kc + (16 * (st / DB) + tr.row) * L::kPitch + (4 * (st % DB) + tr.gran) * 16 + tr.byte;
-                return tr_operand(base, base + 8 * L::kPitch);
-            };
-            bf16x8 ta[kRing];
+            // dQ'^T += K^T dZ^T over the block's two 16-key steps, K^T from transpose reads
+            {
+                constexpr int NST = 2 * DB;
+                auto top = [&](int st) __attribute__((always_inline)) {
+                    const char* base = kc + (32 * kb + 16 * (st / DB) + tr.row) * L::kPitch + (4 * (st % DB) + tr.gran) * 16 + tr.byte;
+                    return tr_operand(base, base + 8 * L::kPitch);
+                };
+                bf16x8 ta[kR];
 #pragma unroll
-            for (int st = 0; st < kRing - 1; ++st) ta[st] = top(st);
+                for (int st = 0; st < kR - 1; ++st) ta[st] = top(st);
 #pragma unroll
-            for (int st = 0; st < NST; ++st) {
-                if (st + kRing - 1 < NST) ta[(st + kRing - 1) % kRing] = top(st + kRing - 1);
-                dqacc[st % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[st % kRing], dzb[st / DB], dqacc[st % DB], 0, 0, 0);
+                for (int st = 0; st < NST; ++st) {
+                    if (st + kR - 1 < NST) ta[(st + kR - 1) % kR] = top(st + kR - 1);
+                    dqacc[st % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[st % kR], dzb[st / DB], dqacc[st % DB], 0, 0, 0);
+                }
             }
-            __builtin_amdgcn_sched_group_barrier(0x100, 2 * (kRing - 1), 0);
-#pragma unroll
-            for (int i = 0; i < NST - (kRing - 1); ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            }
-            __builtin_amdgcn_sched_group_barrier(0x008, kRing - 1, 0);
         }
         if (t + 1 < nt) store_kv((t + 1) & 1);
         wait_vm_loads();
@@ -787,7 +766,7 @@ static hipError_t launch_bwd_k(const AttnBwdParams& a, hipStream_t stream) {
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_kv);
     if (e != hipSuccess) return e;
     // dq first: it writes D, which the dk/dv kernel reads (same stream, so in order)
-    hipLaunchKernelGGL((attn_bwd_dq_kernel<D, E, KDQ>), dim3(a.num_work), dim3(kBwdThreads), lds_dq, stream, a);
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<D, E, KDQ>), dim3(a.dq_num_work), dim3(kDqThreads), lds_dq, stream, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, E, KKV>), dim3(a.num_work), dim3(kBwdThreads), lds_kv, stream, a);
@@ -807,5 +786,6 @@ hipError_t launch_attn_bwd(const AttnBwdParams& a, int head_dim, int dtype, hipS
 }
 
 int attn_bwd_block_rows() { return kBwdRows; }
+int attn_bwd_dq_rows() { return kDqRows; }
 
 }  // namespace skiparse

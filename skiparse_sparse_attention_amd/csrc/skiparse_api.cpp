@@ -202,6 +202,9 @@ int skiparse_attn_bwd(const void* q, const void* k, const void* v, const void* o
     const int64_t work = (int64_t)B * heads * sparse_k * a.tiles;
     if (work > kI32Max) return SKIPARSE_E_SHAPE;
     a.num_work = (int)work;
+    const int dq_rows = skiparse::attn_bwd_dq_rows();
+    a.dq_tiles = (int)((d.L + dq_rows - 1) / dq_rows);
+    a.dq_num_work = (int)((int64_t)B * heads * sparse_k * a.dq_tiles);
     a.scale = (float)(1.0 / std::sqrt((double)head_dim));
     a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)head_dim));
     a.phi_mul = phi_mul_of(mode, sparse_k);

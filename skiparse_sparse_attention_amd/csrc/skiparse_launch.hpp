@@ -51,8 +51,10 @@ struct AttnBwdParams {
     void* dk;
     void* dv;
     int B, T, H, W, heads, sparse_k, mode, N, L;
-    int tiles;           // ceil(L / 128): query tiles of the dq kernel, key tiles of the dk/dv kernel
-    int num_work;        // B*heads*sparse_k*tiles workgroups per kernel
+    int tiles;           // ceil(L / 128): key tiles of the dk/dv kernel
+    int num_work;        // B*heads*sparse_k*tiles workgroups of the dk/dv kernel
+    int dq_tiles;        // ceil(L / 256): query tiles of the dq kernel
+    int dq_num_work;     // B*heads*sparse_k*dq_tiles workgroups of the dq kernel
     float scale_log2;    // log2(e) / sqrt(head_dim)
     float scale;         // 1 / sqrt(head_dim)
     int phi_mul;
@@ -93,7 +95,8 @@ hipError_t launch_reverse(const ReverseParams& a, hipStream_t stream, int grid);
 hipError_t launch_attn(const AttnParams& a, int head_dim, int dtype, hipStream_t stream);
 hipError_t launch_attn_bwd(const AttnBwdParams& a, int head_dim, int dtype, hipStream_t stream);
 int attn_block_rows();  // query rows per attention workgroup
-int attn_bwd_block_rows();  // queries / keys per backward workgroup
+int attn_bwd_block_rows();  // keys per dk/dv workgroup
+int attn_bwd_dq_rows();     // queries per dq workgroup
 int attn_tile_keys();   // keys per attention K/V tile
 hipError_t launch_quant8(const Q8Params& a, int head_dim, int dtype, hipStream_t stream);
 hipError_t launch_attn8(const Attn8Params& a, hipStream_t stream);
