@@ -40,14 +40,12 @@ using namespace attn;
 
 namespace {
 
-constexpr int kBwdThreads = 256;   // dk/dv kernel: 4 wavefronts, one per SIMD
 constexpr int kDqThreads = 512;    // dq kernel: 8 wavefronts, two per SIMD
 constexpr int kDqRows = 256;       // queries per dq workgroup
+constexpr int kKvThreads = 512;    // dk/dv kernel: 8 wavefronts, two per SIMD
 constexpr int kBwdRows = 128;      // queries (dq kernel) or keys (dk/dv kernel) per workgroup
 constexpr int kBwdKN = 64;         // keys per K/V tile of the dq kernel
 constexpr int kBwdQN = 64;         // queries per query tile of the dk/dv kernel
-constexpr int kBwdQB = kBwdQN / 32; // 32-query blocks per query tile
-constexpr int kRing = 4;            // depth of the MFMA operand register rings
 
 template <int D>
 struct BwdLds {
@@ -62,10 +60,16 @@ struct BwdLds {
     // log2-sum-exp and D of two query tiles; the table
     static constexpr int kQTile = kBwdQN * kPitch;
     static constexpr int kOTile = kBwdQN * kVPitch;
-    static constexpr int kStage = kBwdRows * kPitch;
-    static constexpr int kQTiles = 2 * kQTile + 2 * kOTile;
-    static constexpr int kLdOff = kStage > kQTiles ? kStage : kQTiles;
-    static constexpr int kDkvTab = kLdOff + 2 * 2 * kBwdQN * 4;
+    // dk/dv kernel: resident K' and V rows of the workgroup's keys, one Q' and one dO tile, the
+    // log2-sum-exp and D of the tile, the table (the reduction at the end reuses the tiles)
+    static constexpr int kKvK = 0;
+    static constexpr int kKvV = kKvK + kBwdRows * kPitch;
+    static constexpr int kKvQ = kKvV + kBwdRows * kVPitch;
+    static constexpr int kKvO = kKvQ + kQTile;
+    static constexpr int kKvLd = kKvO + kOTile;
+    static constexpr int kKvTab = kKvLd + 2 * kBwdQN * 4;
+    static constexpr int kDkvTab = kKvTab;
+    static_assert(4 * 16 * (D / 32) * 64 * 4 <= kKvLd, "the dV / dK exchange fits the tiles");
 };
 
 // 8 consecutive elements of E as a bf16x8 operand, and as floats (bf16 is exact both ways).
@@ -444,8 +448,14 @@ attn_bwd_dq_kernel(AttnBwdParams a) {
 // dK and dV
 // ---------------------------------------------------------------------------------------------
 // KDIV: sparse_k divides the query-tile height (cursors advance by constants, as in the dq kernel)
+//
+// 8 wavefronts (two per SIMD).  Wavefronts w and w + 4 (one SIMD) own the same 32 keys and take
+// the two 32-query halves of every 64-query tile; at the end they add their partial dV and dK
+// through LDS.  Every MFMA operand comes from LDS (the K', V rows of the workgroup's 128 keys
+// stay resident; the Q', dO tile is staged once per query tile), so a wavefront fits in 256
+// VGPRs and its accumulators stay in VGPRs.
 template <int D, typename E, bool KDIV>
-__global__ void __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_bwd_dkdv_kernel(AttnBwdParams a) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     typedef BwdLds<D> L;
@@ -453,16 +463,22 @@ attn_bwd_dkdv_kernel(AttnBwdParams a) {
     constexpr int KS = D / 16;
     constexpr int DB = D / 32;
     constexpr int ES = E::kBytes;
-    constexpr int G = D / 8;                           // 16-byte granules per dO row (bf16)
-    constexpr int kOPer = kBwdQN * G / kBwdThreads;    // dO granules per thread per tile
-    char* qtile = lds;
-    char* otile = lds + 2 * L::kQTile;
-    float* ldt = reinterpret_cast<float*>(lds + L::kLdOff);   // [buf][0, QN): LSE, [buf][QN, 2 QN): D
-    char* tab = lds + L::kDkvTab;
+    constexpr int G = D / 8;                           // 16-byte granules per dO / V row (bf16)
+    constexpr int kOPer = kBwdQN * G / kKvThreads;     // dO granules per thread per tile
+    constexpr int kQPer = kBwdQN * 8 / kKvThreads;     // Q staging tasks per thread per tile
+    constexpr int kKPer = kBwdRows * 8 / kKvThreads;   // K staging tasks per thread
+    constexpr int kVPer = kBwdRows * G / kKvThreads;   // V granules per thread
+    char* kres = lds + L::kKvK;       // resident K' rows of the workgroup's keys
+    char* vres = lds + L::kKvV;       // resident V rows
+    char* qtile = lds + L::kKvQ;      // Q' rows of the current query tile
+    char* otile = lds + L::kKvO;      // dO rows of the current query tile
+    float* ldt = reinterpret_cast<float*>(lds + L::kKvLd);   // [0, QN): LSE, [QN, 2 QN): D
+    char* tab = lds + L::kKvTab;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int kgrp = wave & 3, qhalf = wave >> 2;
     const int l32 = lane & 31, hf = lane >> 5;
     const int work = xcd_remap(blockIdx.x, gridDim.x);
     const int kt = work % a.tiles;
@@ -494,65 +510,54 @@ attn_bwd_dkdv_kernel(AttnBwdParams a) {
     const RopePair rp = rope_pair(cp);
     __syncthreads();
 
-    // ---- K tile (rotated, unscaled) through LDS into B-operand registers; V of this lane's key ----
-#pragma unroll 2
-    for (int it = 0; it < kBwdRows * 8 / kBwdThreads; ++it) {
-        const int r = (tid >> 3) + it * (kBwdThreads / 8);
+    // ---- resident K' (rotated, unscaled) and V rows of the workgroup's 128 keys ----
+#pragma unroll
+    for (int it = 0; it < kKPer; ++it) {
+        const int r = (tid >> 3) + it * (kKvThreads / 8);
         const int n = (int)scope_token(kt * kBwdRows + r, s, k_, a.mode);
         stage_rotated_pair<D, E>(kbuf, n * row_bytes, rp, cp, tab, a.T, a.H, pos_of(n), a.phi_mul, 1.0f,
-                                 lds + r * L::kPitch);
+                                 kres + r * L::kPitch);
     }
-    __syncthreads();
-    bf16x8 kreg[KS];
-    {
-        const char* krow = lds + (wave * 32 + l32) * L::kPitch;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) kreg[ks] = *reinterpret_cast<const bf16x8*>(krow + (2 * ks + hf) * 16);
+    for (int i = 0; i < kVPer; ++i) {
+        const int idx = tid + kKvThreads * i;
+        const int r = idx / G;
+        const int n = (int)scope_token(kt * kBwdRows + r, s, k_, a.mode);
+        uint32_t w[4];
+        buffer_load_8_as_bf16x2<E>(vbuf, n * row_bytes + (idx % G) * 8 * ES, w);
+        *reinterpret_cast<u32x4*>(vres + r * L::kVPitch + (((idx % G) ^ vswz<D>(r)) * 16)) = u32x4{w[0], w[1], w[2], w[3]};
     }
-    const int pk = kt * kBwdRows + wave * 32 + l32;
+    const int pk = kt * kBwdRows + kgrp * 32 + l32;   // this lane's key (the B-operand column)
     const int nk = (int)scope_token(pk, s, k_, a.mode);
-    bf16x8 vreg[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        float xv[8];
-        vreg[ks] = load8<E>(vbuf, nk * row_bytes + (2 * ks + hf) * 8 * ES, xv);
-    }
-    __syncthreads();   // the staging rows become query tiles
+    const int kr = kgrp * 32 + l32;                    // its row in the resident tiles
 
-    // ---- query tiles: loaded into registers one tile ahead, staged at the end of a tile ----
-    constexpr int kQPer = kBwdQN * 8 / kBwdThreads;   // Q staging tasks per thread per tile
-    const int qrow = tid >> 3;   // Q staging tasks: rows qrow + 32 j, chunk pair cp
-    ChunkRaw<E, CH> qraw[kQPer][2];
-    Pos qpos[kQPer];
+    // ---- query tiles: loaded into registers one tile ahead, staged at the start of a tile ----
+    const int qrow = tid >> 3;   // Q staging task: row qrow, chunk pair cp
+    static_assert(kQPer == 1, "one Q staging task per thread per tile");
+    ChunkRaw<E, CH> qraw[2];
+    Pos qpos;
     uint32_t oraw[kOPer][4];
     float ldv = 0.f;
-    // cursors of the tile being loaded: the Q rows, the dO rows, the lse / D row (threads < 2 QN)
-    int qn[kQPer], on[kOPer], ln;
+    int qn, on[kOPer], ln;
     const int tile_dn = kBwdQN * a.sparse_k;
     const int dt = tile_dn / HW, drem = tile_dn % HW;
     const int dh = drem / a.W, dw = drem % a.W;
     auto set_rows = [&](int i) __attribute__((always_inline)) {
+        qn = (int)scope_token(i * kBwdQN + qrow, s, k_, a.mode);
+        qpos = pos_of(qn);
 #pragma unroll
-        for (int j = 0; j < kQPer; ++j) {
-            qn[j] = (int)scope_token(i * kBwdQN + qrow + 32 * j, s, k_, a.mode);
-            qpos[j] = pos_of(qn[j]);
-        }
-#pragma unroll
-        for (int j = 0; j < kOPer; ++j) on[j] = (int)scope_token(i * kBwdQN + (tid + kBwdThreads * j) / G, s, k_, a.mode);
+        for (int j = 0; j < kOPer; ++j) on[j] = (int)scope_token(i * kBwdQN + (tid + kKvThreads * j) / G, s, k_, a.mode);
         ln = (int)scope_token(i * kBwdQN + (tid % kBwdQN), s, k_, a.mode);
     };
     auto advance_rows = [&](int i) __attribute__((always_inline)) {   // to tile i, from i - 1
         if constexpr (KDIV) {
-#pragma unroll
-            for (int j = 0; j < kQPer; ++j) {
-                qn[j] += tile_dn;
-                int w = qpos[j].w + dw, c = w >= a.W;
-                qpos[j].w = w - (c ? a.W : 0);
-                int h = qpos[j].h + dh + c;
-                c = h >= a.H;
-                qpos[j].h = h - (c ? a.H : 0);
-                qpos[j].t += dt + c;
-            }
+            qn += tile_dn;
+            int w = qpos.w + dw, c = w >= a.W;
+            qpos.w = w - (c ? a.W : 0);
+            int h = qpos.h + dh + c;
+            c = h >= a.H;
+            qpos.h = h - (c ? a.H : 0);
+            qpos.t += dt + c;
 #pragma unroll
             for (int j = 0; j < kOPer; ++j) on[j] += tile_dn;
             ln += tile_dn;
@@ -561,49 +566,42 @@ attn_bwd_dkdv_kernel(AttnBwdParams a) {
         }
     };
     auto load_q = [&](int i) __attribute__((always_inline)) {
-#pragma unroll
-        for (int j = 0; j < kQPer; ++j) {
-            buffer_load_dwords(qbuf, qn[j] * row_bytes + rp.c1 * CH * ES, qraw[j][0].w);
-            buffer_load_dwords(qbuf, qn[j] * row_bytes + rp.c2 * CH * ES, qraw[j][1].w);
-        }
+        buffer_load_dwords(qbuf, qn * row_bytes + rp.c1 * CH * ES, qraw[0].w);
+        buffer_load_dwords(qbuf, qn * row_bytes + rp.c2 * CH * ES, qraw[1].w);
 #pragma unroll
         for (int j = 0; j < kOPer; ++j)
-            buffer_load_8_as_bf16x2<E>(dobuf, on[j] * row_bytes + ((tid + kBwdThreads * j) % G) * 8 * ES, oraw[j]);
+            buffer_load_8_as_bf16x2<E>(dobuf, on[j] * row_bytes + ((tid + kKvThreads * j) % G) * 8 * ES, oraw[j]);
         if (tid < 2 * kBwdQN) {
             const int p = i * kBwdQN + (tid % kBwdQN);
             ldv = tid < kBwdQN ? (p < a.L ? a.lse[vec0 + ln] : __builtin_inff())
                                : (p < a.L ? a.delta[vec0 + ln] : 0.f);
         }
     };
-    auto store_q = [&](int buf) __attribute__((always_inline)) {
+    auto store_q = [&]() __attribute__((always_inline)) {
+        float x1[CH], x2[CH];
+        raw_to_f32(qraw[0], x1);
+        raw_to_f32(qraw[1], x2);
+        const int pos = rp.axis == 0 ? min(qpos.t, a.T - 1) : (rp.axis == 1 ? qpos.h : qpos.w);
+        const char* row = tab + rope_tab_offset<D>(a.T, a.H, rp.axis, pos, rp.jchunk * CH, rp.axis == 2 ? a.phi_mul : 0);
+        f32x4 cs[CH / 2];
 #pragma unroll
-        for (int jq = 0; jq < kQPer; ++jq) {
-            float x1[CH], x2[CH];
-            raw_to_f32(qraw[jq][0], x1);
-            raw_to_f32(qraw[jq][1], x2);
-            const int pos = rp.axis == 0 ? min(qpos[jq].t, a.T - 1) : (rp.axis == 1 ? qpos[jq].h : qpos[jq].w);
-            const char* row = tab + rope_tab_offset<D>(a.T, a.H, rp.axis, pos, rp.jchunk * CH, rp.axis == 2 ? a.phi_mul : 0);
-            f32x4 cs[CH / 2];
+        for (int j = 0; j < CH / 2; ++j) cs[j] = *reinterpret_cast<const f32x4*>(row + 16 * j);
+        rope_rotate_cs<CH>(x1, x2, cs);
 #pragma unroll
-            for (int j = 0; j < CH / 2; ++j) cs[j] = *reinterpret_cast<const f32x4*>(row + 16 * j);
-            rope_rotate_cs<CH>(x1, x2, cs);
-#pragma unroll
-            for (int e = 0; e < CH; ++e) {
-                x1[e] *= a.scale_log2;
-                x2[e] *= a.scale_log2;
-            }
-            char* dst = qtile + buf * L::kQTile + (qrow + 32 * jq) * L::kPitch;
-            store_rotated_chunks<CH>(dst + 2 * cp * CH * 2, dst + (2 * cp + 1) * CH * 2, x1, x2);
+        for (int e = 0; e < CH; ++e) {
+            x1[e] *= a.scale_log2;
+            x2[e] *= a.scale_log2;
         }
-        char* od = otile + buf * L::kOTile;
+        char* dst = qtile + qrow * L::kPitch;
+        store_rotated_chunks<CH>(dst + 2 * cp * CH * 2, dst + (2 * cp + 1) * CH * 2, x1, x2);
 #pragma unroll
         for (int j = 0; j < kOPer; ++j) {
-            const int idx = tid + kBwdThreads * j;
+            const int idx = tid + kKvThreads * j;
             const int r = idx / G;
-            *reinterpret_cast<u32x4*>(od + r * L::kVPitch + (((idx % G) ^ vswz<D>(r)) * 16)) =
+            *reinterpret_cast<u32x4*>(otile + r * L::kVPitch + (((idx % G) ^ vswz<D>(r)) * 16)) =
                 u32x4{oraw[j][0], oraw[j][1], oraw[j][2], oraw[j][3]};
         }
-        if (tid < 2 * kBwdQN) ldt[buf * 2 * kBwdQN + tid] = ldv;
+        if (tid < 2 * kBwdQN) ldt[tid] = ldv;
     };
 
     const TrLane tr(lane);
@@ -615,127 +613,132 @@ attn_bwd_dkdv_kernel(AttnBwdParams a) {
             dvacc[db][x] = 0.f;
             dkacc[db][x] = 0.f;
         }
+    constexpr int kR = 2;   // depth of the operand rings
+    const int qb0 = 32 * qhalf;   // this wavefront's query rows in each tile
     const int nq = (a.L + kBwdQN - 1) / kBwdQN;
     set_rows(0);
     load_q(0);
-    store_q(0);
-    __syncthreads();
     for (int i = 0; i < nq; ++i) {
+        wait_vm_loads();
+        __syncthreads();           // every read of the previous tile's Q', dO is done
+        store_q();
+        __syncthreads();
         if (i + 1 < nq) {
             advance_rows(i + 1);
             load_q(i + 1);
         }
-        const char* qc = qtile + (i & 1) * L::kQTile;
-        const char* oc = otile + (i & 1) * L::kOTile;
-        const float* lc = ldt + (i & 1) * 2 * kBwdQN;
-        // start values -LSE and D of the queries 32 qb + 8 g + 4 hf + jj this lane's accumulator rows hold
-        f32x16 sacc[kBwdQB], dpacc[kBwdQB];
-        float dd[kBwdQB][16];
+        // start values -LSE and D of the queries qb0 + 8 g + 4 hf + jj this lane's accumulator rows hold
+        f32x16 sacc, dpacc;
+        float dd[16];
 #pragma unroll
-        for (int qb = 0; qb < kBwdQB; ++qb)
+        for (int g = 0; g < 4; ++g) {
+            const f32x4 l4 = *reinterpret_cast<const f32x4*>(ldt + qb0 + 8 * g + 4 * hf);
+            const f32x4 d4 = *reinterpret_cast<const f32x4*>(ldt + kBwdQN + qb0 + 8 * g + 4 * hf);
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const f32x4 l4 = *reinterpret_cast<const f32x4*>(lc + 32 * qb + 8 * g + 4 * hf);
-                const f32x4 d4 = *reinterpret_cast<const f32x4*>(lc + kBwdQN + 32 * qb + 8 * g + 4 * hf);
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    sacc[qb][4 * g + jj] = -l4[jj];
-                    dd[qb][4 * g + jj] = d4[jj];
-                    dpacc[qb][4 * g + jj] = 0.f;
-                }
+            for (int jj = 0; jj < 4; ++jj) {
+                sacc[4 * g + jj] = -l4[jj];
+                dd[4 * g + jj] = d4[jj];
+                dpacc[4 * g + jj] = 0.f;
             }
-        // S = Q' K'^T and dP = dO V^T in (ks, qb) steps, operands through a 4-deep register ring
-        {
-            constexpr int NST = KS * kBwdQB;
-            auto qop = [&](int st) __attribute__((always_inline)) {
-                const int r = 32 * (st % kBwdQB) + l32;
-                return *reinterpret_cast<const bf16x8*>(qc + r * L::kPitch + (2 * (st / kBwdQB) + hf) * 16);
-            };
-            auto oop = [&](int st) __attribute__((always_inline)) {
-                const int r = 32 * (st % kBwdQB) + l32;
-                return *reinterpret_cast<const bf16x8*>(oc + r * L::kVPitch + (((2 * (st / kBwdQB) + hf) ^ vswz<D>(r)) * 16));
-            };
-            bf16x8 qa[kRing], oa[kRing];
-#pragma unroll
-            for (int st = 0; st < kRing - 1; ++st) {
-                qa[st] = qop(st);
-                oa[st] = oop(st);
-            }
-#pragma unroll
-            for (int st = 0; st < NST; ++st) {
-                if (st + kRing - 1 < NST) {
-                    qa[(st + kRing - 1) % kRing] = qop(st + kRing - 1);
-                    oa[(st + kRing - 1) % kRing] = oop(st + kRing - 1);
-                }
-                sacc[st % kBwdQB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[st % kRing], kreg[st / kBwdQB], sacc[st % kBwdQB], 0, 0, 0);
-                dpacc[st % kBwdQB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[st % kRing], vreg[st / kBwdQB], dpacc[st % kBwdQB], 0, 0, 0);
-            }
-            __builtin_amdgcn_sched_group_barrier(0x100, 2 * (kRing - 1), 0);
-#pragma unroll
-            for (int i = 0; i < NST - (kRing - 1); ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-            }
-            __builtin_amdgcn_sched_group_barrier(0x008, 2 * (kRing - 1), 0);
         }
-        // P and dZ as bf16 B operands (query 32 qb + 8 g + 4 hf + jj in k-step 2 qb + g / 2, slot
-        // 4 (g % 2) + jj)
-        bf16x8 pbb[2 * kBwdQB], dzb[2 * kBwdQB];
-#pragma unroll
-        for (int qb = 0; qb < kBwdQB; ++qb)
-#pragma unroll
-            for (int g = 0; g < 4; ++g)
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const int x = 4 * g + jj;
-                    const float p = __builtin_amdgcn_exp2f(sacc[qb][x]);
-                    pbb[2 * qb + (g >> 1)][(g & 1) * 4 + jj] = (__bf16)p;
-                    dzb[2 * qb + (g >> 1)][(g & 1) * 4 + jj] = (__bf16)(p * (dpacc[qb][x] - dd[qb][x]));
-                }
-        // dV^T += dO^T P and dK^T += Q'^T dZ, both A operands from transpose reads (ring as above)
+        // S = Q' K'^T and dP = dO V^T of the 32-query block, all four operands from LDS
         {
-            constexpr int NST = 2 * kBwdQB * DB;
+            const int r = qb0 + l32;
+            auto qop = [&](int ks) __attribute__((always_inline)) {
+                return *reinterpret_cast<const bf16x8*>(qtile + r * L::kPitch + (2 * ks + hf) * 16);
+            };
+            auto oop = [&](int ks) __attribute__((always_inline)) {
+                return *reinterpret_cast<const bf16x8*>(otile + r * L::kVPitch + (((2 * ks + hf) ^ vswz<D>(r)) * 16));
+            };
+            auto kop = [&](int ks) __attribute__((always_inline)) {
+                return *reinterpret_cast<const bf16x8*>(kres + kr * L::kPitch + (2 * ks + hf) * 16);
+            };
+            auto vop = [&](int ks) __attribute__((always_inline)) {
+                return *reinterpret_cast<const bf16x8*>(vres + kr * L::kVPitch + (((2 * ks + hf) ^ vswz<D>(kr)) * 16));
+            };
+            bf16x8 qa[kR], oa[kR], kb_[kR], vb_[kR];
+#pragma unroll
+            for (int ks = 0; ks < kR - 1; ++ks) {
+                qa[ks] = qop(ks); oa[ks] = oop(ks); kb_[ks] = kop(ks); vb_[ks] = vop(ks);
+            }
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                if (ks + kR - 1 < KS) {
+                    const int n1 = (ks + kR - 1) % kR;
+                    qa[n1] = qop(ks + kR - 1); oa[n1] = oop(ks + kR - 1);
+                    kb_[n1] = kop(ks + kR - 1); vb_[n1] = vop(ks + kR - 1);
+                }
+                sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ks % kR], kb_[ks % kR], sacc, 0, 0, 0);
+                dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[ks % kR], vb_[ks % kR], dpacc, 0, 0, 0);
+            }
+        }
+        // P and dZ as bf16 B operands (query qb0 + 8 g + 4 hf + jj in 16-query step g / 2, slot
+        // 4 (g % 2) + jj)
+        bf16x8 pbb[2], dzb[2];
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int x = 4 * g + jj;
+                const float p = __builtin_amdgcn_exp2f(sacc[x]);
+                pbb[g >> 1][(g & 1) * 4 + jj] = (__bf16)p;
+                dzb[g >> 1][(g & 1) * 4 + jj] = (__bf16)(p * (dpacc[x] - dd[x]));
+            }
+        // dV^T += dO^T P and dK^T += Q'^T dZ over the block's two 16-query steps
+        {
+            constexpr int NST = 2 * DB;
             auto dop = [&](int st) __attribute__((always_inline)) {
                 const int kk = st / DB, db = st % DB;
-                const int r0 = 16 * kk + tr.row, r8 = r0 + 8;
-                return tr_operand(oc + r0 * L::kVPitch + (((4 * db + tr.gran) ^ vswz<D>(r0)) * 16) + tr.byte,
-                                  oc + r8 * L::kVPitch + (((4 * db + tr.gran) ^ vswz<D>(r8)) * 16) + tr.byte);
+                const int r0 = qb0 + 16 * kk + tr.row, r8 = r0 + 8;
+                return tr_operand(otile + r0 * L::kVPitch + (((4 * db + tr.gran) ^ vswz<D>(r0)) * 16) + tr.byte,
+                                  otile + r8 * L::kVPitch + (((4 * db + tr.gran) ^ vswz<D>(r8)) * 16) + tr.byte);
             };
-            auto kop2 = [&](int st) __attribute__((always_inline)) {
+            auto qtop = [&](int st) __attribute__((always_inline)) {
                 const int kk = st / DB, db = st % DB;
-                const char* qb = qc + (16 * kk + tr.row) * L::kPitch + (4 * db + tr.gran) * 16 + tr.byte;
+                const char* qb = qtile + (qb0 + 16 * kk + tr.row) * L::kPitch + (4 * db + tr.gran) * 16 + tr.byte;
                 return tr_operand(qb, qb + 8 * L::kPitch);
             };
-            bf16x8 da[kRing], ka2[kRing];
+            bf16x8 da[kR], ka2[kR];
 #pragma unroll
-            for (int st = 0; st < kRing - 1; ++st) {
+            for (int st = 0; st < kR - 1; ++st) {
                 da[st] = dop(st);
-                ka2[st] = kop2(st);
+                ka2[st] = qtop(st);
             }
 #pragma unroll
             for (int st = 0; st < NST; ++st) {
-                if (st + kRing - 1 < NST) {
-                    da[(st + kRing - 1) % kRing] = dop(st + kRing - 1);
-                    ka2[(st + kRing - 1) % kRing] = kop2(st + kRing - 1);
+                if (st + kR - 1 < NST) {
+                    da[(st + kR - 1) % kR] = dop(st + kR - 1);
+                    ka2[(st + kR - 1) % kR] = qtop(st + kR - 1);
                 }
-                dvacc[st % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[st % kRing], pbb[st / DB], dvacc[st % DB], 0, 0, 0);
-                dkacc[st % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka2[st % kRing], dzb[st / DB], dkacc[st % DB], 0, 0, 0);
+                dvacc[st % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[st % kR], pbb[st / DB], dvacc[st % DB], 0, 0, 0);
+                dkacc[st % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka2[st % kR], dzb[st / DB], dkacc[st % DB], 0, 0, 0);
             }
-            __builtin_amdgcn_sched_group_barrier(0x100, 4 * (kRing - 1), 0);
-#pragma unroll
-            for (int i = 0; i < NST - (kRing - 1); ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-            }
-            __builtin_amdgcn_sched_group_barrier(0x008, 2 * (kRing - 1), 0);
         }
-        if (i + 1 < nq) store_q((i + 1) & 1);
-        wait_vm_loads();
-        __syncthreads();
     }
 
-    // ---- epilogue: dv rows, and dk = (transposed RoPE of dK') / log2(e), to the key's token ----
-    if (pk >= a.L) return;
+    // ---- the two query halves' partial sums meet in LDS (the tiles are free now) ----
+    float* red = reinterpret_cast<float*>(lds);   // [kgrp][16 * DB values][64 lanes]
+    auto exchange = [&](f32x16 (&acc)[DB]) __attribute__((always_inline)) {
+        __syncthreads();
+        if (qhalf == 1) {
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int x = 0; x < 16; ++x) red[(kgrp * 16 * DB + db * 16 + x) * 64 + lane] = acc[db][x];
+        }
+        __syncthreads();
+        if (qhalf == 0) {
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int x = 0; x < 16; ++x) acc[db][x] += red[(kgrp * 16 * DB + db * 16 + x) * 64 + lane];
+        }
+    };
+    exchange(dvacc);
+    exchange(dkacc);
+
+    // ---- epilogue (query half 0): dv rows, and dk = (transposed RoPE of dK') / log2(e) ----
+    if (qhalf != 0 || pk >= a.L) return;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -769,7 +772,7 @@ static hipError_t launch_bwd_k(const AttnBwdParams& a, hipStream_t stream) {
     hipLaunchKernelGGL((attn_bwd_dq_kernel<D, E, KDQ>), dim3(a.dq_num_work), dim3(kDqThreads), lds_dq, stream, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, E, KKV>), dim3(a.num_work), dim3(kBwdThreads), lds_kv, stream, a);
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, E, KKV>), dim3(a.num_work), dim3(kKvThreads), lds_kv, stream, a);
     return hipGetLastError();
 }
 
