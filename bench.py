@@ -45,6 +45,8 @@ def parse_args():
     ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass timing")
     ap.add_argument("--no-8bit", action="store_true", help="skip the 8-bit attention timing")
     ap.add_argument("--no-schedule", action="store_true", help="skip the per-layer schedule timing")
+    ap.add_argument("--no-rotated", action="store_true",
+                    help="skip the timing of the pre-rotated path (skiparse_rope_qk + skiparse_attn_rotated)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -220,6 +222,54 @@ def eight_bit(sk, wl, q, k, v, stream, reps=20):
     return {"kernel": "attn8_fwd_kernel (int8 QK, E4M3 PV)", "bound": "mfma", "achieved": round(tf, 1),
             "peak": PEAK_8BIT_TOPS, "unit": "TFLOP/s", "frac": round(tf / PEAK_8BIT_TOPS, 4),
             "flop_per_call": flops, "per_mode": res}
+
+
+def rotated(sk, wl, q, k, v, stream, reps=20):
+    """The pre-rotated path on the 24x22x40 workload: skiparse_rope_qk (one HBM pass over q and
+    k) and skiparse_attn_rotated per mode, each the median of `reps` calls, with the fused
+    skiparse_attn timed in the same loop (calls interleaved) for comparison.  `per_call` prices
+    one attention as a model layer runs it (a rotation, then the attention); `shared` prices the
+    step of this benchmark with one rotation serving both modes' attention."""
+    import torch
+    ws = wl.OSP_SINGLE
+    flops = sk.attn_flops(ws.B, ws.grid, ws.heads, ws.head_dim, ws.sparse_k)
+    qr, kr = sk.rope_qk(q, k, ws.grid, stream=stream)
+    out = torch.empty_like(q)
+    calls = {"rope": lambda: sk.rope_qk(q, k, ws.grid, outs=(qr, kr), stream=stream)}
+    for w in (wl.OSP_SINGLE, wl.OSP_GROUP):
+        m = "single" if w.mode == 0 else "group"
+        calls["rot_" + m] = (lambda w=w: sk.attn_rotated(qr, kr, v, w.grid, w.sparse_k, w.mode, out=out, stream=stream))
+        calls["fused_" + m] = (lambda w=w: sk.attn(q, k, v, w.grid, w.sparse_k, w.mode, out=out, stream=stream))
+    for fn in calls.values():
+        for _ in range(3):
+            fn()
+    times = {name: [] for name in calls}
+    for _ in range(reps):
+        for name, fn in calls.items():
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            times[name].append((e0, e1))
+    torch.cuda.synchronize()
+    ms = {name: sorted(a.elapsed_time(b) for a, b in ev)[reps // 2] for name, ev in times.items()}
+    rope_bytes = 4 * q.numel() * q.element_size()          # read q, k; write qr, kr
+    res = {"rope_qk": {"kernel": "rope_qk_kernel", "bound": "hbm", "ms": round(ms["rope"], 4),
+                       "bytes": rope_bytes,
+                       "gbs": round(rope_bytes / (ms["rope"] * 1e-3) / 1e9, 1)}}
+    for m in ("single", "group"):
+        r, f = ms["rot_" + m], ms["fused_" + m]
+        res[m] = {"attn_rotated_ms": round(r, 4), "attn_rotated_tflops": round(flops / (r * 1e-3) / 1e12, 1),
+                  "fused_ms": round(f, 4), "fused_tflops": round(flops / (f * 1e-3) / 1e12, 1)}
+    rot_ms = ms["rot_single"] + ms["rot_group"]
+    fused_ms = ms["fused_single"] + ms["fused_group"]
+    res["per_call_tflops"] = round(2 * flops / ((rot_ms + 2 * ms["rope"]) * 1e-3) / 1e12, 1)
+    res["shared_tflops"] = round(2 * flops / ((rot_ms + ms["rope"]) * 1e-3) / 1e12, 1)
+    res["fused_tflops"] = round(2 * flops / (fused_ms * 1e-3) / 1e12, 1)
+    res["attn_rotated"] = {"kernel": "attn_rot_kernel", "bound": "mfma",
+                           "achieved": round(2 * flops / (rot_ms * 1e-3) / 1e12, 1), "peak": PEAK_BF16_TFLOPS,
+                           "unit": "TFLOP/s", "frac": round(2 * flops / (rot_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    return res
 
 
 def schedule(sk, wl, q, k, v, stream, reps=5):
@@ -405,6 +455,9 @@ def main():
 
     if not args.no_schedule:
         result["schedule"] = schedule(sk, wl, qg, kg, vg, stream)
+
+    if not args.no_rotated:
+        result["rotated"] = rotated(sk, wl, qg, kg, vg, stream)
 
     if not args.no_sweep:
         result["sweep"] = sweep(sk, wl, stream)

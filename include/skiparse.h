@@ -112,6 +112,43 @@ int skiparse_attn_lse(const void* q, const void* k, const void* v,
                       void* stream);
 
 /*
+ * skiparse_rope_qk -- the 3D RoPE of q and k, once, for any number of Skiparse
+ * attentions over them (Open-Sora Plan documentation, "Skiparse Attention":
+ * q and k are rotated at their original token positions before the scopes are
+ * formed, so the rotation is the same for every k and mode).
+ *
+ * q, k   : (B, N, heads, 128) bf16 inputs, N = T*H*W (device memory).
+ * qr, kr : (B, N, heads, 128) bf16 outputs, caller-owned, in token order:
+ *          qr = bf16(RoPE(q) * log2(e)/sqrt(128)) -- the softmax scale in base-2
+ *          units folded in -- and kr = bf16(RoPE(k)), each element computed as
+ *          skiparse_attn computes its operands (same cos/sin table, same float32
+ *          operations), so they are bit for bit the operands skiparse_attn feeds
+ *          its matrix cores.  No output may overlap an input or the other output.
+ * head_dim must be 128 and dtype SKIPARSE_BF16 (else SKIPARSE_E_UNSUPPORTED);
+ * other limits as skiparse_attn.  One kernel launch; outputs untouched on error.
+ */
+int skiparse_rope_qk(const void* q, const void* k, int B, int T, int H, int W,
+                     int heads, int head_dim, int dtype, void* qr, void* kr,
+                     void* stream);
+
+/*
+ * skiparse_attn_rotated -- skiparse_attn on operands from skiparse_rope_qk:
+ * the gather, attention and scatter of skiparse_attn (steps 2-4 above) with
+ * RoPE and the softmax scale already applied.
+ *
+ * qr, kr : outputs of skiparse_rope_qk for the same B, grid, heads.
+ * v, out : as skiparse_attn.  out must not overlap qr, kr or v.
+ * head_dim 128, dtype SKIPARSE_BF16 and sparse_k dividing 64 (else
+ * SKIPARSE_E_UNSUPPORTED); other limits as skiparse_attn.
+ * skiparse_rope_qk followed by skiparse_attn_rotated gives out equal to
+ * skiparse_attn's bit for bit.  One kernel launch; out untouched on error.
+ */
+int skiparse_attn_rotated(const void* qr, const void* kr, const void* v,
+                          int B, int T, int H, int W, int heads, int head_dim,
+                          int sparse_k, int mode, int dtype, void* out,
+                          void* stream);
+
+/*
  * skiparse_attn_bwd -- gradients of a loss through skiparse_attn (the chain
  * rule of steps 1-4, taken backwards).  Open-Sora Plan's page says Skiparse
  * exists to speed up training; these are the gradients training needs.

@@ -29,11 +29,13 @@ from ._lib import (  # noqa: F401
     attn_bwd_flops,
     attn_flops,
     attn_lse,
+    attn_rotated,
     lib,
     q8_scope_pitch,
     quant8,
     rearrange,
     reverse,
+    rope_qk,
     rope_remap,
     scope_table,
     status_string,

@@ -82,6 +82,10 @@ def lib():
         L.skiparse_attn8.restype = i
         L.skiparse_attn_schedule.argtypes = [ctypes.POINTER(Layer), i] + dims + [i, vp]
         L.skiparse_attn_schedule.restype = i
+        L.skiparse_rope_qk.argtypes = [vp, vp] + dims + [i, vp, vp, vp]
+        L.skiparse_rope_qk.restype = i
+        L.skiparse_attn_rotated.argtypes = [vp, vp, vp] + dims + [i, i, i, vp, vp]
+        L.skiparse_attn_rotated.restype = i
         L.skiparse_status_string.argtypes = [i]
         L.skiparse_status_string.restype = ctypes.c_char_p
         L.skiparse_version.argtypes = []
@@ -142,6 +146,37 @@ def attn(q, k, v, grid, sparse_k, mode, out=None, stream=None):
     _check(lib().skiparse_attn(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, T, H, W, heads, d,
                                int(sparse_k), int(mode), _dtype_code(q), out.data_ptr(),
                                _stream_ptr(stream)), "skiparse_attn")
+    return out
+
+
+def rope_qk(q, k, grid, outs=None, stream=None):
+    """3D RoPE of q and k once (bf16, head_dim 128): returns (qr, kr), qr with the softmax
+    scale log2(e)/sqrt(d) folded in -- the operands of attn_rotated."""
+    import torch
+    B, T, H, W, heads, d = _dims(q, grid)
+    if k.shape != q.shape or k.dtype != q.dtype or not k.is_contiguous():
+        raise ValueError("q, k must share shape, dtype and be contiguous")
+    qr, kr = outs if outs is not None else (torch.empty_like(q), torch.empty_like(k))
+    for t in (qr, kr):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
+            raise ValueError("qr, kr must match q's shape and dtype and be contiguous")
+    _check(lib().skiparse_rope_qk(q.data_ptr(), k.data_ptr(), B, T, H, W, heads, d, _dtype_code(q),
+                                  qr.data_ptr(), kr.data_ptr(), _stream_ptr(stream)), "skiparse_rope_qk")
+    return qr, kr
+
+
+def attn_rotated(qr, kr, v, grid, sparse_k, mode, out=None, stream=None):
+    """Skiparse attention on rope_qk's outputs; equals attn(q, k, v, ...) bit for bit."""
+    import torch
+    B, T, H, W, heads, d = _dims(qr, grid)
+    for t in (kr, v):
+        if t.shape != qr.shape or t.dtype != qr.dtype or not t.is_contiguous():
+            raise ValueError("qr, kr, v must share shape, dtype and be contiguous")
+    if out is None:
+        out = torch.empty_like(v)
+    _check(lib().skiparse_attn_rotated(qr.data_ptr(), kr.data_ptr(), v.data_ptr(), B, T, H, W, heads, d,
+                                       int(sparse_k), int(mode), _dtype_code(qr), out.data_ptr(),
+                                       _stream_ptr(stream)), "skiparse_attn_rotated")
     return out
 
 

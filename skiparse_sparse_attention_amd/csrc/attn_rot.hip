@@ -1,0 +1,411 @@
+// Skiparse attention on pre-rotated q and k, and the pass that rotates them (gfx950).
+//
+// The fused kernel (attn_fwd.hip) rotates every K tile while staging it into LDS, and each
+// of a scope's query-tile workgroups repeats that work for the same keys.  RoPE does not
+// depend on the scope pattern, so here it runs once, in an HBM-bound pass, and its output
+// serves every Skiparse attention over the same q and k (Single Skip and Group Skip alike):
+//   rope_qk_kernel:  qr = bf16(RoPE(q) * log2(e)/sqrt(d)), kr = bf16(RoPE(k)) in token order,
+//     with the same float64-evaluated cos/sin table and the same float32 arithmetic as the
+//     fused kernel's staging, so qr and kr hold exactly the operands the fused kernel feeds
+//     its matrix cores;
+//   attn_rot_kernel: the fused kernel's workgroup shape, two-group MFMA/VALU schedule, online
+//     softmax and PV product, with Q'^T read from qr straight into registers and the K tiles,
+//     like the V tiles, copied from kr straight into LDS by buffer loads that write LDS.
+//     The QK k-steps take head_dim in the fused kernel's order (k-step c contracts RoPE chunk
+//     pair c: first-half chunk in lanes 0-31, its partner in lanes 32-63), so every product
+//     and sum is the fused kernel's and the output is the same bit for bit.
+// Open-Sora Plan documentation, "Skiparse Attention": RoPE on q and k at the original token
+// positions, then attention within each scope.  head_dim 128, bf16, sparse_k dividing 64.
+#include "attn_common.hpp"
+#include "skiparse_device.hpp"
+#include "skiparse_launch.hpp"
+
+namespace skiparse {
+
+using namespace attn;
+
+namespace {
+
+constexpr int kRD = 128;                  // head_dim
+constexpr int kRCH = kRD / 16;            // elements per RoPE chunk (one 16-byte granule)
+constexpr int kRWaves = 8;                // wavefronts per workgroup (2 per SIMD)
+constexpr int kRThreads = 64 * kRWaves;
+constexpr int kRBM = 32 * kRWaves;        // query rows per workgroup
+constexpr int kRBN = 64;                  // keys per tile
+constexpr int kRRow = kRD * 2;            // bytes per K / V row in LDS (bf16, unpadded)
+constexpr int kRTile = kRBN * kRRow;      // bytes per K or V tile
+constexpr int kRBufs = 3;                 // K tiles and V tiles in LDS
+constexpr int kRKOff = 0;
+constexpr int kRVOff = kRBufs * kRTile;
+constexpr int kRLds = 2 * kRBufs * kRTile;
+constexpr float kRRescaleLog2 = 8.0f;
+
+constexpr int kRopeThreads = 256;
+constexpr int kRopeGrid = 2048;           // rotation workgroups; each builds the table once
+
+// K tile row r: logical granule g of the row is stored at granule g ^ krswz(r).  The QK operand
+// reads fetch one granule of 16 consecutive rows per 16 lanes, which then fall on 16 distinct
+// granule positions, i.e. all 64 banks; the loads into LDS write whole 1 KiB pieces.
+__device__ __forceinline__ int krswz(int r) { return r & 15; }
+
+// Chunk of head_dim that lane half hf contributes to QK k-step ks (RoPE chunk pair ks)
+__device__ __forceinline__ int qk_chunk(int ks, int hf) {
+    const RopePair rp = rope_pair(ks);
+    return hf ? rp.c2 : rp.c1;
+}
+
+}  // namespace
+
+// ---- the rotation pass: one (token, head) row per 8 lanes, one RoPE chunk pair per lane ----
+__global__ void __launch_bounds__(kRopeThreads) rope_qk_kernel(RopeQkParams a) {
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    build_banked_rope_table<kRD>(lds, a.T, a.H, a.W, 0);
+    __syncthreads();
+    const int cp = threadIdx.x & 7;
+    const RopePair rp = rope_pair(cp);
+    const int HW = a.H * a.W;
+    const int tasks = a.B * a.N * a.heads;                  // (token row, head) rows
+    const int step = gridDim.x * (kRopeThreads / 8);
+    for (int t = blockIdx.x * (kRopeThreads / 8) + (threadIdx.x >> 3); t < tasks; t += step) {
+        const int n = (t / a.heads) % a.N;
+        const int pos = rp.axis == 0 ? n / HW : (rp.axis == 1 ? (n / a.W) % a.H : n % a.W);
+        const char* trow = lds + rope_tab_offset<kRD>(a.T, a.H, rp.axis, pos, rp.jchunk * kRCH, 0);
+        f32x4 cs[kRCH / 2];
+#pragma unroll
+        for (int j = 0; j < kRCH / 2; ++j) cs[j] = *reinterpret_cast<const f32x4*>(trow + 16 * j);
+        const int64_t row = (int64_t)t * kRRow;             // byte offset of the (token, head) row
+#pragma unroll
+        for (int which = 0; which < 2; ++which) {
+            const char* in = reinterpret_cast<const char*>(which == 0 ? a.q : a.k) + row;
+            char* out = reinterpret_cast<char*>(which == 0 ? a.qr : a.kr) + row;
+            ChunkRaw<BF16, kRCH> r1, r2;
+            const u32x4 w1 = *reinterpret_cast<const u32x4*>(in + rp.c1 * 16);
+            const u32x4 w2 = *reinterpret_cast<const u32x4*>(in + rp.c2 * 16);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                r1.w[i] = w1[i];
+                r2.w[i] = w2[i];
+            }
+            float x1[kRCH], x2[kRCH];
+            raw_to_f32(r1, x1);
+            raw_to_f32(r2, x2);
+            rope_rotate_cs<kRCH>(x1, x2, cs);
+            if (which == 0) {
+#pragma unroll
+                for (int e = 0; e < kRCH; ++e) {
+                    x1[e] *= a.scale_log2;
+                    x2[e] *= a.scale_log2;
+                }
+            }
+            store_rotated_chunks<kRCH>(out + rp.c1 * 16, out + rp.c2 * 16, x1, x2);
+        }
+    }
+}
+
+// ---- attention on qr, kr, v ----
+__global__ void __launch_bounds__(kRThreads) __attribute__((amdgpu_waves_per_eu(kRThreads / 256, kRThreads / 256)))
+attn_rot_kernel(AttnParams a) {
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    constexpr int KS = kRD / 16;   // 16-deep k-steps of Q K^T
+    constexpr int DB = kRD / 32;   // 32-row blocks of O^T
+    constexpr int KB = kRBN / 32;  // 32-key blocks of S^T
+    constexpr int KK = kRBN / 16;  // 16-deep k-steps of P V
+    constexpr int G = kRD / 8;     // 16-byte granules per row
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, hf = lane >> 5;
+
+    const int work = xcd_remap(blockIdx.x, gridDim.x);
+    const int qt = work % a.q_tiles;
+    const int sc = work / a.q_tiles;
+    const int s = sc % a.sparse_k;
+    const int bh = sc / a.sparse_k;
+    const int head = bh % a.heads;
+    const int b = bh / a.heads;
+    const int64_t k_ = a.sparse_k;
+    const int row_bytes = a.heads * kRRow;                 // bytes per token
+    // buffer descriptors over this (batch, head) slice; tokens >= N lie past its end
+    const int64_t slice = ((int64_t)b * a.N * a.heads + head) * kRRow;
+    const int slice_bytes = a.N * row_bytes - head * kRRow;
+    const __amdgpu_buffer_rsrc_t qbuf = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(reinterpret_cast<const char*>(a.q) + slice), (short)0, slice_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t kbuf = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(reinterpret_cast<const char*>(a.k) + slice), (short)0, slice_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vbuf = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(reinterpret_cast<const char*>(a.v) + slice), (short)0, slice_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t obuf = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(reinterpret_cast<char*>(a.out) + slice), (short)0, slice_bytes, 0x00020000);
+
+    // ---- Q'^T of the wave's 32 query rows, straight from qr into registers ----
+    bf16x8 qreg[KS];
+    {
+        const int p = qt * kRBM + wave * 32 + l32;
+        const int off = (int)scope_token(p, s, k_, a.mode) * row_bytes;   // past the slice: zeros
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            qreg[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qbuf, off + qk_chunk(ks, hf) * 16, 0, 0));
+    }
+
+    // ---- tile loads into LDS: each wave moves two 1 KiB pieces (4 rows each) of every K tile
+    // and two of every V tile; in a piece, lane l fills LDS granule l of the piece with the
+    // granule of row l / G that the row's swizzle puts there ----
+    constexpr int kOps = kRBN * G / 64 / kRWaves;   // pieces per wave per tile
+    static_assert(kOps == 2, "two pieces per wave and tile");
+    const int tile_dn = kRBN * a.sparse_k;          // token advance per tile (sparse_k | 64)
+    int koff[kOps], voff[kOps];
+#pragma unroll
+    for (int i = 0; i < kOps; ++i) {
+        const int r = (wave * kOps + i) * (64 / G) + lane / G;
+        const int tok = (int)scope_token(r, s, k_, a.mode);
+        koff[i] = tok * row_bytes + ((lane % G) ^ krswz(r)) * 16;
+        voff[i] = tok * row_bytes + ((lane % G) ^ vswz<kRD>(r)) * 16;
+    }
+    // each call moves the next tile (the cursors advance one tile per call)
+    auto load_k = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < kOps; ++i) {
+            buffer_load_to_lds16(kbuf, lds + kRKOff + buf * kRTile + (wave * kOps + i) * 1024, koff[i]);
+            koff[i] += tile_dn * row_bytes;
+        }
+    };
+    auto load_v = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < kOps; ++i) {
+            buffer_load_to_lds16(vbuf, lds + kRVOff + buf * kRTile + (wave * kOps + i) * 1024, voff[i]);
+            voff[i] += tile_dn * row_bytes;
+        }
+    };
+
+    // QK operand reads: row 32 kb + l32, logical granule qk_chunk(ks, hf)
+    int k_rd[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) k_rd[ks] = l32 * kRRow + ((qk_chunk(ks, hf) ^ krswz(l32)) << 4);
+    // PV operand reads with ds_read_b64_tr_b16, as in the fused kernel: within each group of
+    // 16 lanes, lane 4t + j points at 4 consecutive d of key row t and receives element j of
+    // each of those 4 keys; lanes 0-31 read keys {0-3, 8-11} and lanes 32-63 keys {4-7, 12-15}
+    // of every 16-key step (the order of P^T in the accumulator layout).
+    const int tr_i = lane & 15;
+    const int tr_row = (tr_i >> 2) + 4 * (lane >> 5);
+    const int tr_gran = 2 * ((lane >> 4) & 1) + ((tr_i & 3) >> 1);
+    const int tr_byte = (tr_i & 1) * 8;
+    auto v_rd = [&](int h, int db) __attribute__((always_inline)) {
+        const int r = 8 * h + tr_row;
+        return r * kRRow + (((4 * db + tr_gran) ^ vswz<kRD>(r)) * 16) + tr_byte;
+    };
+
+    // ---- accumulators and softmax state: scores arrive as S' = s*log2(e)/sqrt(d) - m_ref ----
+    f32x16 o[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int x = 0; x < 16; ++x) o[db][x] = 0.f;
+    float m_ref = 0.f, l_part = 0.f;
+    f32x16 s_init;
+#pragma unroll
+    for (int x = 0; x < 16; ++x) s_init[x] = 0.f;
+    const int nt = (a.L + kRBN - 1) / kRBN;
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    f32x16 sacc[KB];
+    bf16x8 pb[KK];
+
+    // S'^T = K Q'^T onto -m_ref, 16 MFMAs in (ks, kb) order, K operands through a 4-deep ring
+    constexpr int kRing = 4;
+    auto qk = [&](int buf) __attribute__((always_inline)) {
+        const char* kcur = lds + kRKOff + buf * kRTile;
+        constexpr int NST = KS * KB;
+        auto kop = [&](int st) __attribute__((always_inline)) {
+            return *reinterpret_cast<const bf16x8*>(kcur + k_rd[st / KB] + (st % KB) * 32 * kRRow);
+        };
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) sacc[kb] = s_init;
+        bf16x8 ka[kRing];
+#pragma unroll
+        for (int st = 0; st < kRing - 1; ++st) ka[st] = kop(st);
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int st = 0; st < NST; ++st) {
+            if (st + kRing - 1 < NST) ka[(st + kRing - 1) % kRing] = kop(st + kRing - 1);
+            sacc[st % KB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[st % kRing], qreg[st / KB], sacc[st % KB], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, kRing - 1, 0);
+#pragma unroll
+        for (int i = 0; i < NST - (kRing - 1); ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, kRing - 1, 0);
+        __builtin_amdgcn_s_setprio(0);
+    };
+
+    // online softmax of tile j (the fused kernel's: lazy reference moves beyond 2^8)
+    auto softmax = [&](int j) __attribute__((always_inline)) {
+        if (j == nt - 1 && (a.L % kRBN) != 0) {
+            const int valid = a.L - j * kRBN;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj)
+                        if (kb * 32 + 8 * g + 4 * hf + jj >= valid) sacc[kb][4 * g + jj] = -__builtin_inff();
+        }
+        float mt = sacc[0][0];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int x = 0; x < 16; ++x) mt = fmaxf(mt, sacc[kb][x]);
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
+        mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        if (j == 0 || __ballot(mt > kRRescaleLog2) != 0ull) {
+            const float delta = j == 0 ? mt : fmaxf(mt, 0.f);
+            const float alpha = __builtin_amdgcn_exp2f(-delta);
+            m_ref += delta;
+            l_part *= alpha;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int x = 0; x < 16; ++x) o[db][x] *= alpha;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int x = 0; x < 16; ++x) sacc[kb][x] -= delta;
+#pragma unroll
+            for (int x = 0; x < 16; ++x) s_init[x] = -m_ref;
+        }
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                // keys 32kb + 8g + 4hf + jj sit in k-step 2kb + g/2, slots (g%2)*4 + jj
+                const int kk = 2 * kb + (g >> 1), sl = (g & 1) * 4;
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) pb[kk][sl + jj] = (__bf16)__builtin_amdgcn_exp2f(sacc[kb][4 * g + jj]);
+            }
+        float lsum[2] = {l_part, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const bf16x2 pair = {pb[kk][2 * x], pb[kk][2 * x + 1]};
+                lsum[x & 1] = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, lsum[x & 1], false);
+            }
+        l_part = lsum[0] + lsum[1];
+    };
+
+    // O^T += V^T P^T, V^T operands by transpose reads through a 4-deep ring
+    auto pv = [&](int buf) __attribute__((always_inline)) {
+        const char* vcur = lds + kRVOff + buf * kRTile;
+        constexpr int NST = KK * DB;
+        auto vop = [&](int st) __attribute__((always_inline)) {
+            const int kk = st / DB, db = st % DB;
+            const i16x4 lo = ds_read_tr16(vcur + (16 * kk) * kRRow + v_rd(0, db));
+            const i16x4 hi = ds_read_tr16(vcur + (16 * kk) * kRRow + v_rd(1, db));
+            const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            return __builtin_bit_cast(bf16x8, v);
+        };
+        bf16x8 va[kRing];
+#pragma unroll
+        for (int st = 0; st < kRing - 1; ++st) va[st] = vop(st);
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int st = 0; st < NST; ++st) {
+            if (st + kRing - 1 < NST) va[(st + kRing - 1) % kRing] = vop(st + kRing - 1);
+            o[st % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[st % kRing], pb[st / DB], o[st % DB], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * (kRing - 1), 0);
+#pragma unroll
+        for (int i = 0; i < NST - (kRing - 1); ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, kRing - 1, 0);
+        __builtin_amdgcn_s_setprio(0);
+    };
+
+    // ---- schedule ----
+    // Waves 0-3 (group 0) and 4-7 (group 1) alternate between an MFMA block and a VALU block,
+    // one phase apart, a workgroup barrier closing every phase.  Phases ph = 1, 2, ...; group
+    // g runs MFMA block m = (ph - 1 - g) / 2 when ph + g is odd (PV(m-1) if m >= 1, QK(m) if
+    // m < nt) and VALU block m = (ph - 2 + g) / 2 when ph + g is even: its pieces of V tile m+1
+    // and K tile m+2 requested into LDS, softmax(m) (g = 0) or softmax(m-1) (g = 1), then a
+    // wait for the requests of the wave's previous VALU block.
+    // K tile m sits in K buffer m % 3 and V tile m in V buffer m % 3.  K tile m+2 is requested
+    // in phases 2m+1 / 2m+2, after QK(m-1), the last reader of its buffer, ended (phases 2m-1
+    // and 2m), and has landed after phase 2m+4, before QK(m+2) in phase 2m+5.  V tile m+1 is
+    // requested in the same phases, after PV(m-2) ended (phases 2m-1, 2m), and has landed
+    // before PV(m+1) in phase 2m+5.
+    const int grp = wave >= kRWaves / 2 ? 1 : 0;
+    load_k(0);
+    if (nt > 1) load_k(1);
+    load_v(0);
+    wait_vm_loads();
+    __syncthreads();
+    auto opaque = [](int x) __attribute__((always_inline)) { return __builtin_amdgcn_readfirstlane(x); };
+    auto mfma_block = [&](int m) __attribute__((always_inline)) {
+        if (m >= 1) pv(opaque((m - 1) % 3));
+        if (m < nt) qk(opaque(m % 3));
+    };
+    auto valu_block = [&](int m, int sm) __attribute__((always_inline)) {
+        const bool lv = m + 1 < nt, lk = m + 2 < nt;
+        if (lv) load_v(opaque((m + 1) % 3));
+        if (lk) load_k(opaque((m + 2) % 3));
+        if (sm >= 0 && sm < nt) softmax(sm);
+        if (lk) wait_vm_loads_but<2 * kOps>();   // this block's requests may stay in flight
+        else if (lv) wait_vm_loads_but<kOps>();
+        else wait_vm_loads();
+    };
+    if (grp == 0) {
+        for (int m = 0; m <= nt; ++m) {
+            mfma_block(m);
+            __syncthreads();
+            valu_block(m, m);
+            __syncthreads();
+        }
+    } else {
+        for (int m = 0; m <= nt; ++m) {
+            valu_block(m, m - 1);
+            __syncthreads();
+            mfma_block(m);
+            __syncthreads();
+        }
+    }
+
+    // ---- epilogue: normalise and scatter rows back to their tokens ----
+    {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_part), __float_as_uint(l_part), false, false);
+        const float inv = 1.0f / (__uint_as_float(sw[0]) + __uint_as_float(sw[1]));
+        const int p = qt * kRBM + wave * 32 + l32;
+        const int off = (int)scope_token(p, s, k_, a.mode) * row_bytes;   // past the slice when p >= L
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int d0 = db * 32 + 8 * g + 4 * hf;
+                const float y0 = o[db][4 * g] * inv, y1 = o[db][4 * g + 1] * inv;
+                const float y2 = o[db][4 * g + 2] * inv, y3 = o[db][4 * g + 3] * inv;
+                const u32x2 v2 = {pack_bf16x2(y0, y1), pack_bf16x2(y2, y3)};
+                __builtin_amdgcn_raw_buffer_store_b64(v2, obuf, off + d0 * 2, 0, 0);
+            }
+    }
+}
+
+hipError_t launch_rope_qk(const RopeQkParams& a, hipStream_t stream) {
+    const size_t lds = (size_t)(a.T + a.H + a.W) * 256;
+    const int64_t tasks = (int64_t)a.B * a.N * a.heads;
+    const int64_t blocks = (tasks + kRopeThreads / 8 - 1) / (kRopeThreads / 8);
+    const int grid = (int)(blocks < kRopeGrid ? blocks : kRopeGrid);
+    hipLaunchKernelGGL(rope_qk_kernel, dim3(grid), dim3(kRopeThreads), lds, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_attn_rot(const AttnParams& a, hipStream_t stream) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_rot_kernel),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, kRLds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(attn_rot_kernel, dim3(a.num_work), dim3(kRThreads), kRLds, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace skiparse

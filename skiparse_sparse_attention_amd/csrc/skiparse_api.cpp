@@ -134,6 +134,49 @@ int skiparse_attn(const void* q, const void* k, const void* v, int B, int T, int
     return attn_forward(q, k, v, B, T, H, W, heads, head_dim, sparse_k, mode, dtype, out, nullptr, stream);
 }
 
+int skiparse_rope_qk(const void* q, const void* k, int B, int T, int H, int W, int heads, int head_dim,
+                     int dtype, void* qr, void* kr, void* stream) {
+    if (!q || !k || !qr || !kr) return SKIPARSE_E_NULL;
+    Dims d;
+    const int st = check_dims(B, T, H, W, heads, head_dim, 1, SKIPARSE_SINGLE, dtype, &d);
+    if (st != SKIPARSE_OK) return st;
+    if (head_dim != 128 || dtype != SKIPARSE_BF16) return SKIPARSE_E_UNSUPPORTED;
+    if (overlaps(qr, q, d.bytes) || overlaps(qr, k, d.bytes) || overlaps(kr, q, d.bytes) ||
+        overlaps(kr, k, d.bytes) || overlaps(qr, kr, d.bytes))
+        return SKIPARSE_E_ALIAS;
+    skiparse::RopeQkParams a;
+    a.q = q; a.k = k; a.qr = qr; a.kr = kr;
+    a.B = B; a.T = T; a.H = H; a.W = W; a.heads = heads; a.N = (int)d.N;
+    a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)head_dim));
+    return to_status(skiparse::launch_rope_qk(a, static_cast<hipStream_t>(stream)));
+}
+
+int skiparse_attn_rotated(const void* qr, const void* kr, const void* v, int B, int T, int H, int W,
+                          int heads, int head_dim, int sparse_k, int mode, int dtype, void* out,
+                          void* stream) {
+    const int st = skiparse_validate(qr, kr, v, B, T, H, W, heads, head_dim, sparse_k, mode, dtype, out);
+    if (st != SKIPARSE_OK) return st;
+    if (head_dim != 128 || dtype != SKIPARSE_BF16 || skiparse::attn_tile_keys() % sparse_k != 0)
+        return SKIPARSE_E_UNSUPPORTED;
+    Dims d;
+    check_dims(B, T, H, W, heads, head_dim, sparse_k, mode, dtype, &d);
+    skiparse::AttnParams a;
+    a.q = qr; a.k = kr; a.v = v; a.out = out;
+    a.B = B; a.T = T; a.H = H; a.W = W; a.heads = heads;
+    a.sparse_k = sparse_k; a.mode = mode;
+    a.N = (int)d.N; a.L = (int)d.L;
+    const int bm = skiparse::attn_block_rows();
+    a.q_tiles = (int)((d.L + bm - 1) / bm);
+    const int64_t work = (int64_t)B * heads * sparse_k * a.q_tiles;
+    if (work > kI32Max) return SKIPARSE_E_SHAPE;
+    a.num_work = (int)work;
+    a.k_divides_bn = 1;
+    a.scale_log2 = 0.f;   // already folded into qr
+    a.phi_mul = 0;
+    a.lse = nullptr;
+    return to_status(skiparse::launch_attn_rot(a, static_cast<hipStream_t>(stream)));
+}
+
 int skiparse_attn_schedule(const skiparse_layer* layers, int n_layers, int B, int T, int H, int W, int heads,
                            int head_dim, int dtype, void* stream) {
     if (!layers) return SKIPARSE_E_NULL;

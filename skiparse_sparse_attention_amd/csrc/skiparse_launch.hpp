@@ -90,6 +90,18 @@ struct Attn8Params {
     int out_bytes;       // 2 (bf16) or 4 (fp32)
 };
 
+// Pre-rotated operands (attn_rot.hip): qr = bf16(RoPE(q) * scale_log2), kr = bf16(RoPE(k)),
+// both (B, N, heads, 128) in token order; the attention on them takes AttnParams with q = qr,
+// k = kr (bf16 only, sparse_k dividing 64).
+struct RopeQkParams {
+    const void* q;
+    const void* k;
+    void* qr;
+    void* kr;
+    int B, T, H, W, heads, N;
+    float scale_log2;
+};
+
 hipError_t launch_rope_remap(const RemapParams& a, int head_dim, int dtype, hipStream_t stream, int grid);
 hipError_t launch_reverse(const ReverseParams& a, hipStream_t stream, int grid);
 hipError_t launch_attn(const AttnParams& a, int head_dim, int dtype, hipStream_t stream);
@@ -102,5 +114,7 @@ hipError_t launch_quant8(const Q8Params& a, int head_dim, int dtype, hipStream_t
 hipError_t launch_attn8(const Attn8Params& a, hipStream_t stream);
 int q8_scope_pitch(int L);  // Lp of the vt8 layout
 int attn8_block_rows();     // query rows per 8-bit attention workgroup
+hipError_t launch_rope_qk(const RopeQkParams& a, hipStream_t stream);
+hipError_t launch_attn_rot(const AttnParams& a, hipStream_t stream);
 
 }  // namespace skiparse

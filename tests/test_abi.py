@@ -31,7 +31,8 @@ def test_header_declares_the_boundary():
                  "skiparse_validate", "skiparse_scope_table", "skiparse_attn_flops",
                  "skiparse_status_string", "skiparse_version", "skiparse_attn_lse",
                  "skiparse_attn_bwd", "skiparse_attn_bwd_flops", "skiparse_quant8", "skiparse_attn8",
-                 "skiparse_q8_scope_pitch", "skiparse_attn_schedule"):
+                 "skiparse_q8_scope_pitch", "skiparse_attn_schedule", "skiparse_rope_qk",
+                 "skiparse_attn_rotated"):
         assert want in names
 
 
@@ -216,3 +217,23 @@ def test_u_schedule_shape():
     assert sk.u_schedule(8, 8) == [(1, 0), (2, 1), (4, 0), (8, 1), (8, 0), (4, 1), (2, 0), (1, 1)]
     ks = [k for k, _ in sk.u_schedule(9, 4)]
     assert ks == ks[::-1] and ks[0] == 1 and max(ks) == 4
+
+
+def test_rotated_path_rejects_before_any_device_call():
+    L = sk.lib()
+    # skiparse_rope_qk(q, k, B, T, H, W, heads, head_dim, dtype, qr, kr, stream)
+    g = (1, 4, 8, 8, 2, 128, 0)
+    assert L.skiparse_rope_qk(Q, K, *g, V, None, None) == sk.E_NULL
+    assert L.skiparse_rope_qk(Q, K, 1, 4, 8, 8, 2, 64, 0, V, OUT, None) == sk.E_UNSUPPORTED   # head_dim 128 only
+    assert L.skiparse_rope_qk(Q, K, 1, 4, 8, 8, 2, 128, 1, V, OUT, None) == sk.E_UNSUPPORTED  # bf16 only
+    assert L.skiparse_rope_qk(Q, K, *g, Q, OUT, None) == sk.E_ALIAS      # qr over q
+    assert L.skiparse_rope_qk(Q, K, *g, V, K, None) == sk.E_ALIAS        # kr over k
+    assert L.skiparse_rope_qk(Q, K, *g, V, V, None) == sk.E_ALIAS        # qr and kr in one buffer
+    assert L.skiparse_rope_qk(Q, K, 0, 4, 8, 8, 2, 128, 0, V, OUT, None) == sk.E_SHAPE
+    # skiparse_attn_rotated(qr, kr, v, B, T, H, W, heads, head_dim, sparse_k, mode, dtype, out, stream)
+    assert L.skiparse_attn_rotated(Q, K, V, 1, 4, 8, 8, 2, 128, 2, 0, 0, None, None) == sk.E_NULL
+    assert L.skiparse_attn_rotated(Q, K, V, 1, 4, 8, 8, 2, 64, 2, 0, 0, OUT, None) == sk.E_UNSUPPORTED
+    assert L.skiparse_attn_rotated(Q, K, V, 1, 4, 8, 8, 2, 128, 2, 0, 1, OUT, None) == sk.E_UNSUPPORTED
+    assert L.skiparse_attn_rotated(Q, K, V, 1, 3, 8, 8, 2, 128, 3, 0, 0, OUT, None) == sk.E_UNSUPPORTED  # 3 does not divide 64
+    assert L.skiparse_attn_rotated(Q, K, V, 1, 4, 8, 8, 2, 128, 3, 0, 0, OUT, None) == sk.E_DIVISIBILITY
+    assert L.skiparse_attn_rotated(Q, K, V, 1, 4, 8, 8, 2, 128, 2, 0, 0, K, None) == sk.E_ALIAS

@@ -1,0 +1,110 @@
+"""GPU tests of the pre-rotated path (skiparse_rope_qk + skiparse_attn_rotated through the C ABI).
+
+Bars:
+* rope_qk against the fp64 oracle's 3D RoPE: each element is the bf16 rounding of a float32
+  rotation (float32 table, three float32 operations, the scale), so it lies within one bf16
+  rounding (2^-8 relative) plus a few float32 ulps of the exact rotated value; elements whose
+  bf16 rounding differs from that of the exact value must stay rare (near-ties only);
+* attn_rotated(rope_qk(q, k), v) equals skiparse_attn(q, k, v) bit for bit: the same operands
+  in the same contraction order, the same softmax;
+* one case per mode against the fp64 oracle at the attention bars (max 2e-2, mean 2e-3).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import skiparse_sparse_attention_amd as sk
+from skiparse_sparse_attention_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+LOG2E = 1.4426950408889634
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a ROCm GPU")
+    sk.lib()
+    yield
+
+
+def _bf16_round(x64):
+    return torch.from_numpy(x64.astype(np.float32)).to(torch.bfloat16).float().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("B,T,H,W,heads", [(1, 4, 8, 16, 2), (2, 3, 10, 12, 3), (1, 24, 22, 40, 4)])
+def test_rope_qk_matches_the_oracle_rotation(B, T, H, W, heads):
+    w = wl.Workload("rot", B, T, H, W, heads, 128, 1, oracle.SINGLE, "bf16")
+    q, k, _ = wl.make_inputs(w, seed=1, device="cpu")
+    print(f"rope_qk B={B} grid={T}x{H}x{W} heads={heads}", flush=True)
+    qr, kr = sk.rope_qk(q.cuda(), k.cuda(), (T, H, W))
+    torch.cuda.synchronize()
+    scale = LOG2E / np.sqrt(128.0)
+    for got_t, x, sc, name in ((qr, q, scale, "qr"), (kr, k, 1.0, "kr")):
+        exact = oracle.rope_3d(x.float().numpy().astype(np.float64), T, H, W) * sc
+        got = got_t.float().cpu().numpy().astype(np.float64)
+        bound = 2.0 ** -8 * np.abs(exact) + 2.0 ** -20 * np.abs(x.float().numpy()).max() * sc
+        err = np.abs(got - exact)
+        flips = np.count_nonzero(got != _bf16_round(exact))
+        print(f"{name}: max err/bound {(err / bound).max():.3f}, rounding flips {flips} of {got.size}", flush=True)
+        assert (err <= bound).all(), name
+        assert flips <= 1e-3 * got.size, name
+
+
+CASES = [
+    # B, T, H, W, heads, k, mode
+    (1, 4, 8, 16, 2, 4, oracle.SINGLE),      # L = 128
+    (1, 4, 10, 12, 3, 1, oracle.SINGLE),     # dense, ragged L = 480
+    (2, 4, 10, 12, 2, 2, oracle.GROUP),      # B = 2, L = 240
+    (1, 6, 10, 12, 2, 4, oracle.SINGLE),     # L = 180
+    (1, 8, 12, 16, 2, 4, oracle.GROUP),      # L = 384
+    (1, 4, 10, 16, 2, 8, oracle.SINGLE),     # L = 80
+    (1, 4, 16, 16, 1, 8, oracle.GROUP),      # L = 128
+    (1, 2, 4, 8, 2, 2, oracle.GROUP),        # L = 32: one partial tile
+]
+
+
+@pytest.mark.parametrize("B,T,H,W,heads,k,mode", CASES)
+def test_rotated_attention_equals_fused(B, T, H, W, heads, k, mode):
+    w = wl.Workload("rot", B, T, H, W, heads, 128, k, mode, "bf16")
+    q, kk, v = (x.cuda() for x in wl.make_inputs(w, seed=2, device="cpu"))
+    print(f"case B={B} grid={T}x{H}x{W} heads={heads} k={k} mode={mode}", flush=True)
+    qr, kr = sk.rope_qk(q, kk, (T, H, W))
+    got = sk.attn_rotated(qr, kr, v, (T, H, W), k, mode)
+    ref = sk.attn(q, kk, v, (T, H, W), k, mode)
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref), (got.float() - ref.float()).abs().max().item()
+    if k in (2, 4) and T * H * W <= 1536:
+        want = oracle.skiparse_attention(*(x.float().cpu().numpy() for x in (q, kk, v)), T, H, W, k, mode)
+        err = np.abs(got.float().cpu().numpy() - want)
+        print(f"vs oracle: max {err.max():.3e} mean {err.mean():.3e}", flush=True)
+        assert err.max() <= 2e-2 and err.mean() <= 2e-3
+
+
+def test_peaked_scores_equal_fused():
+    """q x 8: peaked softmax, the running reference moves between tiles."""
+    T, H, W, heads, k, mode = 4, 8, 16, 2, 2, oracle.SINGLE
+    w = wl.Workload("rot", 1, T, H, W, heads, 128, k, mode, "bf16")
+    q, kk, v = (x.cuda() for x in wl.make_inputs(w, seed=4, device="cpu"))
+    q = (q.float() * 8).to(torch.bfloat16)
+    qr, kr = sk.rope_qk(q, kk, (T, H, W))
+    got = sk.attn_rotated(qr, kr, v, (T, H, W), k, mode)
+    ref = sk.attn(q, kk, v, (T, H, W), k, mode)
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref)
+
+
+@pytest.mark.parametrize("w", [wl.OSP_SINGLE, wl.OSP_GROUP], ids=lambda w: w.name)
+def test_full_size_equals_fused(w):
+    """The bench workload (24x22x40, 24 heads, k = 4), in the bench's launch configuration:
+    one rotation serving the attention, bit-exact against the fused kernel everywhere."""
+    print(f"full size {w.name}", flush=True)
+    q, kk, v = (x.cuda() for x in wl.make_inputs(w, seed=0, device="cpu"))
+    qr, kr = sk.rope_qk(q, kk, w.grid)
+    got = sk.attn_rotated(qr, kr, v, w.grid, w.sparse_k, w.mode)
+    ref = sk.attn(q, kk, v, w.grid, w.sparse_k, w.mode)
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref)
