@@ -343,9 +343,51 @@ attn_rot_kernel(AttnParams a) {
     wait_vm_loads();
     __syncthreads();
     auto opaque = [](int x) __attribute__((always_inline)) { return __builtin_amdgcn_readfirstlane(x); };
-    auto mfma_block = [&](int m) __attribute__((always_inline)) {
-        if (m >= 1) pv(opaque((m - 1) % 3));
-        if (m < nt) qk(opaque(m % 3));
+    // PV(m-1) and QK(m) as one sequence of 32 MFMAs whose operands come through one ring, so
+    // the first QK operands are read while the last PV products run
+    auto mfma_both = [&](int vb, int kbuf) __attribute__((always_inline)) {
+        const char* vcur = lds + kRVOff + vb * kRTile;
+        const char* kcur = lds + kRKOff + kbuf * kRTile;
+        constexpr int NPV = KK * DB, NQK = KS * KB, NST = NPV + NQK;
+        auto op = [&](int st) __attribute__((always_inline)) {
+            if (st < NPV) {
+                const int kk = st / DB, db = st % DB;
+                const i16x4 lo = ds_read_tr16(vcur + (16 * kk) * kRRow + v_rd(0, db));
+                const i16x4 hi = ds_read_tr16(vcur + (16 * kk) * kRRow + v_rd(1, db));
+                const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                return __builtin_bit_cast(bf16x8, v);
+            }
+            const int t = st - NPV;
+            return *reinterpret_cast<const bf16x8*>(kcur + k_rd[t / KB] + (t % KB) * 32 * kRRow);
+        };
+        bf16x8 ra[kRing];
+#pragma unroll
+        for (int st = 0; st < kRing - 1; ++st) ra[st] = op(st);
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int st = 0; st < NST; ++st) {
+            if (st + kRing - 1 < NST) ra[(st + kRing - 1) % kRing] = op(st + kRing - 1);
+            if (st < NPV) {
+                o[st % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[st % kRing], pb[st / DB], o[st % DB], 0, 0, 0);
+            } else {
+                const int t = st - NPV;
+                sacc[t % KB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[st % kRing], qreg[t / KB], t < KB ? s_init : sacc[t % KB], 0, 0, 0);
+            }
+        }
+        constexpr int kPro = (kRing - 1) * 2;
+        __builtin_amdgcn_sched_group_barrier(0x100, kPro, 0);
+#pragma unroll
+        for (int i = 0; i < NPV - (kRing - 1); ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+#pragma unroll
+        for (int i = NPV - (kRing - 1); i < NST - (kRing - 1); ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, kRing - 1, 0);
+        __builtin_amdgcn_s_setprio(0);
     };
     auto valu_block = [&](int m, int sm) __attribute__((always_inline)) {
         const bool lv = m + 1 < nt, lk = m + 2 < nt;
@@ -356,20 +398,37 @@ attn_rot_kernel(AttnParams a) {
         else if (lv) wait_vm_loads_but<kOps>();
         else wait_vm_loads();
     };
+    // The first and last MFMA blocks (QK(0) alone, PV(nt-1) alone) are peeled off the loops.
     if (grp == 0) {
-        for (int m = 0; m <= nt; ++m) {
-            mfma_block(m);
+        qk(0);
+        __syncthreads();
+        valu_block(0, 0);
+        __syncthreads();
+        for (int m = 1; m < nt; ++m) {
+            mfma_both(opaque((m - 1) % 3), opaque(m % 3));
             __syncthreads();
             valu_block(m, m);
             __syncthreads();
         }
+        pv(opaque((nt - 1) % 3));
+        __syncthreads();
+        valu_block(nt, nt);
+        __syncthreads();
     } else {
-        for (int m = 0; m <= nt; ++m) {
+        valu_block(0, -1);
+        __syncthreads();
+        qk(0);
+        __syncthreads();
+        for (int m = 1; m < nt; ++m) {
             valu_block(m, m - 1);
             __syncthreads();
-            mfma_block(m);
+            mfma_both(opaque((m - 1) % 3), opaque(m % 3));
             __syncthreads();
         }
+        valu_block(nt, nt - 1);
+        __syncthreads();
+        pv(opaque((nt - 1) % 3));
+        __syncthreads();
     }
 
     // ---- epilogue: normalise and scatter rows back to their tokens ----
