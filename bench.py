@@ -4,11 +4,14 @@
 
 A step is one Skiparse attention forward of the 24x22x40-token (N = 21120)
 Open-Sora-Plan-like workload (B=1, 24 heads, head_dim 128, bf16, k = 4) in
-Single Skip mode followed by one in Group Skip mode, each a single launch of
-the fused kernel (RoPE, gather, attention, scatter).  Inputs are resident in
-HBM before timing starts.  Prints one JSON line with the throughput in
-TFLOP/s, the fused kernel's roofline figures, the standalone RoPE+remap pass
-in GB/s, and the fp64 oracle's throughput on the host cores.
+Single Skip mode followed by one in Group Skip mode.  Each of the two is run as
+a model layer would run it: the RoPE pass over q and k (skiparse_rope_qk), then
+the attention on the rotated operands (skiparse_attn_rotated: gather,
+attention, scatter) -- four launches per step, the rotation not shared between
+the two modes.  Inputs are resident in HBM before timing starts.  Prints one
+JSON line with the throughput in TFLOP/s, the attention kernel's roofline
+figures, the RoPE pass in GB/s, the single-launch fused path (skiparse_attn)
+timed beside it, and the fp64 oracle's throughput on the host cores.
 """
 
 from __future__ import annotations
@@ -27,9 +30,9 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 PEAK_8BIT_TOPS = 5000.0     # MI355X dense int8 (TOP/s) and fp8 (TFLOP/s) MFMA
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_osp_24x22x40_traffic.md")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_rot_osp_24x22x40_traffic.md")
 ATTN_SOURCES = [os.path.join(ROOT, "skiparse_sparse_attention_amd", "csrc", f)
-                for f in ("attn_fwd.hip", "attn_common.hpp")]
+                for f in ("attn_rot.hip", "attn_common.hpp")]
 
 
 def parse_args():
@@ -45,8 +48,8 @@ def parse_args():
     ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass timing")
     ap.add_argument("--no-8bit", action="store_true", help="skip the 8-bit attention timing")
     ap.add_argument("--no-schedule", action="store_true", help="skip the per-layer schedule timing")
-    ap.add_argument("--no-rotated", action="store_true",
-                    help="skip the timing of the pre-rotated path (skiparse_rope_qk + skiparse_attn_rotated)")
+    ap.add_argument("--no-fused", action="store_true",
+                    help="skip the timing of the single-launch fused path (skiparse_attn)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -113,8 +116,10 @@ def cpu_baseline(w, q, k, v, budget_s=15.0):
 
 
 def sweep(sk, wl, stream, reps=3):
-    """Fused-attention TFLOP/s on the other workloads (median of `reps` launches after one warmup
-    launch, HIP events on the launch stream): the k sweep on the 24x22x40 grid and the larger grids."""
+    """Attention TFLOP/s on the other workloads (median of `reps` launches after one warmup
+    launch, HIP events on the launch stream): the k sweep on the 24x22x40 grid and the larger
+    grids; the fused kernel (`tflops`) and the attention on rotated operands (`rot_tflops`,
+    the RoPE pass not included)."""
     import torch
     works = []
     for k_ in (1, 2, 4, 8):
@@ -128,21 +133,30 @@ def sweep(sk, wl, stream, reps=3):
         if key not in cache:
             cache.clear()
             cache[key] = tuple(t.cuda() for t in wl.make_inputs(w, seed=0, device="cpu"))
-        q, k, v = cache[key]
+            q, k, _ = cache[key]
+            cache[key] += sk.rope_qk(q, k, w.grid, stream=stream)
+        q, k, v, qr, kr = cache[key]
         out = torch.empty_like(q)
-        sk.attn(q, k, v, w.grid, w.sparse_k, w.mode, out=out, stream=stream)
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
-        ev[0].record(stream)
-        for i in range(reps):
-            sk.attn(q, k, v, w.grid, w.sparse_k, w.mode, out=out, stream=stream)
-            ev[i + 1].record(stream)
-        torch.cuda.synchronize()
-        ms = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(reps))[reps // 2]
+
+        def timed(fn):
+            fn()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+            ev[0].record(stream)
+            for i in range(reps):
+                fn()
+                ev[i + 1].record(stream)
+            torch.cuda.synchronize()
+            return sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(reps))[reps // 2]
+
         flops = sk.attn_flops(w.B, w.grid, w.heads, w.head_dim, w.sparse_k)
+        ms = timed(lambda: sk.attn(q, k, v, w.grid, w.sparse_k, w.mode, out=out, stream=stream))
         tf = flops / (ms * 1e-3) / 1e12
+        rms = timed(lambda: sk.attn_rotated(qr, kr, v, w.grid, w.sparse_k, w.mode, out=out, stream=stream))
+        rtf = flops / (rms * 1e-3) / 1e12
         name = f"{w.T}x{w.H}x{w.W}_b{w.B}_h{w.heads}_k{w.sparse_k}_{'single' if w.mode == 0 else 'group'}"
         res[name] = {"N": w.N, "ms": round(ms, 4), "tflops": round(tf, 1),
-                     "pct_of_bf16_peak": round(100.0 * tf / PEAK_BF16_TFLOPS, 2)}
+                     "pct_of_bf16_peak": round(100.0 * tf / PEAK_BF16_TFLOPS, 2),
+                     "rot_ms": round(rms, 4), "rot_tflops": round(rtf, 1)}
         del out
     cache.clear()
     return res
@@ -224,52 +238,32 @@ def eight_bit(sk, wl, q, k, v, stream, reps=20):
             "flop_per_call": flops, "per_mode": res}
 
 
-def rotated(sk, wl, q, k, v, stream, reps=20):
-    """The pre-rotated path on the 24x22x40 workload: skiparse_rope_qk (one HBM pass over q and
-    k) and skiparse_attn_rotated per mode, each the median of `reps` calls, with the fused
-    skiparse_attn timed in the same loop (calls interleaved) for comparison.  `per_call` prices
-    one attention as a model layer runs it (a rotation, then the attention); `shared` prices the
-    step of this benchmark with one rotation serving both modes' attention."""
+def fused(sk, wl, q, k, v, stream, reps=20):
+    """The single-launch fused path (skiparse_attn: RoPE inside the tile loads) on the 24x22x40
+    workload, both modes, each the median of `reps` launches timed with HIP events on the
+    launch stream."""
     import torch
     ws = wl.OSP_SINGLE
     flops = sk.attn_flops(ws.B, ws.grid, ws.heads, ws.head_dim, ws.sparse_k)
-    qr, kr = sk.rope_qk(q, k, ws.grid, stream=stream)
     out = torch.empty_like(q)
-    calls = {"rope": lambda: sk.rope_qk(q, k, ws.grid, outs=(qr, kr), stream=stream)}
+    res = {}
     for w in (wl.OSP_SINGLE, wl.OSP_GROUP):
-        m = "single" if w.mode == 0 else "group"
-        calls["rot_" + m] = (lambda w=w: sk.attn_rotated(qr, kr, v, w.grid, w.sparse_k, w.mode, out=out, stream=stream))
-        calls["fused_" + m] = (lambda w=w: sk.attn(q, k, v, w.grid, w.sparse_k, w.mode, out=out, stream=stream))
-    for fn in calls.values():
         for _ in range(3):
-            fn()
-    times = {name: [] for name in calls}
-    for _ in range(reps):
-        for name, fn in calls.items():
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            fn()
-            e1.record(stream)
-            times[name].append((e0, e1))
-    torch.cuda.synchronize()
-    ms = {name: sorted(a.elapsed_time(b) for a, b in ev)[reps // 2] for name, ev in times.items()}
-    rope_bytes = 4 * q.numel() * q.element_size()          # read q, k; write qr, kr
-    res = {"rope_qk": {"kernel": "rope_qk_kernel", "bound": "hbm", "ms": round(ms["rope"], 4),
-                       "bytes": rope_bytes,
-                       "gbs": round(rope_bytes / (ms["rope"] * 1e-3) / 1e9, 1)}}
-    for m in ("single", "group"):
-        r, f = ms["rot_" + m], ms["fused_" + m]
-        res[m] = {"attn_rotated_ms": round(r, 4), "attn_rotated_tflops": round(flops / (r * 1e-3) / 1e12, 1),
-                  "fused_ms": round(f, 4), "fused_tflops": round(flops / (f * 1e-3) / 1e12, 1)}
-    rot_ms = ms["rot_single"] + ms["rot_group"]
-    fused_ms = ms["fused_single"] + ms["fused_group"]
-    res["per_call_tflops"] = round(2 * flops / ((rot_ms + 2 * ms["rope"]) * 1e-3) / 1e12, 1)
-    res["shared_tflops"] = round(2 * flops / ((rot_ms + ms["rope"]) * 1e-3) / 1e12, 1)
-    res["fused_tflops"] = round(2 * flops / (fused_ms * 1e-3) / 1e12, 1)
-    res["attn_rotated"] = {"kernel": "attn_rot_kernel", "bound": "mfma",
-                           "achieved": round(2 * flops / (rot_ms * 1e-3) / 1e12, 1), "peak": PEAK_BF16_TFLOPS,
-                           "unit": "TFLOP/s", "frac": round(2 * flops / (rot_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
-    return res
+            sk.attn(q, k, v, w.grid, w.sparse_k, w.mode, out=out, stream=stream)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev[0].record(stream)
+        for i in range(reps):
+            sk.attn(q, k, v, w.grid, w.sparse_k, w.mode, out=out, stream=stream)
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        ms = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(reps))[reps // 2]
+        res["single" if w.mode == 0 else "group"] = {"ms": round(ms, 4),
+                                                     "tflops": round(flops / (ms * 1e-3) / 1e12, 1)}
+    ms = 0.5 * (res["single"]["ms"] + res["group"]["ms"])
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"kernel": "attn_fwd_kernel<128, bf16>", "bound": "mfma", "achieved": round(tf, 1),
+            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+            "per_mode": res}
 
 
 def schedule(sk, wl, q, k, v, stream, reps=5):
@@ -342,40 +336,55 @@ def main():
     wg = wl.OSP_GROUP
     q, k, v = wl.make_inputs(ws, seed=0, device="cpu")
     qg, kg, vg = q.cuda(), k.cuda(), v.cuda()
+    qr = torch.empty_like(qg)
+    kr = torch.empty_like(kg)
     out_s = torch.empty_like(qg)
     out_g = torch.empty_like(qg)
     stream = torch.cuda.current_stream()
     flops_launch = sk.attn_flops(ws.B, ws.grid, ws.heads, ws.head_dim, ws.sparse_k)
 
-    def step():
-        sk.attn(qg, kg, vg, ws.grid, ws.sparse_k, ws.mode, out=out_s, stream=stream)
-        sk.attn(qg, kg, vg, wg.grid, wg.sparse_k, wg.mode, out=out_g, stream=stream)
+    def rope():
+        sk.rope_qk(qg, kg, ws.grid, outs=(qr, kr), stream=stream)
+
+    def attn(w, out):
+        sk.attn_rotated(qr, kr, vg, w.grid, w.sparse_k, w.mode, out=out, stream=stream)
 
     for _ in range(args.warmup):
-        step()
+        rope()
+        attn(ws, out_s)
+        rope()
+        attn(wg, out_g)
     torch.cuda.synchronize()
 
     # per-launch HIP events on the launch stream, inside the timed region
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps + 1)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4 * args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev[0].record(stream)
     for i in range(args.steps):
-        sk.attn(qg, kg, vg, ws.grid, ws.sparse_k, ws.mode, out=out_s, stream=stream)
-        ev[2 * i + 1].record(stream)
-        sk.attn(qg, kg, vg, wg.grid, wg.sparse_k, wg.mode, out=out_g, stream=stream)
-        ev[2 * i + 2].record(stream)
+        rope()
+        ev[4 * i + 1].record(stream)
+        attn(ws, out_s)
+        ev[4 * i + 2].record(stream)
+        rope()
+        ev[4 * i + 3].record(stream)
+        attn(wg, out_g)
+        ev[4 * i + 4].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    durs = [ev[i].elapsed_time(ev[i + 1]) for i in range(2 * args.steps)]   # ms per launch
-    single_ms = sorted(durs[0::2])[len(durs[0::2]) // 2]
-    group_ms = sorted(durs[1::2])[len(durs[1::2]) // 2]
-    gpu_ms = sum(durs)
+    durs = [ev[i].elapsed_time(ev[i + 1]) for i in range(4 * args.steps)]   # ms per launch
+    rope_durs = durs[0::4] + durs[2::4]
+    single_durs, group_durs = durs[1::4], durs[3::4]
+    single_ms = sorted(single_durs)[len(single_durs) // 2]
+    group_ms = sorted(group_durs)[len(group_durs) // 2]
     ms_per_step = wall * 1e3 / args.steps
     value = 2 * flops_launch * args.steps / wall / 1e12
-    avg_launch_ms = gpu_ms / len(durs)
+    avg_launch_ms = sum(single_durs + group_durs) / (2 * args.steps)
     achieved = flops_launch / (avg_launch_ms * 1e-3) / 1e12
     traffic = measured_traffic(flops_launch)
+    rope_ms = sum(rope_durs) / len(rope_durs)
+    rope_bytes = 4 * qg.numel() * qg.element_size()      # read q, k; write qr, kr
+    rope_gbs = rope_bytes / (rope_ms * 1e-3) / 1e9
 
     result = {
         "metric": "Skiparse attention TFLOP/s (bf16) and % of MFMA peak at N~21k-46k, k=4",
@@ -391,7 +400,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": "osp_24x22x40_h24_d128_k4: Single Skip + Group Skip per step",
+            "workload": "osp_24x22x40_h24_d128_k4: Single Skip + Group Skip per step, each a RoPE pass then the attention",
             "B": ws.B, "T": ws.T, "H": ws.H, "W": ws.W, "N": ws.N, "heads": ws.heads,
             "head_dim": ws.head_dim, "sparse_k": ws.sparse_k, "modes": ["single", "group"],
             "flop_per_launch": flops_launch,
@@ -400,13 +409,18 @@ def main():
         "per_mode_ms": {"single": round(single_ms, 4), "group": round(group_ms, 4)},
         "roofline": {
             "bound": "mfma",
-            "kernel": "attn_fwd_kernel<128, bf16>",
+            "kernel": "attn_rot_kernel (bf16, head_dim 128)",
             "achieved": round(achieved, 2),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
             "avg_launch_ms": round(avg_launch_ms, 4),
+        },
+        "rope_pass": {
+            "kernel": "rope_qk_kernel", "bound": "hbm", "achieved": round(rope_gbs, 1), "peak": PEAK_HBM_GBS,
+            "unit": "GB/s", "frac": round(rope_gbs / PEAK_HBM_GBS, 4), "avg_launch_ms": round(rope_ms, 4),
+            "bytes_per_launch": rope_bytes, "launches_per_step": 2,
         },
     }
 
@@ -456,8 +470,8 @@ def main():
     if not args.no_schedule:
         result["schedule"] = schedule(sk, wl, qg, kg, vg, stream)
 
-    if not args.no_rotated:
-        result["rotated"] = rotated(sk, wl, qg, kg, vg, stream)
+    if not args.no_fused:
+        result["fused"] = fused(sk, wl, qg, kg, vg, stream)
 
     if not args.no_sweep:
         result["sweep"] = sweep(sk, wl, stream)

@@ -40,8 +40,8 @@ constexpr int kRVOff = kRBufs * kRTile;
 constexpr int kRLds = 2 * kRBufs * kRTile;
 constexpr float kRRescaleLog2 = 8.0f;
 
-constexpr int kRopeThreads = 256;
-constexpr int kRopeGrid = 2048;           // rotation workgroups; each builds the table once
+constexpr int kRopeThreads = 1024;         // one workgroup per CU: the table is built once per CU
+constexpr int kRopeGrid = 256;            // rotation workgroups (one per CU of a 256-CU part)
 
 // K tile row r: logical granule g of the row is stored at granule g ^ krswz(r).  The QK operand
 // reads fetch one granule of 16 consecutive rows per 16 lanes, which then fall on 16 distinct
@@ -56,17 +56,27 @@ __device__ __forceinline__ int qk_chunk(int ks, int hf) {
 
 }  // namespace
 
-// ---- the rotation pass: one (token, head) row per 8 lanes, one RoPE chunk pair per lane ----
+// ---- the rotation pass: one (token, head) row per 16 lanes, one RoPE chunk per lane ----
+// Lane c of a row loads its own chunk c and its rotate-half partner (the partner load hits the
+// cache lines of the row that the own-chunk loads of the other 15 lanes fetch), rotates the
+// pair with the fused kernel's helper and keeps the half it owns, so each load and store
+// instruction moves 4 whole rows (1 KiB) and the values are the fused kernel's bit for bit.
 __global__ void __launch_bounds__(kRopeThreads) rope_qk_kernel(RopeQkParams a) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     build_banked_rope_table<kRD>(lds, a.T, a.H, a.W, 0);
     __syncthreads();
-    const int cp = threadIdx.x & 7;
+    const int c = threadIdx.x & 15;
+    // the chunk pair of chunk c (rope_pair order: t pairs 0-1, h pairs 2-4, w pairs 5-7)
+    const int cp = c < 4 ? (c & 1) : (c < 10 ? 2 + (c - 4) % 3 : 5 + (c - 10) % 3);
     const RopePair rp = rope_pair(cp);
+    const bool first = c == rp.c1;
+    const int other = first ? rp.c2 : rp.c1;
     const int HW = a.H * a.W;
+    constexpr int kRows = kRopeThreads / 16;                // rows per workgroup step
     const int tasks = a.B * a.N * a.heads;                  // (token row, head) rows
-    const int step = gridDim.x * (kRopeThreads / 8);
-    for (int t = blockIdx.x * (kRopeThreads / 8) + (threadIdx.x >> 3); t < tasks; t += step) {
+    const int step = gridDim.x * kRows;
+#pragma unroll 2
+    for (int t = blockIdx.x * kRows + (threadIdx.x >> 4); t < tasks; t += step) {
         const int n = (t / a.heads) % a.N;
         const int pos = rp.axis == 0 ? n / HW : (rp.axis == 1 ? (n / a.W) % a.H : n % a.W);
         const char* trow = lds + rope_tab_offset<kRD>(a.T, a.H, rp.axis, pos, rp.jchunk * kRCH, 0);
@@ -74,17 +84,20 @@ __global__ void __launch_bounds__(kRopeThreads) rope_qk_kernel(RopeQkParams a) {
 #pragma unroll
         for (int j = 0; j < kRCH / 2; ++j) cs[j] = *reinterpret_cast<const f32x4*>(trow + 16 * j);
         const int64_t row = (int64_t)t * kRRow;             // byte offset of the (token, head) row
+        u32x4 wown[2], woth[2];
 #pragma unroll
         for (int which = 0; which < 2; ++which) {
             const char* in = reinterpret_cast<const char*>(which == 0 ? a.q : a.k) + row;
-            char* out = reinterpret_cast<char*>(which == 0 ? a.qr : a.kr) + row;
+            wown[which] = *reinterpret_cast<const u32x4*>(in + c * 16);
+            woth[which] = *reinterpret_cast<const u32x4*>(in + other * 16);
+        }
+#pragma unroll
+        for (int which = 0; which < 2; ++which) {
             ChunkRaw<BF16, kRCH> r1, r2;
-            const u32x4 w1 = *reinterpret_cast<const u32x4*>(in + rp.c1 * 16);
-            const u32x4 w2 = *reinterpret_cast<const u32x4*>(in + rp.c2 * 16);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                r1.w[i] = w1[i];
-                r2.w[i] = w2[i];
+                r1.w[i] = first ? wown[which][i] : woth[which][i];
+                r2.w[i] = first ? woth[which][i] : wown[which][i];
             }
             float x1[kRCH], x2[kRCH];
             raw_to_f32(r1, x1);
@@ -97,7 +110,12 @@ __global__ void __launch_bounds__(kRopeThreads) rope_qk_kernel(RopeQkParams a) {
                     x2[e] *= a.scale_log2;
                 }
             }
-            store_rotated_chunks<kRCH>(out + rp.c1 * 16, out + rp.c2 * 16, x1, x2);
+            u32x4 w;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                w[i] = first ? pack_bf16x2(x1[2 * i], x1[2 * i + 1]) : pack_bf16x2(x2[2 * i], x2[2 * i + 1]);
+            char* out = reinterpret_cast<char*>(which == 0 ? a.qr : a.kr) + row;
+            *reinterpret_cast<u32x4*>(out + c * 16) = w;
         }
     }
 }
@@ -453,7 +471,7 @@ attn_rot_kernel(AttnParams a) {
 hipError_t launch_rope_qk(const RopeQkParams& a, hipStream_t stream) {
     const size_t lds = (size_t)(a.T + a.H + a.W) * 256;
     const int64_t tasks = (int64_t)a.B * a.N * a.heads;
-    const int64_t blocks = (tasks + kRopeThreads / 8 - 1) / (kRopeThreads / 8);
+    const int64_t blocks = (tasks + kRopeThreads / 16 - 1) / (kRopeThreads / 16);
     const int grid = (int)(blocks < kRopeGrid ? blocks : kRopeGrid);
     hipLaunchKernelGGL(rope_qk_kernel, dim3(grid), dim3(kRopeThreads), lds, stream, a);
     return hipGetLastError();
