@@ -162,20 +162,27 @@ def sweep(sk, wl, stream, reps=3):
     return res
 
 
-def backward(sk, wl, q, k, v, stream, reps=10):
+def backward(sk, wl, q, k, v, stream, reps=10, rotated=False):
     """skiparse_attn_bwd (dq kernel, then dk/dv kernel) on the 24x22x40 workload, both modes:
     median of `reps` calls after warm-up, HIP events on the launch stream.  FLOPs counted as
-    twice the forward's (the backward price of Wan 2.1 report section 4.3.1)."""
+    twice the forward's (the backward price of Wan 2.1 report section 4.3.1).  rotated:
+    skiparse_attn_bwd_rotated on skiparse_rope_qk's outputs instead (the rotation pass, run
+    once per forward, is not timed here)."""
     import torch
     res = {}
     ws = wl.OSP_SINGLE
     do = wl.make_output_grad(ws, seed=1, device="cuda")
     grads = tuple(torch.empty_like(q) for _ in range(3))
+    qr, kr = sk.rope_qk(q, k, ws.grid, stream=stream) if rotated else (None, None)
     for w in (wl.OSP_SINGLE, wl.OSP_GROUP):
         out, lse = sk.attn_lse(q, k, v, w.grid, w.sparse_k, w.mode, stream=stream)
         delta = torch.empty_like(lse)
         def call():
-            sk.attn_bwd(q, k, v, out, do, lse, w.grid, w.sparse_k, w.mode, grads=grads, delta=delta, stream=stream)
+            if rotated:
+                sk.attn_bwd_rotated(qr, kr, v, out, do, lse, w.grid, w.sparse_k, w.mode, grads=grads, delta=delta,
+                                    stream=stream)
+            else:
+                sk.attn_bwd(q, k, v, out, do, lse, w.grid, w.sparse_k, w.mode, grads=grads, delta=delta, stream=stream)
         for _ in range(3):
             call()
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
@@ -190,7 +197,8 @@ def backward(sk, wl, q, k, v, stream, reps=10):
         res["single" if w.mode == 0 else "group"] = {"ms": round(ms, 4), "tflops": round(tf, 1)}
     avg_ms = 0.5 * (res["single"]["ms"] + res["group"]["ms"])
     tf = sk.attn_bwd_flops(ws.B, ws.grid, ws.heads, ws.head_dim, ws.sparse_k) / (avg_ms * 1e-3) / 1e12
-    return {"kernels": "attn_bwd_dq_kernel<128, bf16> + attn_bwd_dkdv_kernel<128, bf16>",
+    return {"kernels": "attn_bwd_dq_kernel<128, bf16" + (", rotated" if rotated else "") +
+                       "> + attn_bwd_dkdv_kernel<128, bf16" + (", rotated" if rotated else "") + ">",
             "bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(tf / PEAK_BF16_TFLOPS, 4), "flop_per_call": sk.attn_bwd_flops(ws.B, ws.grid, ws.heads, ws.head_dim, ws.sparse_k),
             "per_mode": res}
@@ -463,6 +471,7 @@ def main():
 
     if not args.no_backward:
         result["backward"] = backward(sk, wl, qg, kg, vg, stream)
+        result["backward_rotated"] = backward(sk, wl, qg, kg, vg, stream, rotated=True)
 
     if not args.no_8bit:
         result["attn8"] = eight_bit(sk, wl, qg, kg, vg, stream)

@@ -149,6 +149,20 @@ int skiparse_attn_rotated(const void* qr, const void* kr, const void* v,
                           void* stream);
 
 /*
+ * skiparse_attn_rotated_lse -- skiparse_attn_rotated that also writes, for the
+ * backward pass, each output row's log2-sum-exp.
+ *
+ * Everything as skiparse_attn_rotated, plus lse: (B, heads, N) fp32, device
+ * memory, caller-owned, with the meaning given at skiparse_attn_lse; must not
+ * overlap qr, kr, v or out.  out and lse equal skiparse_attn_lse's on the
+ * unrotated q, k bit for bit.  One kernel launch.
+ */
+int skiparse_attn_rotated_lse(const void* qr, const void* kr, const void* v,
+                              int B, int T, int H, int W, int heads, int head_dim,
+                              int sparse_k, int mode, int dtype, void* out, float* lse,
+                              void* stream);
+
+/*
  * skiparse_attn_bwd -- gradients of a loss through skiparse_attn (the chain
  * rule of steps 1-4, taken backwards).  Open-Sora Plan's page says Skiparse
  * exists to speed up training; these are the gradients training needs.
@@ -176,6 +190,22 @@ int skiparse_attn_bwd(const void* q, const void* k, const void* v,
                       int B, int T, int H, int W, int heads, int head_dim,
                       int sparse_k, int mode, int dtype,
                       void* dq, void* dk, void* dv, float* delta, void* stream);
+
+/*
+ * skiparse_attn_bwd_rotated -- skiparse_attn_bwd with q and k given as the
+ * outputs of skiparse_rope_qk (qr, kr: rotated, qr also scaled).  out and lse
+ * come from skiparse_attn_rotated_lse (or skiparse_attn_lse) on the same
+ * inputs.  dq and dk are still the gradients with respect to the unrotated
+ * q and k (rotated back inside the kernels), dv with respect to v; they equal
+ * skiparse_attn_bwd's bit for bit.  head_dim 128 and dtype SKIPARSE_BF16 only
+ * (else SKIPARSE_E_UNSUPPORTED); every other rule as skiparse_attn_bwd.  Two
+ * kernel launches.
+ */
+int skiparse_attn_bwd_rotated(const void* qr, const void* kr, const void* v,
+                              const void* out, const void* dout, const float* lse,
+                              int B, int T, int H, int W, int heads, int head_dim,
+                              int sparse_k, int mode, int dtype,
+                              void* dq, void* dk, void* dv, float* delta, void* stream);
 
 /*
  * skiparse_attn_bwd_flops -- FLOPs counted for one skiparse_attn_bwd call:

@@ -25,11 +25,13 @@ from ._lib import (  # noqa: F401
     attn,
     attn8,
     attn_bwd,
+    attn_bwd_rotated,
     attn_schedule,
     attn_bwd_flops,
     attn_flops,
     attn_lse,
     attn_rotated,
+    attn_rotated_lse,
     lib,
     q8_scope_pitch,
     quant8,

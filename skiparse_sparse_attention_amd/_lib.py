@@ -86,6 +86,10 @@ def lib():
         L.skiparse_rope_qk.restype = i
         L.skiparse_attn_rotated.argtypes = [vp, vp, vp] + dims + [i, i, i, vp, vp]
         L.skiparse_attn_rotated.restype = i
+        L.skiparse_attn_rotated_lse.argtypes = [vp, vp, vp] + dims + [i, i, i, vp, vp, vp]
+        L.skiparse_attn_rotated_lse.restype = i
+        L.skiparse_attn_bwd_rotated.argtypes = [vp] * 6 + dims + [i, i, i] + [vp] * 5
+        L.skiparse_attn_bwd_rotated.restype = i
         L.skiparse_status_string.argtypes = [i]
         L.skiparse_status_string.restype = ctypes.c_char_p
         L.skiparse_version.argtypes = []
@@ -178,6 +182,47 @@ def attn_rotated(qr, kr, v, grid, sparse_k, mode, out=None, stream=None):
                                        int(sparse_k), int(mode), _dtype_code(qr), out.data_ptr(),
                                        _stream_ptr(stream)), "skiparse_attn_rotated")
     return out
+
+
+def attn_rotated_lse(qr, kr, v, grid, sparse_k, mode, out=None, lse=None, stream=None):
+    """attn_rotated that also returns each row's log2-sum-exp (B, heads, N) fp32; equals
+    attn_lse(q, k, v, ...) bit for bit."""
+    import torch
+    B, T, H, W, heads, d = _dims(qr, grid)
+    for t in (kr, v):
+        if t.shape != qr.shape or t.dtype != qr.dtype or not t.is_contiguous():
+            raise ValueError("qr, kr, v must share shape, dtype and be contiguous")
+    if out is None:
+        out = torch.empty_like(v)
+    if lse is None:
+        lse = torch.empty((B, heads, T * H * W), dtype=torch.float32, device=v.device)
+    _check(lib().skiparse_attn_rotated_lse(qr.data_ptr(), kr.data_ptr(), v.data_ptr(), B, T, H, W, heads, d,
+                                           int(sparse_k), int(mode), _dtype_code(qr), out.data_ptr(),
+                                           lse.data_ptr(), _stream_ptr(stream)), "skiparse_attn_rotated_lse")
+    return out, lse
+
+
+def attn_bwd_rotated(qr, kr, v, out, dout, lse, grid, sparse_k, mode, grads=None, delta=None, stream=None):
+    """attn_bwd on rope_qk's outputs: (dq, dk, dv) with respect to the unrotated q, k and v;
+    equals attn_bwd(q, k, v, ...) bit for bit."""
+    import torch
+    B, T, H, W, heads, d = _dims(qr, grid)
+    for t in (kr, v, out, dout):
+        if t.shape != qr.shape or t.dtype != qr.dtype or not t.is_contiguous():
+            raise ValueError("qr, kr, v, out, dout must share shape, dtype and be contiguous")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, heads, T * H * W) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous (B, heads, N) float32 tensor")
+    if grads is None:
+        grads = tuple(torch.empty_like(v) for _ in range(3))
+    if delta is None:
+        delta = torch.empty((B, heads, T * H * W), dtype=torch.float32, device=v.device)
+    dq, dk, dv = grads
+    _check(lib().skiparse_attn_bwd_rotated(qr.data_ptr(), kr.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                           dout.data_ptr(), lse.data_ptr(), B, T, H, W, heads, d,
+                                           int(sparse_k), int(mode), _dtype_code(qr), dq.data_ptr(),
+                                           dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
+                                           _stream_ptr(stream)), "skiparse_attn_bwd_rotated")
+    return dq, dk, dv
 
 
 def u_schedule(n_layers, k_max, modes=(SINGLE, GROUP)):

@@ -193,7 +193,22 @@ __device__ __forceinline__ void store_unrotated(const f32x16 (&acc)[D / 32], flo
 // block's score accumulators are live and a wavefront fits in 256 VGPRs: the MFMAs take their
 // accumulators in VGPRs (no AGPR copies) and the two wavefronts of a SIMD hide each other's
 // LDS and dependency latency.
-template <int D, typename E, bool KDIV>
+// One (row, RoPE chunk pair) staging task for operands that are already rotated (and, for q,
+// scaled): the output of skiparse_rope_qk.  The pair's two chunks are moved unchanged into the
+// pair-slot order, so the LDS rows hold exactly what stage_rotated_pair computes from q, k.
+template <int D>
+__device__ __forceinline__ void stage_copied_pair(__amdgpu_buffer_rsrc_t r, int off, const RopePair& rp, int cp,
+                                                  char* lds_row) {
+    constexpr int CH = D / 16;
+    static_assert(CH == 8, "rotated operands: head_dim 128");
+    uint32_t w1[4], w2[4];
+    buffer_load_dwords(r, off + rp.c1 * CH * 2, w1);
+    buffer_load_dwords(r, off + rp.c2 * CH * 2, w2);
+    *reinterpret_cast<u32x4*>(lds_row + 2 * cp * CH * 2) = u32x4{w1[0], w1[1], w1[2], w1[3]};
+    *reinterpret_cast<u32x4*>(lds_row + (2 * cp + 1) * CH * 2) = u32x4{w2[0], w2[1], w2[2], w2[3]};
+}
+
+template <int D, typename E, bool KDIV, bool ROT>
 __global__ void __launch_bounds__(kDqThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_bwd_dq_kernel(AttnBwdParams a) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
@@ -249,8 +264,11 @@ attn_bwd_dq_kernel(AttnBwdParams a) {
     for (int it = 0; it < kDqRows * 8 / kDqThreads; ++it) {
         const int r = (tid >> 3) + it * (kDqThreads / 8);
         const int n = (int)scope_token(qt * kDqRows + r, s, k_, a.mode);   // >= N past the scope end
-        stage_rotated_pair<D, E>(qbuf, n * row_bytes, rp, cp, tab, a.T, a.H, pos_of(n), a.phi_mul, a.scale_log2,
-                                 ktile + r * L::kPitch);
+        if constexpr (ROT)
+            stage_copied_pair<D>(qbuf, n * row_bytes, rp, cp, ktile + r * L::kPitch);
+        else
+            stage_rotated_pair<D, E>(qbuf, n * row_bytes, rp, cp, tab, a.T, a.H, pos_of(n), a.phi_mul, a.scale_log2,
+                                     ktile + r * L::kPitch);
     }
     __syncthreads();
     bf16x8 qreg[KS];
@@ -325,17 +343,23 @@ attn_bwd_dq_kernel(AttnBwdParams a) {
     };
     auto store_kv = [&](int buf) __attribute__((always_inline)) {
         char* kd = ktile + buf * L::kKTile;
-        float x1[CH], x2[CH];
-        raw_to_f32(kraw[0], x1);
-        raw_to_f32(kraw[1], x2);
-        const int pos = rp.axis == 0 ? min(kpos.t, a.T - 1) : (rp.axis == 1 ? kpos.h : kpos.w);
-        const char* row = tab + rope_tab_offset<D>(a.T, a.H, rp.axis, pos, rp.jchunk * CH, rp.axis == 2 ? a.phi_mul : 0);
-        f32x4 cs[CH / 2];
-#pragma unroll
-        for (int j = 0; j < CH / 2; ++j) cs[j] = *reinterpret_cast<const f32x4*>(row + 16 * j);
-        rope_rotate_cs<CH>(x1, x2, cs);
         char* dst = kd + krow * L::kPitch;
-        store_rotated_chunks<CH>(dst + 2 * cp * CH * 2, dst + (2 * cp + 1) * CH * 2, x1, x2);
+        if constexpr (ROT) {
+            // already rotated: the chunks move unchanged
+            *reinterpret_cast<u32x4*>(dst + 2 * cp * CH * 2) = u32x4{kraw[0].w[0], kraw[0].w[1], kraw[0].w[2], kraw[0].w[3]};
+            *reinterpret_cast<u32x4*>(dst + (2 * cp + 1) * CH * 2) = u32x4{kraw[1].w[0], kraw[1].w[1], kraw[1].w[2], kraw[1].w[3]};
+        } else {
+            float x1[CH], x2[CH];
+            raw_to_f32(kraw[0], x1);
+            raw_to_f32(kraw[1], x2);
+            const int pos = rp.axis == 0 ? min(kpos.t, a.T - 1) : (rp.axis == 1 ? kpos.h : kpos.w);
+            const char* row = tab + rope_tab_offset<D>(a.T, a.H, rp.axis, pos, rp.jchunk * CH, rp.axis == 2 ? a.phi_mul : 0);
+            f32x4 cs[CH / 2];
+#pragma unroll
+            for (int j = 0; j < CH / 2; ++j) cs[j] = *reinterpret_cast<const f32x4*>(row + 16 * j);
+            rope_rotate_cs<CH>(x1, x2, cs);
+            store_rotated_chunks<CH>(dst + 2 * cp * CH * 2, dst + (2 * cp + 1) * CH * 2, x1, x2);
+        }
         char* vd = vtile + buf * L::kVTile;
 #pragma unroll
         for (int i = 0; i < kVPer; ++i) {
@@ -454,7 +478,7 @@ attn_bwd_dq_kernel(AttnBwdParams a) {
 // through LDS.  Every MFMA operand comes from LDS (the K', V rows of the workgroup's 128 keys
 // stay resident; the Q', dO tile is staged once per query tile), so a wavefront fits in 256
 // VGPRs and its accumulators stay in VGPRs.
-template <int D, typename E, bool KDIV>
+template <int D, typename E, bool KDIV, bool ROT>
 __global__ void __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_bwd_dkdv_kernel(AttnBwdParams a) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
@@ -515,8 +539,11 @@ attn_bwd_dkdv_kernel(AttnBwdParams a) {
     for (int it = 0; it < kKPer; ++it) {
         const int r = (tid >> 3) + it * (kKvThreads / 8);
         const int n = (int)scope_token(kt * kBwdRows + r, s, k_, a.mode);
-        stage_rotated_pair<D, E>(kbuf, n * row_bytes, rp, cp, tab, a.T, a.H, pos_of(n), a.phi_mul, 1.0f,
-                                 kres + r * L::kPitch);
+        if constexpr (ROT)
+            stage_copied_pair<D>(kbuf, n * row_bytes, rp, cp, kres + r * L::kPitch);
+        else
+            stage_rotated_pair<D, E>(kbuf, n * row_bytes, rp, cp, tab, a.T, a.H, pos_of(n), a.phi_mul, 1.0f,
+                                     kres + r * L::kPitch);
     }
 #pragma unroll
     for (int i = 0; i < kVPer; ++i) {
@@ -578,22 +605,28 @@ attn_bwd_dkdv_kernel(AttnBwdParams a) {
         }
     };
     auto store_q = [&]() __attribute__((always_inline)) {
-        float x1[CH], x2[CH];
-        raw_to_f32(qraw[0], x1);
-        raw_to_f32(qraw[1], x2);
-        const int pos = rp.axis == 0 ? min(qpos.t, a.T - 1) : (rp.axis == 1 ? qpos.h : qpos.w);
-        const char* row = tab + rope_tab_offset<D>(a.T, a.H, rp.axis, pos, rp.jchunk * CH, rp.axis == 2 ? a.phi_mul : 0);
-        f32x4 cs[CH / 2];
-#pragma unroll
-        for (int j = 0; j < CH / 2; ++j) cs[j] = *reinterpret_cast<const f32x4*>(row + 16 * j);
-        rope_rotate_cs<CH>(x1, x2, cs);
-#pragma unroll
-        for (int e = 0; e < CH; ++e) {
-            x1[e] *= a.scale_log2;
-            x2[e] *= a.scale_log2;
-        }
         char* dst = qtile + qrow * L::kPitch;
-        store_rotated_chunks<CH>(dst + 2 * cp * CH * 2, dst + (2 * cp + 1) * CH * 2, x1, x2);
+        if constexpr (ROT) {
+            // already rotated and scaled: the chunks move unchanged
+            *reinterpret_cast<u32x4*>(dst + 2 * cp * CH * 2) = u32x4{qraw[0].w[0], qraw[0].w[1], qraw[0].w[2], qraw[0].w[3]};
+            *reinterpret_cast<u32x4*>(dst + (2 * cp + 1) * CH * 2) = u32x4{qraw[1].w[0], qraw[1].w[1], qraw[1].w[2], qraw[1].w[3]};
+        } else {
+            float x1[CH], x2[CH];
+            raw_to_f32(qraw[0], x1);
+            raw_to_f32(qraw[1], x2);
+            const int pos = rp.axis == 0 ? min(qpos.t, a.T - 1) : (rp.axis == 1 ? qpos.h : qpos.w);
+            const char* row = tab + rope_tab_offset<D>(a.T, a.H, rp.axis, pos, rp.jchunk * CH, rp.axis == 2 ? a.phi_mul : 0);
+            f32x4 cs[CH / 2];
+#pragma unroll
+            for (int j = 0; j < CH / 2; ++j) cs[j] = *reinterpret_cast<const f32x4*>(row + 16 * j);
+            rope_rotate_cs<CH>(x1, x2, cs);
+#pragma unroll
+            for (int e = 0; e < CH; ++e) {
+                x1[e] *= a.scale_log2;
+                x2[e] *= a.scale_log2;
+            }
+            store_rotated_chunks<CH>(dst + 2 * cp * CH * 2, dst + (2 * cp + 1) * CH * 2, x1, x2);
+        }
 #pragma unroll
         for (int j = 0; j < kOPer; ++j) {
             const int idx = tid + kKvThreads * j;
@@ -757,35 +790,41 @@ attn_bwd_dkdv_kernel(AttnBwdParams a) {
     store_unrotated<D, E>(dkacc, 0.69314718055994530942f, dkbuf, nk, row_bytes, pos_of(nk), tab, a.T, a.H, a.phi_mul, lane);
 }
 
-template <int D, typename E, bool KDQ, bool KKV>
+template <int D, typename E, bool KDQ, bool KKV, bool ROT>
 static hipError_t launch_bwd_k(const AttnBwdParams& a, hipStream_t stream) {
     typedef BwdLds<D> L;
     const size_t table = (size_t)(a.T + a.H + a.W) * 256;
     const size_t lds_dq = (size_t)L::kDqTab + table, lds_kv = (size_t)L::kDkvTab + table;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bwd_dq_kernel<D, E, KDQ>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bwd_dq_kernel<D, E, KDQ, ROT>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_dq);
     if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<D, E, KKV>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<D, E, KKV, ROT>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_kv);
     if (e != hipSuccess) return e;
     // dq first: it writes D, which the dk/dv kernel reads (same stream, so in order)
-    hipLaunchKernelGGL((attn_bwd_dq_kernel<D, E, KDQ>), dim3(a.dq_num_work), dim3(kDqThreads), lds_dq, stream, a);
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<D, E, KDQ, ROT>), dim3(a.dq_num_work), dim3(kDqThreads), lds_dq, stream, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, E, KKV>), dim3(a.num_work), dim3(kKvThreads), lds_kv, stream, a);
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, E, KKV, ROT>), dim3(a.num_work), dim3(kKvThreads), lds_kv, stream, a);
     return hipGetLastError();
 }
 
-template <int D, typename E>
+template <int D, typename E, bool ROT>
 static hipError_t launch_bwd_t(const AttnBwdParams& a, hipStream_t stream) {
     static_assert(kBwdQN == kBwdKN, "one divisibility test covers both tile heights");
-    if (kBwdKN % a.sparse_k == 0) return launch_bwd_k<D, E, true, true>(a, stream);
-    return launch_bwd_k<D, E, false, false>(a, stream);
+    if (kBwdKN % a.sparse_k == 0) return launch_bwd_k<D, E, true, true, ROT>(a, stream);
+    return launch_bwd_k<D, E, false, false, ROT>(a, stream);
 }
 
 hipError_t launch_attn_bwd(const AttnBwdParams& a, int head_dim, int dtype, hipStream_t stream) {
-    if (head_dim == 128) return dtype == 0 ? launch_bwd_t<128, BF16>(a, stream) : launch_bwd_t<128, FP32>(a, stream);
-    return dtype == 0 ? launch_bwd_t<64, BF16>(a, stream) : launch_bwd_t<64, FP32>(a, stream);
+    if (head_dim == 128)
+        return dtype == 0 ? launch_bwd_t<128, BF16, false>(a, stream) : launch_bwd_t<128, FP32, false>(a, stream);
+    return dtype == 0 ? launch_bwd_t<64, BF16, false>(a, stream) : launch_bwd_t<64, FP32, false>(a, stream);
+}
+
+// q and k already rotated (q also scaled) by skiparse_rope_qk: head_dim 128, bf16
+hipError_t launch_attn_bwd_rot(const AttnBwdParams& a, hipStream_t stream) {
+    return launch_bwd_t<128, BF16, true>(a, stream);
 }
 
 int attn_bwd_block_rows() { return kBwdRows; }

@@ -121,6 +121,9 @@ __global__ void __launch_bounds__(kRopeThreads) rope_qk_kernel(RopeQkParams a) {
 }
 
 // ---- attention on qr, kr, v ----
+// LSE: also write each row's log2-sum-exp for the backward (a separate instantiation, so the
+// plain forward carries none of its code).
+template <bool LSE>
 __global__ void __launch_bounds__(kRThreads) __attribute__((amdgpu_waves_per_eu(kRThreads / 256, kRThreads / 256)))
 attn_rot_kernel(AttnParams a) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
@@ -452,9 +455,13 @@ attn_rot_kernel(AttnParams a) {
     // ---- epilogue: normalise and scatter rows back to their tokens ----
     {
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_part), __float_as_uint(l_part), false, false);
-        const float inv = 1.0f / (__uint_as_float(sw[0]) + __uint_as_float(sw[1]));
+        const float l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+        const float inv = 1.0f / l_tot;
         const int p = qt * kRBM + wave * 32 + l32;
-        const int off = (int)scope_token(p, s, k_, a.mode) * row_bytes;   // past the slice when p >= L
+        const int n_tok = (int)scope_token(p, s, k_, a.mode);
+        const int off = n_tok * row_bytes;   // past the slice when p >= L
+        if (LSE && hf == 0 && p < a.L)
+            a.lse[((int64_t)b * a.heads + head) * a.N + n_tok] = m_ref + log2f(l_tot);
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -477,12 +484,17 @@ hipError_t launch_rope_qk(const RopeQkParams& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-hipError_t launch_attn_rot(const AttnParams& a, hipStream_t stream) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_rot_kernel),
+template <bool LSE>
+static hipError_t launch_attn_rot_l(const AttnParams& a, hipStream_t stream) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_rot_kernel<LSE>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, kRLds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(attn_rot_kernel, dim3(a.num_work), dim3(kRThreads), kRLds, stream, a);
+    hipLaunchKernelGGL(attn_rot_kernel<LSE>, dim3(a.num_work), dim3(kRThreads), kRLds, stream, a);
     return hipGetLastError();
+}
+
+hipError_t launch_attn_rot(const AttnParams& a, hipStream_t stream) {
+    return a.lse != nullptr ? launch_attn_rot_l<true>(a, stream) : launch_attn_rot_l<false>(a, stream);
 }
 
 }  // namespace skiparse

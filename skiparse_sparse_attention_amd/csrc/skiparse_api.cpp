@@ -151,15 +151,22 @@ int skiparse_rope_qk(const void* q, const void* k, int B, int T, int H, int W, i
     return to_status(skiparse::launch_rope_qk(a, static_cast<hipStream_t>(stream)));
 }
 
-int skiparse_attn_rotated(const void* qr, const void* kr, const void* v, int B, int T, int H, int W,
-                          int heads, int head_dim, int sparse_k, int mode, int dtype, void* out,
-                          void* stream) {
+// skiparse_attn_rotated and skiparse_attn_rotated_lse (lse may be NULL)
+static int attn_rotated_impl(const void* qr, const void* kr, const void* v, int B, int T, int H, int W,
+                             int heads, int head_dim, int sparse_k, int mode, int dtype, void* out,
+                             float* lse, void* stream) {
     const int st = skiparse_validate(qr, kr, v, B, T, H, W, heads, head_dim, sparse_k, mode, dtype, out);
     if (st != SKIPARSE_OK) return st;
     if (head_dim != 128 || dtype != SKIPARSE_BF16 || skiparse::attn_tile_keys() % sparse_k != 0)
         return SKIPARSE_E_UNSUPPORTED;
     Dims d;
     check_dims(B, T, H, W, heads, head_dim, sparse_k, mode, dtype, &d);
+    if (lse) {
+        const int64_t lse_bytes = (int64_t)B * heads * d.N * 4;
+        if (ranges_overlap(lse, lse_bytes, qr, d.bytes) || ranges_overlap(lse, lse_bytes, kr, d.bytes) ||
+            ranges_overlap(lse, lse_bytes, v, d.bytes) || ranges_overlap(lse, lse_bytes, out, d.bytes))
+            return SKIPARSE_E_ALIAS;
+    }
     skiparse::AttnParams a;
     a.q = qr; a.k = kr; a.v = v; a.out = out;
     a.B = B; a.T = T; a.H = H; a.W = W; a.heads = heads;
@@ -173,8 +180,21 @@ int skiparse_attn_rotated(const void* qr, const void* kr, const void* v, int B, 
     a.k_divides_bn = 1;
     a.scale_log2 = 0.f;   // already folded into qr
     a.phi_mul = 0;
-    a.lse = nullptr;
+    a.lse = lse;
     return to_status(skiparse::launch_attn_rot(a, static_cast<hipStream_t>(stream)));
+}
+
+int skiparse_attn_rotated(const void* qr, const void* kr, const void* v, int B, int T, int H, int W,
+                          int heads, int head_dim, int sparse_k, int mode, int dtype, void* out,
+                          void* stream) {
+    return attn_rotated_impl(qr, kr, v, B, T, H, W, heads, head_dim, sparse_k, mode, dtype, out, nullptr, stream);
+}
+
+int skiparse_attn_rotated_lse(const void* qr, const void* kr, const void* v, int B, int T, int H, int W,
+                              int heads, int head_dim, int sparse_k, int mode, int dtype, void* out,
+                              float* lse, void* stream) {
+    if (!lse) return SKIPARSE_E_NULL;
+    return attn_rotated_impl(qr, kr, v, B, T, H, W, heads, head_dim, sparse_k, mode, dtype, out, lse, stream);
 }
 
 int skiparse_attn_schedule(const skiparse_layer* layers, int n_layers, int B, int T, int H, int W, int heads,
@@ -210,13 +230,15 @@ int skiparse_attn_lse(const void* q, const void* k, const void* v, int B, int T,
     return attn_forward(q, k, v, B, T, H, W, heads, head_dim, sparse_k, mode, dtype, out, lse, stream);
 }
 
-int skiparse_attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
-                      const float* lse, int B, int T, int H, int W, int heads, int head_dim,
-                      int sparse_k, int mode, int dtype, void* dq, void* dk, void* dv, float* delta,
-                      void* stream) {
+// skiparse_attn_bwd and skiparse_attn_bwd_rotated (q, k already rotated, q scaled)
+static int attn_backward(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                         const float* lse, int B, int T, int H, int W, int heads, int head_dim,
+                         int sparse_k, int mode, int dtype, void* dq, void* dk, void* dv, float* delta,
+                         bool rotated, void* stream) {
     if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv || !delta) return SKIPARSE_E_NULL;
     const int st = skiparse_validate(q, k, v, B, T, H, W, heads, head_dim, sparse_k, mode, dtype, out);
     if (st != SKIPARSE_OK) return st;
+    if (rotated && (head_dim != 128 || dtype != SKIPARSE_BF16)) return SKIPARSE_E_UNSUPPORTED;
     Dims d;
     check_dims(B, T, H, W, heads, head_dim, sparse_k, mode, dtype, &d);
     const int64_t vec_bytes = (int64_t)B * heads * d.N * 4;
@@ -251,7 +273,24 @@ int skiparse_attn_bwd(const void* q, const void* k, const void* v, const void* o
     a.scale = (float)(1.0 / std::sqrt((double)head_dim));
     a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)head_dim));
     a.phi_mul = phi_mul_of(mode, sparse_k);
-    return to_status(skiparse::launch_attn_bwd(a, head_dim, dtype, static_cast<hipStream_t>(stream)));
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    return to_status(rotated ? skiparse::launch_attn_bwd_rot(a, hs) : skiparse::launch_attn_bwd(a, head_dim, dtype, hs));
+}
+
+int skiparse_attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                      const float* lse, int B, int T, int H, int W, int heads, int head_dim,
+                      int sparse_k, int mode, int dtype, void* dq, void* dk, void* dv, float* delta,
+                      void* stream) {
+    return attn_backward(q, k, v, out, dout, lse, B, T, H, W, heads, head_dim, sparse_k, mode, dtype, dq, dk, dv,
+                         delta, false, stream);
+}
+
+int skiparse_attn_bwd_rotated(const void* qr, const void* kr, const void* v, const void* out, const void* dout,
+                              const float* lse, int B, int T, int H, int W, int heads, int head_dim,
+                              int sparse_k, int mode, int dtype, void* dq, void* dk, void* dv, float* delta,
+                              void* stream) {
+    return attn_backward(qr, kr, v, out, dout, lse, B, T, H, W, heads, head_dim, sparse_k, mode, dtype, dq, dk, dv,
+                         delta, true, stream);
 }
 
 double skiparse_attn_bwd_flops(int B, int T, int H, int W, int heads, int head_dim, int sparse_k) {

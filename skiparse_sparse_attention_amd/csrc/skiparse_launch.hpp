@@ -115,6 +115,7 @@ hipError_t launch_attn8(const Attn8Params& a, hipStream_t stream);
 int q8_scope_pitch(int L);  // Lp of the vt8 layout
 int attn8_block_rows();     // query rows per 8-bit attention workgroup
 hipError_t launch_rope_qk(const RopeQkParams& a, hipStream_t stream);
-hipError_t launch_attn_rot(const AttnParams& a, hipStream_t stream);
+hipError_t launch_attn_rot(const AttnParams& a, hipStream_t stream);   // a.lse set: also writes it
+hipError_t launch_attn_bwd_rot(const AttnBwdParams& a, hipStream_t stream);
 
 }  // namespace skiparse

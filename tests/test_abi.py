@@ -32,7 +32,7 @@ def test_header_declares_the_boundary():
                  "skiparse_status_string", "skiparse_version", "skiparse_attn_lse",
                  "skiparse_attn_bwd", "skiparse_attn_bwd_flops", "skiparse_quant8", "skiparse_attn8",
                  "skiparse_q8_scope_pitch", "skiparse_attn_schedule", "skiparse_rope_qk",
-                 "skiparse_attn_rotated"):
+                 "skiparse_attn_rotated", "skiparse_attn_rotated_lse", "skiparse_attn_bwd_rotated"):
         assert want in names
 
 
@@ -237,3 +237,22 @@ def test_rotated_path_rejects_before_any_device_call():
     assert L.skiparse_attn_rotated(Q, K, V, 1, 3, 8, 8, 2, 128, 3, 0, 0, OUT, None) == sk.E_UNSUPPORTED  # 3 does not divide 64
     assert L.skiparse_attn_rotated(Q, K, V, 1, 4, 8, 8, 2, 128, 3, 0, 0, OUT, None) == sk.E_DIVISIBILITY
     assert L.skiparse_attn_rotated(Q, K, V, 1, 4, 8, 8, 2, 128, 2, 0, 0, K, None) == sk.E_ALIAS
+
+
+def test_rotated_lse_and_backward_reject_before_any_device_call():
+    L = sk.lib()
+    # skiparse_attn_rotated_lse(qr, kr, v, B, T, H, W, heads, head_dim, sparse_k, mode, dtype, out, lse, stream)
+    assert L.skiparse_attn_rotated_lse(Q, K, V, 1, 4, 8, 8, 2, 128, 2, 0, 0, OUT, None, None) == sk.E_NULL
+    assert L.skiparse_attn_rotated_lse(Q, K, V, 1, 4, 8, 8, 2, 128, 2, 0, 0, OUT, Q, None) == sk.E_ALIAS
+    assert L.skiparse_attn_rotated_lse(Q, K, V, 1, 4, 8, 8, 2, 64, 2, 0, 0, OUT, DELTA, None) == sk.E_UNSUPPORTED
+    # skiparse_attn_bwd_rotated(qr, kr, v, out, dout, lse, B, T, H, W, heads, head_dim, sparse_k, mode, dtype,
+    #                           dq, dk, dv, delta, stream)
+    base = [Q, K, V, OUT, DO, LSE, 1, 4, 8, 8, 2, 128, 2, 0, 0, DQ, DK, DV, DELTA, None]   # valid: never called as is
+    bad = list(base); bad[11] = 64
+    assert L.skiparse_attn_bwd_rotated(*bad) == sk.E_UNSUPPORTED      # head_dim 128 only
+    bad = list(base); bad[14] = 1
+    assert L.skiparse_attn_bwd_rotated(*bad) == sk.E_UNSUPPORTED      # bf16 only
+    bad = list(base); bad[15] = Q
+    assert L.skiparse_attn_bwd_rotated(*bad) == sk.E_ALIAS
+    bad = list(base); bad[5] = None
+    assert L.skiparse_attn_bwd_rotated(*bad) == sk.E_NULL

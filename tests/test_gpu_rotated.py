@@ -7,7 +7,11 @@ Bars:
   bf16 rounding differs from that of the exact value must stay rare (near-ties only);
 * attn_rotated(rope_qk(q, k), v) equals skiparse_attn(q, k, v) bit for bit: the same operands
   in the same contraction order, the same softmax;
-* one case per mode against the fp64 oracle at the attention bars (max 2e-2, mean 2e-3).
+* one case per mode against the fp64 oracle at the attention bars (max 2e-2, mean 2e-3);
+* attn_rotated_lse equals attn_lse (output and log2-sum-exp) bit for bit, and
+  attn_bwd_rotated on rope_qk's outputs equals attn_bwd on q, k bit for bit (the backward
+  kernels stage the same operand bits either way); one backward case against the fp64
+  oracle's chain rule at the bars of test_gpu_backward.py.
 """
 
 import numpy as np
@@ -108,3 +112,86 @@ def test_full_size_equals_fused(w):
     ref = sk.attn(q, kk, v, w.grid, w.sparse_k, w.mode)
     torch.cuda.synchronize()
     assert torch.equal(got, ref)
+
+
+BWD_CASES = [
+    # B, T, H, W, heads, k, mode
+    (1, 4, 8, 16, 2, 4, oracle.SINGLE),      # L = 128
+    (2, 4, 10, 12, 2, 2, oracle.GROUP),      # B = 2, ragged L = 240
+    (1, 4, 10, 12, 3, 1, oracle.SINGLE),     # dense, ragged L = 480
+    (1, 4, 10, 16, 2, 8, oracle.SINGLE),     # L = 80
+    (1, 4, 16, 16, 1, 8, oracle.GROUP),      # L = 128
+]
+
+
+@pytest.mark.parametrize("B,T,H,W,heads,k,mode", BWD_CASES)
+def test_rotated_training_step_equals_fused(B, T, H, W, heads, k, mode):
+    w = wl.Workload("rot", B, T, H, W, heads, 128, k, mode, "bf16")
+    q, kk, v = (x.cuda() for x in wl.make_inputs(w, seed=5, device="cpu"))
+    do = wl.make_output_grad(w, seed=6, device="cuda")
+    print(f"training step B={B} grid={T}x{H}x{W} heads={heads} k={k} mode={mode}", flush=True)
+    qr, kr = sk.rope_qk(q, kk, (T, H, W))
+    out_r, lse_r = sk.attn_rotated_lse(qr, kr, v, (T, H, W), k, mode)
+    out_f, lse_f = sk.attn_lse(q, kk, v, (T, H, W), k, mode)
+    torch.cuda.synchronize()
+    assert torch.equal(out_r, out_f)
+    assert torch.equal(lse_r, lse_f)
+    g_r = sk.attn_bwd_rotated(qr, kr, v, out_r, do, lse_r, (T, H, W), k, mode)
+    g_f = sk.attn_bwd(q, kk, v, out_f, do, lse_f, (T, H, W), k, mode)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dq", "dk", "dv"), g_r, g_f):
+        assert torch.equal(a, b), (name, (a.float() - b.float()).abs().max().item())
+
+
+def test_rotated_backward_k_not_dividing_the_tile():
+    """k = 3 (the backward's per-tile cursor path): the rotated backward on the fused
+    forward's out and lse equals the plain backward bit for bit."""
+    T, H, W, heads, k, mode = 3, 8, 12, 2, 3, oracle.SINGLE
+    w = wl.Workload("rot", 1, T, H, W, heads, 128, k, mode, "bf16")
+    q, kk, v = (x.cuda() for x in wl.make_inputs(w, seed=7, device="cpu"))
+    do = wl.make_output_grad(w, seed=8, device="cuda")
+    out, lse = sk.attn_lse(q, kk, v, (T, H, W), k, mode)
+    qr, kr = sk.rope_qk(q, kk, (T, H, W))
+    g_r = sk.attn_bwd_rotated(qr, kr, v, out, do, lse, (T, H, W), k, mode)
+    g_f = sk.attn_bwd(q, kk, v, out, do, lse, (T, H, W), k, mode)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dq", "dk", "dv"), g_r, g_f):
+        assert torch.equal(a, b), name
+
+
+def test_rotated_backward_matches_the_oracle():
+    T, H, W, heads, k, mode = 4, 8, 16, 2, 4, oracle.GROUP
+    w = wl.Workload("rot", 1, T, H, W, heads, 128, k, mode, "bf16")
+    q, kk, v = (x.cuda() for x in wl.make_inputs(w, seed=9, device="cpu"))
+    do = wl.make_output_grad(w, seed=10, device="cuda")
+    qr, kr = sk.rope_qk(q, kk, (T, H, W))
+    out, lse = sk.attn_rotated_lse(qr, kr, v, (T, H, W), k, mode)
+    grads = sk.attn_bwd_rotated(qr, kr, v, out, do, lse, (T, H, W), k, mode)
+    torch.cuda.synchronize()
+    host = [x.double().cpu().numpy() for x in (q, kk, v, do)]
+    want = oracle.skiparse_attention_backward(*host, T, H, W, k, mode)
+    for name, g, r in zip(("dq", "dk", "dv"), grads, want):
+        got = g.double().cpu().numpy()
+        rel = np.linalg.norm(got - r) / np.linalg.norm(r)
+        mx = np.abs(got - r).max() / np.abs(r).max()
+        print(f"{name}: relrms {rel:.3e} max/maxref {mx:.3e}", flush=True)
+        assert rel <= 1e-2 and mx <= 2.5e-2, name
+
+
+@pytest.mark.parametrize("w", [wl.OSP_SINGLE, wl.OSP_GROUP], ids=lambda w: w.name)
+def test_full_size_training_step_equals_fused(w):
+    print(f"full-size training step {w.name}", flush=True)
+    q, kk, v = (x.cuda() for x in wl.make_inputs(w, seed=0, device="cpu"))
+    do = wl.make_output_grad(w, seed=1, device="cuda")
+    qr, kr = sk.rope_qk(q, kk, w.grid)
+    out, lse = sk.attn_rotated_lse(qr, kr, v, w.grid, w.sparse_k, w.mode)
+    out_f, lse_f = sk.attn_lse(q, kk, v, w.grid, w.sparse_k, w.mode)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out_f) and torch.equal(lse, lse_f)
+    g_r = sk.attn_bwd_rotated(qr, kr, v, out, do, lse, w.grid, w.sparse_k, w.mode)
+    torch.cuda.synchronize()
+    g_r = [g.clone() for g in g_r]
+    g_f = sk.attn_bwd(q, kk, v, out, do, lse, w.grid, w.sparse_k, w.mode)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dq", "dk", "dv"), g_r, g_f):
+        assert torch.equal(a, b), name
