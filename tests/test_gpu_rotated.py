@@ -101,10 +101,12 @@ def test_peaked_scores_equal_fused():
     assert torch.equal(got, ref)
 
 
-@pytest.mark.parametrize("w", [wl.OSP_SINGLE, wl.OSP_GROUP], ids=lambda w: w.name)
+@pytest.mark.parametrize("w", [wl.OSP_SINGLE, wl.OSP_GROUP, wl.HC_GROUP, wl.WAN_DENSE, wl.LONG_GROUP,
+                               wl.LONG_SINGLE], ids=lambda w: w.name)
 def test_full_size_equals_fused(w):
-    """The bench workload (24x22x40, 24 heads, k = 4), in the bench's launch configuration:
-    one rotation serving the attention, bit-exact against the fused kernel everywhere."""
+    """The bench workload (24x22x40, 24 heads, k = 4), in the bench's launch configuration, and
+    the other full-size workloads (up to N = 46080, B = 2, 40 heads, k = 1 and 8): bit-exact
+    against the fused kernel everywhere."""
     print(f"full size {w.name}", flush=True)
     q, kk, v = (x.cuda() for x in wl.make_inputs(w, seed=0, device="cpu"))
     qr, kr = sk.rope_qk(q, kk, w.grid)
