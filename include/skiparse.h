@@ -15,6 +15,13 @@
  *
  * With sparse_k == 1 this is dense full-3D attention.
  *
+ * Two forms of the same computation, with bit-identical results:
+ *   - skiparse_attn (+ _lse, _bwd): one launch, RoPE applied inside the
+ *     attention kernel's tile loads;
+ *   - skiparse_rope_qk, then skiparse_attn_rotated (+ _lse, skiparse_attn_bwd_rotated):
+ *     step 1 as its own pass, whose output serves any number of attentions
+ *     over the same q and k; head_dim 128, bf16.
+ *
  * Conventions shared by every entry point
  * ---------------------------------------
  * Token layout.  q, k, v and out are dense, contiguous (B, N, heads, head_dim)
