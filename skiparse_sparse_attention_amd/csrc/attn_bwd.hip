@@ -370,6 +370,50 @@ attn_bwd_dq_kernel(AttnBwdParams a) {
         }
     };
 
+    // Rotated operands (ROT): the K and V tiles need no arithmetic, so they are copied into LDS
+    // by loads that write LDS directly.  The padded K tile is 17 pieces of 1 KiB: in piece p,
+    // lane l fills granule 64 p + l, i.e. slot (64 p + l) mod 17 of row (64 p + l) div 17, with
+    // the chunk that the pair-slot order puts there (slot 16, the pad, takes chunk 0 and is
+    // never read).  Wave w moves pieces w and w + 8, wave 0 also piece 16; the V tile's 16
+    // pieces go two per wave in the swizzled row order.
+    static_assert(!ROT || (kBwdKN * L::kPitch == 17 * 1024 && kBwdKN * L::kVPitch == 16 * 1024 && kDqThreads == 512),
+                  "tile pieces of the direct loads");
+    int kdo[3], vdo[2];
+    auto set_dma_rows = [&](int t) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+            const int gi = 64 * (j < 2 ? wave + 8 * j : 16) + lane;
+            const int row = gi / 17, slot = gi % 17;
+            const RopePair sp = rope_pair((slot >> 1) & 7);
+            const int c = slot == 16 ? 0 : ((slot & 1) ? sp.c2 : sp.c1);
+            kdo[j] = (int)scope_token(t * kBwdKN + row, s, k_, a.mode) * row_bytes + c * 16;
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int r = (2 * wave + j) * 4 + lane / G;
+            vdo[j] = (int)scope_token(t * kBwdKN + r, s, k_, a.mode) * row_bytes + (((lane % G) ^ vswz<D>(r)) * 16);
+        }
+    };
+    auto advance_dma_rows = [&](int t) __attribute__((always_inline)) {   // to tile t, from t - 1
+        if constexpr (KDIV) {
+#pragma unroll
+            for (int j = 0; j < 3; ++j) kdo[j] += tile_dn * row_bytes;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) vdo[j] += tile_dn * row_bytes;
+        } else {
+            set_dma_rows(t);
+        }
+    };
+    auto dma_kv = [&](int buf) __attribute__((always_inline)) {
+        char* kd = ktile + buf * L::kKTile;
+        char* vd = vtile + buf * L::kVTile;
+        buffer_load_to_lds16(kbuf, kd + wave * 1024, kdo[0]);
+        buffer_load_to_lds16(kbuf, kd + (wave + 8) * 1024, kdo[1]);
+        if (wave == 0) buffer_load_to_lds16(kbuf, kd + 16 * 1024, kdo[2]);
+        buffer_load_to_lds16(vbuf, vd + (2 * wave) * 1024, vdo[0]);
+        buffer_load_to_lds16(vbuf, vd + (2 * wave + 1) * 1024, vdo[1]);
+    };
+
     const TrLane tr(lane);
     f32x16 dqacc[DB];
 #pragma unroll
@@ -378,16 +422,28 @@ attn_bwd_dq_kernel(AttnBwdParams a) {
         for (int x = 0; x < 16; ++x) dqacc[db][x] = 0.f;
     const int nt = (a.L + kBwdKN - 1) / kBwdKN;
     set_rows(0);
-    load_kv();
-    store_kv(0);
+    if constexpr (ROT) {
+        set_dma_rows(0);
+        dma_kv(0);
+        wait_vm_loads();
+    } else {
+        load_kv();
+        store_kv(0);
+    }
     __syncthreads();
     constexpr int kR = 3;   // depth of the operand rings
     // one key tile; `masked`: the last tile, whose keys past the end of the scope start at -inf
     // (a separate instantiation, peeled out of the loop, so the other tiles carry no masking)
     auto tile = [&](int t, auto masked) __attribute__((always_inline)) {
         if (t + 1 < nt) {
-            advance_rows(t + 1);
-            load_kv();
+            if constexpr (ROT) {
+                // buffer (t + 1) & 1 held tile t - 1, whose readers all passed the last barrier
+                advance_dma_rows(t + 1);
+                dma_kv((t + 1) & 1);
+            } else {
+                advance_rows(t + 1);
+                load_kv();
+            }
         }
         const char* kc = ktile + (t & 1) * L::kKTile;
         const char* vc = vtile + (t & 1) * L::kVTile;
@@ -456,7 +512,9 @@ attn_bwd_dq_kernel(AttnBwdParams a) {
                 }
             }
         }
-        if (t + 1 < nt) store_kv((t + 1) & 1);
+        if constexpr (!ROT) {
+            if (t + 1 < nt) store_kv((t + 1) & 1);
+        }
         wait_vm_loads();
         __syncthreads();
     };
