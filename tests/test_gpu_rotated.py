@@ -68,6 +68,8 @@ CASES = [
     (1, 4, 10, 16, 2, 8, oracle.SINGLE),     # L = 80
     (1, 4, 16, 16, 1, 8, oracle.GROUP),      # L = 128
     (1, 2, 4, 8, 2, 2, oracle.GROUP),        # L = 32: one partial tile
+    (1, 4, 8, 16, 2, 16, oracle.SINGLE),     # k = 16, L = 32
+    (2, 4, 8, 16, 3, 16, oracle.GROUP),      # k = 16, B = 2, L = 32
 ]
 
 
@@ -123,6 +125,7 @@ BWD_CASES = [
     (1, 4, 10, 12, 3, 1, oracle.SINGLE),     # dense, ragged L = 480
     (1, 4, 10, 16, 2, 8, oracle.SINGLE),     # L = 80
     (1, 4, 16, 16, 1, 8, oracle.GROUP),      # L = 128
+    (2, 4, 8, 16, 3, 16, oracle.GROUP),      # k = 16, B = 2, L = 32
 ]
 
 
