@@ -277,7 +277,9 @@ def fused(sk, wl, q, k, v, stream, reps=20):
 def schedule(sk, wl, q, k, v, stream, reps=5):
     """An 8-layer U-shaped (sparse_k, mode) schedule on the 24x22x40 workload (k = 1, 2, 4, 8,
     8, 4, 2, 1, modes alternating): one skiparse_attn_schedule call, and the same call
-    captured once in a HIP graph and replayed.  Counted FLOPs: the sum of the layers'."""
+    captured once in a HIP graph and replayed; then the same with skiparse_attn_schedule_rotated
+    (each layer a RoPE pass and the attention on rotated operands).  Counted FLOPs: the sum of
+    the layers' attention FLOPs."""
     import torch
     ws = wl.OSP_SINGLE
     sched = sk.u_schedule(8, 8)
@@ -307,10 +309,25 @@ def schedule(sk, wl, q, k, v, stream, reps=5):
         sk.attn_schedule(layers, ws.grid)
     torch.cuda.synchronize()
     graph_ms = timed(g.replay)
+    # the same schedule with every layer as the RoPE pass and the attention on rotated operands
+    scratch = (torch.empty_like(q), torch.empty_like(q))
+    rot_ms = timed(lambda: sk.attn_schedule_rotated(layers, ws.grid, scratch=scratch, stream=stream))
+    g2 = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        sk.attn_schedule_rotated(layers, ws.grid, scratch=scratch)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g2):
+        sk.attn_schedule_rotated(layers, ws.grid, scratch=scratch)
+    torch.cuda.synchronize()
+    rot_graph_ms = timed(g2.replay)
     return {"layers": [{"sparse_k": kk, "mode": "single" if mode == 0 else "group"} for kk, mode in sched],
             "flop_per_schedule": flops, "eager_ms": round(eager_ms, 3),
             "eager_tflops": round(flops / (eager_ms * 1e-3) / 1e12, 1), "graph_ms": round(graph_ms, 3),
-            "graph_tflops": round(flops / (graph_ms * 1e-3) / 1e12, 1)}
+            "graph_tflops": round(flops / (graph_ms * 1e-3) / 1e12, 1),
+            "rotated_eager_ms": round(rot_ms, 3), "rotated_eager_tflops": round(flops / (rot_ms * 1e-3) / 1e12, 1),
+            "rotated_graph_ms": round(rot_graph_ms, 3),
+            "rotated_graph_tflops": round(flops / (rot_graph_ms * 1e-3) / 1e12, 1)}
 
 
 def main():

@@ -313,6 +313,20 @@ int skiparse_attn_schedule(const skiparse_layer* layers, int n_layers,
                            int dtype, void* stream);
 
 /*
+ * skiparse_attn_schedule_rotated -- skiparse_attn_schedule with every layer run as
+ * skiparse_rope_qk into the caller's scratch (qr, kr: (B, N, heads, 128) bf16 each,
+ * rewritten by every layer; they must not overlap each other or any layer's q, k,
+ * v, out) followed by skiparse_attn_rotated.  Results equal skiparse_attn_schedule's
+ * bit for bit.  head_dim 128, dtype SKIPARSE_BF16 and every layer's sparse_k
+ * dividing 64 (else SKIPARSE_E_UNSUPPORTED); all layers are validated before the
+ * first launch; two launches per layer, no allocation or memset (capturable in a
+ * HIP graph).
+ */
+int skiparse_attn_schedule_rotated(const skiparse_layer* layers, int n_layers,
+                                   int B, int T, int H, int W, int heads, int head_dim,
+                                   int dtype, void* qr, void* kr, void* stream);
+
+/*
  * skiparse_rope_remap -- the materialised RoPE + rearrange of q, k and v in
  * one pass (the page's add_rope + *_skip_rearrange calls, before attention).
  *

@@ -27,6 +27,7 @@ from ._lib import (  # noqa: F401
     attn_bwd,
     attn_bwd_rotated,
     attn_schedule,
+    attn_schedule_rotated,
     attn_bwd_flops,
     attn_flops,
     attn_lse,

@@ -90,6 +90,8 @@ def lib():
         L.skiparse_attn_rotated_lse.restype = i
         L.skiparse_attn_bwd_rotated.argtypes = [vp] * 6 + dims + [i, i, i] + [vp] * 5
         L.skiparse_attn_bwd_rotated.restype = i
+        L.skiparse_attn_schedule_rotated.argtypes = [ctypes.POINTER(Layer), i] + dims + [i, vp, vp, vp]
+        L.skiparse_attn_schedule_rotated.restype = i
         L.skiparse_status_string.argtypes = [i]
         L.skiparse_status_string.restype = ctypes.c_char_p
         L.skiparse_version.argtypes = []
@@ -251,6 +253,31 @@ def attn_schedule(layers, grid, stream=None):
         arr[i] = Layer(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), int(sk_), int(mode))
     _check(lib().skiparse_attn_schedule(arr, len(layers), B, T, H, W, heads, d, _dtype_code(q0),
                                         _stream_ptr(stream)), "skiparse_attn_schedule")
+    return [layer[3] for layer in layers]
+
+
+def attn_schedule_rotated(layers, grid, scratch=None, stream=None):
+    """attn_schedule with every layer run as the RoPE pass into `scratch` (qr, kr: two tensors
+    shaped like q, reused by all layers) and the attention on the rotated operands; equals
+    attn_schedule bit for bit (head_dim 128, bf16, every sparse_k dividing 64)."""
+    import torch
+    if not layers:
+        raise ValueError("empty schedule")
+    q0 = layers[0][0]
+    B, T, H, W, heads, d = _dims(q0, grid)
+    arr = (Layer * len(layers))()
+    for i, (q, k, v, out, sk_, mode) in enumerate(layers):
+        for t in (q, k, v, out):
+            if t.shape != q0.shape or t.dtype != q0.dtype or not t.is_contiguous():
+                raise ValueError("every layer's q, k, v, out must share shape, dtype and be contiguous")
+        arr[i] = Layer(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), int(sk_), int(mode))
+    qr, kr = scratch if scratch is not None else (torch.empty_like(q0), torch.empty_like(q0))
+    for t in (qr, kr):
+        if t.shape != q0.shape or t.dtype != q0.dtype or not t.is_contiguous():
+            raise ValueError("scratch tensors must match the layers' shape and dtype and be contiguous")
+    _check(lib().skiparse_attn_schedule_rotated(arr, len(layers), B, T, H, W, heads, d, _dtype_code(q0),
+                                                qr.data_ptr(), kr.data_ptr(), _stream_ptr(stream)),
+           "skiparse_attn_schedule_rotated")
     return [layer[3] for layer in layers]
 
 

@@ -215,6 +215,39 @@ int skiparse_attn_schedule(const skiparse_layer* layers, int n_layers, int B, in
     return SKIPARSE_OK;
 }
 
+int skiparse_attn_schedule_rotated(const skiparse_layer* layers, int n_layers, int B, int T, int H, int W,
+                                   int heads, int head_dim, int dtype, void* qr, void* kr, void* stream) {
+    if (!layers || !qr || !kr) return SKIPARSE_E_NULL;
+    if (n_layers < 1 || n_layers > 4096) return SKIPARSE_E_SHAPE;
+    for (int i = 0; i < n_layers; ++i) {
+        const skiparse_layer& l = layers[i];
+        const int st = skiparse_validate(l.q, l.k, l.v, B, T, H, W, heads, head_dim, l.sparse_k, l.mode, dtype, l.out);
+        if (st != SKIPARSE_OK) return st;
+        if (head_dim != 128 || dtype != SKIPARSE_BF16 || skiparse::attn_tile_keys() % l.sparse_k != 0)
+            return SKIPARSE_E_UNSUPPORTED;
+    }
+    Dims d;
+    check_dims(B, T, H, W, heads, head_dim, 1, SKIPARSE_SINGLE, dtype, &d);
+    // the scratch rows are rewritten by every layer: they may not overlap each other or any
+    // layer's buffers
+    if (overlaps(qr, kr, d.bytes)) return SKIPARSE_E_ALIAS;
+    for (int i = 0; i < n_layers; ++i) {
+        const skiparse_layer& l = layers[i];
+        const void* bufs[4] = {l.q, l.k, l.v, l.out};
+        for (int j = 0; j < 4; ++j)
+            if (overlaps(qr, bufs[j], d.bytes) || overlaps(kr, bufs[j], d.bytes)) return SKIPARSE_E_ALIAS;
+    }
+    for (int i = 0; i < n_layers; ++i) {
+        const skiparse_layer& l = layers[i];
+        int st = skiparse_rope_qk(l.q, l.k, B, T, H, W, heads, head_dim, dtype, qr, kr, stream);
+        if (st != SKIPARSE_OK) return st;
+        st = attn_rotated_impl(qr, kr, l.v, B, T, H, W, heads, head_dim, l.sparse_k, l.mode, dtype, l.out, nullptr,
+                               stream);
+        if (st != SKIPARSE_OK) return st;
+    }
+    return SKIPARSE_OK;
+}
+
 int skiparse_attn_lse(const void* q, const void* k, const void* v, int B, int T, int H, int W,
                       int heads, int head_dim, int sparse_k, int mode, int dtype, void* out,
                       float* lse, void* stream) {

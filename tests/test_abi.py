@@ -32,7 +32,8 @@ def test_header_declares_the_boundary():
                  "skiparse_status_string", "skiparse_version", "skiparse_attn_lse",
                  "skiparse_attn_bwd", "skiparse_attn_bwd_flops", "skiparse_quant8", "skiparse_attn8",
                  "skiparse_q8_scope_pitch", "skiparse_attn_schedule", "skiparse_rope_qk",
-                 "skiparse_attn_rotated", "skiparse_attn_rotated_lse", "skiparse_attn_bwd_rotated"):
+                 "skiparse_attn_rotated", "skiparse_attn_rotated_lse", "skiparse_attn_bwd_rotated",
+                 "skiparse_attn_schedule_rotated"):
         assert want in names
 
 
@@ -256,3 +257,20 @@ def test_rotated_lse_and_backward_reject_before_any_device_call():
     assert L.skiparse_attn_bwd_rotated(*bad) == sk.E_ALIAS
     bad = list(base); bad[5] = None
     assert L.skiparse_attn_bwd_rotated(*bad) == sk.E_NULL
+
+
+def test_rotated_schedule_rejects_before_any_device_call():
+    L = sk.lib()
+    good = sk.Layer(Q, K, V, OUT, 2, 0)
+    arr = (sk.Layer * 2)(good, good)
+    QR, KR = 11 << 40, 12 << 40
+    # skiparse_attn_schedule_rotated(layers, n, B, T, H, W, heads, head_dim, dtype, qr, kr, stream)
+    assert L.skiparse_attn_schedule_rotated(arr, 2, 1, 4, 8, 8, 2, 128, 0, None, KR, None) == sk.E_NULL
+    assert L.skiparse_attn_schedule_rotated(arr, 2, 1, 4, 8, 8, 2, 128, 0, QR, QR, None) == sk.E_ALIAS     # one scratch
+    assert L.skiparse_attn_schedule_rotated(arr, 2, 1, 4, 8, 8, 2, 128, 0, V, KR, None) == sk.E_ALIAS      # over a layer's v
+    assert L.skiparse_attn_schedule_rotated(arr, 2, 1, 4, 8, 8, 2, 128, 0, QR, OUT, None) == sk.E_ALIAS    # over a layer's out
+    assert L.skiparse_attn_schedule_rotated(arr, 2, 1, 4, 8, 8, 2, 64, 0, QR, KR, None) == sk.E_UNSUPPORTED
+    assert L.skiparse_attn_schedule_rotated(arr, 2, 1, 4, 8, 8, 2, 128, 1, QR, KR, None) == sk.E_UNSUPPORTED
+    k3 = (sk.Layer * 1)(sk.Layer(Q, K, V, OUT, 3, 0))
+    assert L.skiparse_attn_schedule_rotated(k3, 1, 1, 3, 8, 8, 2, 128, 0, QR, KR, None) == sk.E_UNSUPPORTED  # 3 does not divide 64
+    assert L.skiparse_attn_schedule_rotated(arr, 0, 1, 4, 8, 8, 2, 128, 0, QR, KR, None) == sk.E_SHAPE

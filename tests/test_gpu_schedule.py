@@ -79,3 +79,45 @@ def test_schedule_graph_replays_bit_exactly():
         torch.cuda.synchronize()
         for layer, ref in zip(layers, eager):
             assert torch.equal(layer[3], ref), rep
+
+
+def test_rotated_schedule_equals_the_schedule():
+    """Every layer run as the RoPE pass into shared scratch and the attention on rotated
+    operands: the outputs equal skiparse_attn_schedule's bit for bit."""
+    layers = _layers(6, 8, seed=50)
+    print("rotated schedule", [(k, m) for *_, k, m in layers], flush=True)
+    sk.attn_schedule(layers, GRID)
+    torch.cuda.synchronize()
+    ref = [layer[3].clone() for layer in layers]
+    for layer in layers:
+        layer[3].zero_()
+    sk.attn_schedule_rotated(layers, GRID)
+    torch.cuda.synchronize()
+    for (q, kk, v, out, k, mode), r in zip(layers, ref):
+        assert torch.equal(out, r), (k, mode)
+
+
+def test_rotated_schedule_graph_replays_bit_exactly():
+    layers = _layers(8, 8, seed=70)
+    scratch = (torch.empty_like(layers[0][0]), torch.empty_like(layers[0][0]))
+    sk.attn_schedule_rotated(layers, GRID, scratch=scratch)
+    torch.cuda.synchronize()
+    eager = [layer[3].clone() for layer in layers]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        sk.attn_schedule_rotated(layers, GRID, scratch=scratch)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        sk.attn_schedule_rotated(layers, GRID, scratch=scratch)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for layer in layers:
+            layer[3].fill_(float(rep + 1))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for layer, r in zip(layers, eager):
+            assert torch.equal(layer[3], r), rep
