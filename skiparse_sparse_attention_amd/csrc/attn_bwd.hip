@@ -14,20 +14,23 @@
 // by -theta).  Wan 2.1 report, section 4.3.1, prices this backward at twice the forward.
 //
 // Two kernels, both recomputing P from the scores and the saved log2-sum-exp:
-//   attn_bwd_dq_kernel: one workgroup per (batch, head, scope, 128-query tile), 4 wavefronts
+//   attn_bwd_dq_kernel: one workgroup per (batch, head, scope, 256-query tile), 8 wavefronts
 //     of 32 queries.  It computes D of its queries (and stores it for the second kernel),
 //     then streams the scope's 64-key K/V tiles: S^T = K Q'^T onto -LSE, P^T = exp2(S^T),
 //     dP^T = V dO^T, dZ^T = P^T * (dP^T - D), dQ'^T += K^T dZ^T, the K^T operands read from
 //     the row-major K tile with the LDS transpose read.
-//   attn_bwd_dkdv_kernel: one workgroup per (batch, head, scope, 128-key tile), 4 wavefronts
-//     of 32 keys holding K'^T and V^T as B operands; streams the scope's 32-query tiles:
-//     S = Q' K'^T onto -LSE, P, dP = dO V^T, dZ, dV^T += dO^T P, dK^T += Q'^T dZ, the dO^T
-//     and Q'^T operands again from transpose reads.
+//   attn_bwd_dkdv_kernel: one workgroup per (batch, head, scope, 128-key tile), 8 wavefronts,
+//     two on each 32-key group; streams the scope's 64-query tiles: S = Q' K'^T onto -LSE, P,
+//     dP = dO V^T, dZ, dV^T += dO^T P, dK^T += Q'^T dZ, the dO^T and Q'^T operands again from
+//     transpose reads.
 // Rows are gathered through the scope map on load (q and k rotated while staged into LDS
 // from the banked RoPE table), the transposed rotation is applied in registers in the
 // epilogue, and every gradient row is written straight to its original token.  Keys past the
 // end of a scope start at -inf (weight exactly 0); queries past the end carry an infinite
 // log2-sum-exp (weight 0) and D = 0.
+// On operands that skiparse_rope_qk already rotated, the dq kernel copies its tiles into LDS
+// with direct loads (template flag ROT) and attn_bwd_dkdv_rot_kernel replaces the dk/dv kernel:
+// K' and V held in registers, the query tiles streamed into a three-deep LDS ring.
 #include <type_traits>
 
 #include "attn_common.hpp"
@@ -536,7 +539,7 @@ attn_bwd_dq_kernel(AttnBwdParams a) {
 // through LDS.  Every MFMA operand comes from LDS (the K', V rows of the workgroup's 128 keys
 // stay resident; the Q', dO tile is staged once per query tile), so a wavefront fits in 256
 // VGPRs and its accumulators stay in VGPRs.
-template <int D, typename E, bool KDIV, bool ROT>
+template <int D, typename E, bool KDIV>
 __global__ void __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_bwd_dkdv_kernel(AttnBwdParams a) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
@@ -597,11 +600,8 @@ attn_bwd_dkdv_kernel(AttnBwdParams a) {
     for (int it = 0; it < kKPer; ++it) {
         const int r = (tid >> 3) + it * (kKvThreads / 8);
         const int n = (int)scope_token(kt * kBwdRows + r, s, k_, a.mode);
-        if constexpr (ROT)
-            stage_copied_pair<D>(kbuf, n * row_bytes, rp, cp, kres + r * L::kPitch);
-        else
-            stage_rotated_pair<D, E>(kbuf, n * row_bytes, rp, cp, tab, a.T, a.H, pos_of(n), a.phi_mul, 1.0f,
-                                     kres + r * L::kPitch);
+        stage_rotated_pair<D, E>(kbuf, n * row_bytes, rp, cp, tab, a.T, a.H, pos_of(n), a.phi_mul, 1.0f,
+                                 kres + r * L::kPitch);
     }
 #pragma unroll
     for (int i = 0; i < kVPer; ++i) {
@@ -664,11 +664,7 @@ attn_bwd_dkdv_kernel(AttnBwdParams a) {
     };
     auto store_q = [&]() __attribute__((always_inline)) {
         char* dst = qtile + qrow * L::kPitch;
-        if constexpr (ROT) {
-            // already rotated and scaled: the chunks move unchanged
-            *reinterpret_cast<u32x4*>(dst + 2 * cp * CH * 2) = u32x4{qraw[0].w[0], qraw[0].w[1], qraw[0].w[2], qraw[0].w[3]};
-            *reinterpret_cast<u32x4*>(dst + (2 * cp + 1) * CH * 2) = u32x4{qraw[1].w[0], qraw[1].w[1], qraw[1].w[2], qraw[1].w[3]};
-        } else {
+        {
             float x1[CH], x2[CH];
             raw_to_f32(qraw[0], x1);
             raw_to_f32(qraw[1], x2);
@@ -848,6 +844,314 @@ attn_bwd_dkdv_kernel(AttnBwdParams a) {
     store_unrotated<D, E>(dkacc, 0.69314718055994530942f, dkbuf, nk, row_bytes, pos_of(nk), tab, a.T, a.H, a.phi_mul, lane);
 }
 
+// ---------------------------------------------------------------------------------------------
+// dK and dV on rotated operands (head_dim 128, bf16)
+// ---------------------------------------------------------------------------------------------
+// The products of attn_bwd_dkdv_kernel, in the same order, for the q' (rotated, scaled) and k'
+// (rotated) that skiparse_rope_qk writes.  With nothing to convert or rotate on the way in:
+// - the K' and V rows of a wavefront's 32 keys go from memory straight into registers as MFMA
+//   B operands, read once instead of from LDS on every query tile;
+// - the query tiles (Q' rows in pair-slot order, dO rows in natural order, both with the
+//   272-byte pitch whose pad granule spreads 16 rows over all banks, log2-sum-exp, D) go from
+//   memory straight into a ring of three LDS buffers, two tiles ahead of their use, with one
+//   barrier per tile.  Both tiles share one row pitch and so one set of read addresses.
+// Rows past the end of the scope map to tokens past the slice and read as zeros, so their
+// log2-sum-exp and D are 0 (not +inf and 0): with Q' = dO = 0 their P is 1 but dP = 0 and
+// dZ = 0, and every product they enter adds exactly zero.
+struct RotKvLds {
+    static constexpr int kQ = 17 * 1024;            // 64 Q' rows of 272 bytes: 17 pieces of 1 KiB
+    static constexpr int kO = 17 * 1024;            // 64 dO rows of 272 bytes
+    static constexpr int kBuf = kQ + kO + 2 * 256;  // + log2-sum-exp and D of the 64 queries
+    static constexpr int kNB = 3;
+    static constexpr int kTab = kNB * kBuf;         // the RoPE table (read by the epilogue only)
+};
+
+template <bool KDIV>
+__global__ void __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_bwd_dkdv_rot_kernel(AttnBwdParams a) {
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    constexpr int D = 128;
+    constexpr int KS = D / 16;
+    constexpr int DB = D / 32;
+    constexpr int kPitch = D * 2 + 16;       // Q' and dO rows: 16 granules and a pad granule
+    typedef RotKvLds R;
+    static_assert(kBwdQN == 64 && kBwdQN * kPitch == R::kQ && R::kO == R::kQ && kKvThreads == 512,
+                  "tile pieces of the direct loads");
+    static_assert(4 * 16 * DB * 64 * 4 <= R::kTab, "the dV / dK exchange fits the ring");
+    char* tab = lds + R::kTab;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int kgrp = wave & 3, qhalf = wave >> 2;
+    const int l32 = lane & 31, hf = lane >> 5;
+    const int work = xcd_remap(blockIdx.x, gridDim.x);
+    const int kt = work % a.tiles;
+    const int sc = work / a.tiles;
+    const int s = sc % a.sparse_k;
+    const int bh = sc / a.sparse_k;
+    const int head = bh % a.heads;
+    const int b = bh / a.heads;
+    const int64_t k_ = a.sparse_k;
+    const int row_bytes = a.heads * D * 2;
+    const int64_t slice = ((int64_t)b * a.N * a.heads + head) * D * 2;
+    const int slice_bytes = a.N * row_bytes - head * D * 2;
+    auto rsrc = [&](const void* base, int64_t off, int bytes) __attribute__((always_inline)) {
+        return __builtin_amdgcn_make_buffer_rsrc((void*)(reinterpret_cast<const char*>(base) + off), (short)0, bytes,
+                                                 0x00020000);
+    };
+    const __amdgpu_buffer_rsrc_t qbuf = rsrc(a.q, slice, slice_bytes), kbuf = rsrc(a.k, slice, slice_bytes),
+                                 vbuf = rsrc(a.v, slice, slice_bytes), dobuf = rsrc(a.dout, slice, slice_bytes),
+                                 dkbuf = rsrc(a.dk, slice, slice_bytes), dvbuf = rsrc(a.dv, slice, slice_bytes);
+    const int64_t vec0 = ((int64_t)b * a.heads + head) * a.N;   // (b, head) row of lse / delta
+    const __amdgpu_buffer_rsrc_t lbuf = rsrc(a.lse, vec0 * 4, a.N * 4), dlbuf = rsrc(a.delta, vec0 * 4, a.N * 4);
+    const int HW = a.H * a.W;
+
+    build_banked_rope_table<D>(tab, a.T, a.H, a.W, a.phi_mul);
+
+    // ---- K' and V of this lane's key as B operands: k-step ks takes chunk c1 (lanes 0-31) or
+    // c2 (lanes 32-63) of RoPE pair ks for K', natural granule 2 ks + hf for V ----
+    const int pk = kt * kBwdRows + kgrp * 32 + l32;
+    const int nk = (int)scope_token(pk, s, k_, a.mode);
+    bf16x8 kreg[KS], vreg[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        const RopePair rp = rope_pair(ks);
+        uint32_t w[4];
+        buffer_load_dwords(kbuf, nk * row_bytes + (hf ? rp.c2 : rp.c1) * 16, w);
+        kreg[ks] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
+        buffer_load_dwords(vbuf, nk * row_bytes + (2 * ks + hf) * 16, w);
+        vreg[ks] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
+    }
+
+    // ---- query tiles, straight into LDS buffer i mod 3 ----
+    // Each tile is 17 pieces of 1 KiB: in piece p, lane l fills granule 64 p + l, i.e. slot
+    // (64 p + l) mod 17 of row (64 p + l) div 17 (slot 16, the pad, takes chunk 0 and is never
+    // read).  A Q' slot holds the chunk that the pair-slot order puts there, a dO slot the chunk
+    // of its own number.  Wave w moves pieces w and w + 8 of both tiles; wave 0 also Q' piece 16,
+    // wave 1 dO piece 16, wave 2 the tile's log2-sum-exp and wave 3 its D.
+    const int tile_dn = kBwdQN * a.sparse_k;
+    int qdo[2], odo[2], xdo = 0;
+    // the lane index, recomputed where it is used: without KDIV the offsets are rebuilt every
+    // tile, and values derived from a lane index kept since the start would hold registers the
+    // loop does not have
+    auto opaque_lane = [&]() __attribute__((always_inline)) {
+        if constexpr (KDIV) return lane;
+        int l;
+        asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+        return l;
+    };
+    auto piece_off = [&](int i, int p, bool pair_slot) __attribute__((always_inline)) {
+        const int gi = 64 * p + opaque_lane();
+        const int row = gi / 17, slot = gi % 17;
+        const RopePair sp = rope_pair((slot >> 1) & 7);
+        const int c = slot == 16 ? 0 : (pair_slot ? ((slot & 1) ? sp.c2 : sp.c1) : slot);
+        return (int)scope_token(i * kBwdQN + row, s, k_, a.mode) * row_bytes + c * 16;
+    };
+    auto set_dma_rows = [&](int i) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            qdo[j] = piece_off(i, wave + 8 * j, true);
+            odo[j] = piece_off(i, wave + 8 * j, false);
+        }
+        if (wave < 2)
+            xdo = piece_off(i, 16, wave == 0);
+        else if (wave < 4)
+            xdo = (int)scope_token(i * kBwdQN + opaque_lane(), s, k_, a.mode) * 4;
+    };
+    auto advance_dma_rows = [&](int i) __attribute__((always_inline)) {   // to tile i, from i - 1
+        if constexpr (KDIV) {
+            qdo[0] += tile_dn * row_bytes;
+            qdo[1] += tile_dn * row_bytes;
+            odo[0] += tile_dn * row_bytes;
+            odo[1] += tile_dn * row_bytes;
+            xdo += wave < 2 ? tile_dn * row_bytes : tile_dn * 4;
+        } else {
+            set_dma_rows(i);
+        }
+    };
+    auto dma = [&](int buf) __attribute__((always_inline)) {
+        char* qd = lds + buf * R::kBuf;
+        char* od = qd + R::kQ;
+        char* ld = od + R::kO;
+        buffer_load_to_lds16(qbuf, qd + wave * 1024, qdo[0]);
+        buffer_load_to_lds16(qbuf, qd + (wave + 8) * 1024, qdo[1]);
+        buffer_load_to_lds16(dobuf, od + wave * 1024, odo[0]);
+        buffer_load_to_lds16(dobuf, od + (wave + 8) * 1024, odo[1]);
+        if (wave == 0)
+            buffer_load_to_lds16(qbuf, qd + 16 * 1024, xdo);
+        else if (wave == 1)
+            buffer_load_to_lds16(dobuf, od + 16 * 1024, xdo);
+        else if (wave == 2)
+            buffer_load_to_lds4(lbuf, ld, xdo);
+        else if (wave == 3)
+            buffer_load_to_lds4(dlbuf, ld + 256, xdo);
+    };
+
+    const TrLane tr(lane);
+    f32x16 dvacc[DB], dkacc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int x = 0; x < 16; ++x) {
+            dvacc[db][x] = 0.f;
+            dkacc[db][x] = 0.f;
+        }
+    constexpr int kR1 = 1;  // depth of the operand rings: S / dP products (registers are short there)
+    constexpr int kR = 2;   // dV / dK products
+    const int qb0 = 32 * qhalf;   // this wavefront's query rows in each tile
+    const int nq = (a.L + kBwdQN - 1) / kBwdQN;
+    set_dma_rows(0);
+    dma(0);
+    if (nq > 1) {
+        advance_dma_rows(1);
+        dma(1);
+    }
+    // Every load so far (the registers above and the first two tiles) has landed.  Written as
+    // the compiler's own wait instruction so that it knows the register loads are complete;
+    // otherwise it places its waits for them inside the loop, where they would also wait for
+    // the tile loads in flight.
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0); expcnt, lgkmcnt left at their maxima
+    int cur = 0;   // buffer of tile i
+    for (int i = 0; i < nq; ++i) {
+        // this wave's pieces of tile i have landed once at most those of tile i + 1 (5 on waves
+        // 0-3, 4 on the others) are outstanding
+        if (i + 1 < nq) {
+            if (wave < 4)
+                wait_vm_loads_but<5>();
+            else
+                wait_vm_loads_but<4>();
+        } else {
+            wait_vm_loads();
+        }
+        __syncthreads();   // tile i is in LDS; every wavefront is done with tile i - 1
+        if (i + 2 < nq) {
+            advance_dma_rows(i + 2);
+            dma(cur == 0 ? 2 : cur - 1);   // buffer (i + 2) mod 3 held tile i - 1
+        }
+        const char* qtile = lds + cur * R::kBuf;
+        const char* otile = qtile + R::kQ;
+        const float* ldt = reinterpret_cast<const float*>(otile + R::kO);
+        cur = cur == 2 ? 0 : cur + 1;
+
+        // start values -LSE of the queries qb0 + 8 g + 4 hf + jj this lane's accumulator rows hold
+        f32x16 sacc, dpacc;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const f32x4 l4 = *reinterpret_cast<const f32x4*>(ldt + qb0 + 8 * g + 4 * hf);
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                sacc[4 * g + jj] = -l4[jj];
+                dpacc[4 * g + jj] = 0.f;
+            }
+        }
+        // S = Q' K'^T and dP = dO V^T of the 32-query block: A operands from LDS, B in registers
+        {
+            const int r = qb0 + l32;
+            auto qop = [&](int ks) __attribute__((always_inline)) {
+                return *reinterpret_cast<const bf16x8*>(qtile + r * kPitch + (2 * ks + hf) * 16);
+            };
+            auto oop = [&](int ks) __attribute__((always_inline)) {
+                return *reinterpret_cast<const bf16x8*>(otile + r * kPitch + (2 * ks + hf) * 16);
+            };
+            bf16x8 qa[kR1], oa[kR1];
+#pragma unroll
+            for (int ks = 0; ks < kR1 - 1; ++ks) {
+                qa[ks] = qop(ks);
+                oa[ks] = oop(ks);
+            }
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                if (ks + kR1 - 1 < KS) {
+                    qa[(ks + kR1 - 1) % kR1] = qop(ks + kR1 - 1);
+                    oa[(ks + kR1 - 1) % kR1] = oop(ks + kR1 - 1);
+                }
+                sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ks % kR1], kreg[ks], sacc, 0, 0, 0);
+                dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[ks % kR1], vreg[ks], dpacc, 0, 0, 0);
+            }
+        }
+        // P and dZ as bf16 B operands (query qb0 + 8 g + 4 hf + jj in 16-query step g / 2, slot
+        // 4 (g % 2) + jj); D is read only now, so it holds no registers during the products above
+        bf16x8 pbb[2], dzb[2];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const f32x4 d4 = *reinterpret_cast<const f32x4*>(ldt + kBwdQN + qb0 + 8 * g + 4 * hf);
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int x = 4 * g + jj;
+                const float p = __builtin_amdgcn_exp2f(sacc[x]);
+                pbb[g >> 1][(g & 1) * 4 + jj] = (__bf16)p;
+                dzb[g >> 1][(g & 1) * 4 + jj] = (__bf16)(p * (dpacc[x] - d4[jj]));
+            }
+        }
+        // dV^T += dO^T P and dK^T += Q'^T dZ over the block's two 16-query steps
+        {
+            constexpr int NST = 2 * DB;
+            auto dop = [&](int st) __attribute__((always_inline)) {
+                const int kk = st / DB, db = st % DB;
+                const char* ob = otile + (qb0 + 16 * kk + tr.row) * kPitch + (4 * db + tr.gran) * 16 + tr.byte;
+                return tr_operand(ob, ob + 8 * kPitch);
+            };
+            auto qtop = [&](int st) __attribute__((always_inline)) {
+                const int kk = st / DB, db = st % DB;
+                const char* qb = qtile + (qb0 + 16 * kk + tr.row) * kPitch + (4 * db + tr.gran) * 16 + tr.byte;
+                return tr_operand(qb, qb + 8 * kPitch);
+            };
+            bf16x8 da[kR], ka2[kR];
+#pragma unroll
+            for (int st = 0; st < kR - 1; ++st) {
+                da[st] = dop(st);
+                ka2[st] = qtop(st);
+            }
+#pragma unroll
+            for (int st = 0; st < NST; ++st) {
+                if (st + kR - 1 < NST) {
+                    da[(st + kR - 1) % kR] = dop(st + kR - 1);
+                    ka2[(st + kR - 1) % kR] = qtop(st + kR - 1);
+                }
+                dvacc[st % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[st % kR], pbb[st / DB], dvacc[st % DB], 0, 0, 0);
+                dkacc[st % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka2[st % kR], dzb[st / DB], dkacc[st % DB], 0, 0, 0);
+            }
+        }
+    }
+
+    // ---- the two query halves' partial sums meet in LDS (every load has landed, see the last wait) ----
+    float* red = reinterpret_cast<float*>(lds);   // [kgrp][16 * DB values][64 lanes]
+    auto exchange = [&](f32x16 (&acc)[DB]) __attribute__((always_inline)) {
+        __syncthreads();
+        if (qhalf == 1) {
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int x = 0; x < 16; ++x) red[(kgrp * 16 * DB + db * 16 + x) * 64 + lane] = acc[db][x];
+        }
+        __syncthreads();
+        if (qhalf == 0) {
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int x = 0; x < 16; ++x) acc[db][x] += red[(kgrp * 16 * DB + db * 16 + x) * 64 + lane];
+        }
+    };
+    exchange(dvacc);
+    exchange(dkacc);
+
+    // ---- epilogue (query half 0): dv rows, and dk = (transposed RoPE of dK') / log2(e) ----
+    if (qhalf != 0 || pk >= a.L) return;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int d0 = db * 32 + 8 * g + 4 * hf;
+            const u32x2 v2 = {pack_bf16x2(dvacc[db][4 * g], dvacc[db][4 * g + 1]),
+                              pack_bf16x2(dvacc[db][4 * g + 2], dvacc[db][4 * g + 3])};
+            __builtin_amdgcn_raw_buffer_store_b64(v2, dvbuf, nk * row_bytes + d0 * 2, 0, 0);
+        }
+    Pos kp;
+    kp.t = nk / HW; kp.h = (nk / a.W) % a.H; kp.w = nk % a.W;
+    store_unrotated<D, BF16>(dkacc, 0.69314718055994530942f, dkbuf, nk, row_bytes, kp, tab, a.T, a.H, a.phi_mul, lane);
+}
+
 template <int D, typename E, bool KDQ, bool KKV, bool ROT>
 static hipError_t launch_bwd_k(const AttnBwdParams& a, hipStream_t stream) {
     typedef BwdLds<D> L;
@@ -856,14 +1160,22 @@ static hipError_t launch_bwd_k(const AttnBwdParams& a, hipStream_t stream) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bwd_dq_kernel<D, E, KDQ, ROT>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_dq);
     if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<D, E, KKV, ROT>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_kv);
+    const size_t lds_kvr = (size_t)RotKvLds::kTab + table;
+    if constexpr (ROT)
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bwd_dkdv_rot_kernel<KKV>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_kvr);
+    else
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<D, E, KKV>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_kv);
     if (e != hipSuccess) return e;
     // dq first: it writes D, which the dk/dv kernel reads (same stream, so in order)
     hipLaunchKernelGGL((attn_bwd_dq_kernel<D, E, KDQ, ROT>), dim3(a.dq_num_work), dim3(kDqThreads), lds_dq, stream, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, E, KKV, ROT>), dim3(a.num_work), dim3(kKvThreads), lds_kv, stream, a);
+    if constexpr (ROT)
+        hipLaunchKernelGGL((attn_bwd_dkdv_rot_kernel<KKV>), dim3(a.num_work), dim3(kKvThreads), lds_kvr, stream, a);
+    else
+        hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, E, KKV>), dim3(a.num_work), dim3(kKvThreads), lds_kv, stream, a);
     return hipGetLastError();
 }
 
