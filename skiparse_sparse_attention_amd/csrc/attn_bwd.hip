@@ -75,6 +75,13 @@ struct BwdLds {
     static_assert(4 * 16 * (D / 32) * 64 * 4 <= kKvLd, "the dV / dK exchange fits the tiles");
 };
 
+// 4 bytes per lane from a buffer straight into LDS: lane l's dword lands at dst + 4 l (dst
+// wave-uniform; out-of-range offsets write zeros), the 4-byte form of buffer_load_to_lds16.
+__device__ __forceinline__ void buffer_load_to_lds4(__amdgpu_buffer_rsrc_t r, char* dst, int off) {
+    const unsigned lds_addr = (unsigned)(size_t)((__attribute__((address_space(3))) char*)dst);
+    asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(off), "s"(r), "{m0}"(lds_addr) : "memory");
+}
+
 // 8 consecutive elements of E as a bf16x8 operand, and as floats (bf16 is exact both ways).
 template <typename E>
 __device__ __forceinline__ bf16x8 load8(__amdgpu_buffer_rsrc_t r, int off, float (&x)[8]) {

@@ -170,12 +170,6 @@ __device__ __forceinline__ void buffer_load_to_lds16(__amdgpu_buffer_rsrc_t r, c
     asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off), "s"(r), "{m0}"(lds_addr) : "memory");
 }
 
-// The same with 4 bytes per lane: lane l's dword lands at dst + 4 l.
-__device__ __forceinline__ void buffer_load_to_lds4(__amdgpu_buffer_rsrc_t r, char* dst, int off) {
-    const unsigned lds_addr = (unsigned)(size_t)((__attribute__((address_space(3))) char*)dst);
-    asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(off), "s"(r), "{m0}"(lds_addr) : "memory");
-}
-
 // Wait until every vector memory load of this wave has completed (including loads into LDS).
 __device__ __forceinline__ void wait_vm_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
