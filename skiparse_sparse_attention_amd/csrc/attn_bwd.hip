@@ -1004,7 +1004,7 @@ attn_bwd_dkdv_rot_kernel(AttnBwdParams a) {
             dvacc[db][x] = 0.f;
             dkacc[db][x] = 0.f;
         }
-    constexpr int kR1 = 1;  // depth of the operand rings: S / dP products (registers are short there)
+    constexpr int kR1 = 2;  // depth of the operand rings: S / dP products
     constexpr int kR = 2;   // dV / dK products
     const int qb0 = 32 * qhalf;   // this wavefront's query rows in each tile
     const int nq = (a.L + kBwdQN - 1) / kBwdQN;
@@ -1075,6 +1075,23 @@ attn_bwd_dkdv_rot_kernel(AttnBwdParams a) {
                 }
                 sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ks % kR1], kreg[ks], sacc, 0, 0, 0);
                 dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[ks % kR1], vreg[ks], dpacc, 0, 0, 0);
+            }
+            // Keep the S and dP products alternating, each step's two operand reads between
+            // them (left alone, the compiler runs all S products and then all dP products,
+            // each waiting for a read issued right after the one before it): first the four
+            // log2-sum-exp reads and the ring's first reads, then per k-step an S product, a
+            // read, a dP product, a read, and the last steps' products without reads.
+            __builtin_amdgcn_sched_group_barrier(0x100, 4 + 2 * (kR1 - 1), 0);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                if (ks + kR1 - 1 < KS) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                } else {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                }
             }
         }
         // P and dZ as bf16 B operands (query qb0 + 8 g + 4 hf + jj in 16-query step g / 2, slot
