@@ -206,8 +206,8 @@ def backward(sk, wl, q, k, v, stream, reps=10, rotated=False):
         res["single" if w.mode == 0 else "group"] = {"ms": round(ms, 4), "tflops": round(tf, 1)}
     avg_ms = 0.5 * (res["single"]["ms"] + res["group"]["ms"])
     tf = sk.attn_bwd_flops(ws.B, ws.grid, ws.heads, ws.head_dim, ws.sparse_k) / (avg_ms * 1e-3) / 1e12
-    return {"kernels": "attn_bwd_dq_kernel<128, bf16" + (", rotated" if rotated else "") +
-                       "> + attn_bwd_dkdv_kernel<128, bf16" + (", rotated" if rotated else "") + ">",
+    return {"kernels": ("attn_bwd_dq_kernel<128, bf16, rotated> + attn_bwd_dkdv_rot_kernel" if rotated else
+                        "attn_bwd_dq_kernel<128, bf16> + attn_bwd_dkdv_kernel<128, bf16>"),
             "bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(tf / PEAK_BF16_TFLOPS, 4), "flop_per_call": sk.attn_bwd_flops(ws.B, ws.grid, ws.heads, ws.head_dim, ws.sparse_k),
             "per_mode": res}
