@@ -148,10 +148,15 @@ def test_rotated_training_step_equals_fused(B, T, H, W, heads, k, mode):
         assert torch.equal(a, b), (name, (a.float() - b.float()).abs().max().item())
 
 
-def test_rotated_backward_k_not_dividing_the_tile():
-    """k = 3 (the backward's per-tile cursor path): the rotated backward on the fused
-    forward's out and lse equals the plain backward bit for bit."""
-    T, H, W, heads, k, mode = 3, 8, 12, 2, 3, oracle.SINGLE
+@pytest.mark.parametrize("T,H,W,heads,k,mode", [
+    (3, 8, 12, 2, 3, oracle.SINGLE),    # L = 96: two query tiles
+    (3, 12, 18, 2, 3, oracle.GROUP),    # L = 216: four query tiles, the last ragged
+])
+def test_rotated_backward_k_not_dividing_the_tile(T, H, W, heads, k, mode):
+    """k = 3 (the backward's per-tile cursor path, whose query-tile loads are rebuilt every
+    tile): the rotated backward on the fused forward's out and lse equals the plain backward
+    bit for bit."""
+    print(f"k = 3 backward grid={T}x{H}x{W} mode={mode}", flush=True)
     w = wl.Workload("rot", 1, T, H, W, heads, 128, k, mode, "bf16")
     q, kk, v = (x.cuda() for x in wl.make_inputs(w, seed=7, device="cpu"))
     do = wl.make_output_grad(w, seed=8, device="cuda")
