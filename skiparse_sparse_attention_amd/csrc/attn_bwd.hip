@@ -53,10 +53,12 @@ constexpr int kBwdQN = 64;         // queries per query tile of the dk/dv kernel
 template <int D>
 struct BwdLds {
     static constexpr int kPitch = D * 2 + 16;   // rotated Q/K rows, pair-slot order, one pad granule
-    static constexpr int kVPitch = D * 2;       // V / dO rows, natural order, swizzled granules
-    // dq kernel: two K tiles and two V tiles (aliased first by the Q staging of 256 rows), the table
+    static constexpr int kVPitch = D * 2;       // V / dO rows of the dk/dv kernel, swizzled granules
+    // dq kernel: two K tiles and two V tiles (aliased first by the Q staging of 256 rows), the
+    // table; its V rows keep natural granule order in the padded pitch of the K rows, which is
+    // conflict-free without a swizzle and lets the K and V operand reads share one address
     static constexpr int kKTile = kBwdKN * kPitch;
-    static constexpr int kVTile = kBwdKN * kVPitch;
+    static constexpr int kVTile = kBwdKN * kPitch;
     static constexpr int kDqTiles = 2 * kKTile + 2 * kVTile;
     static constexpr int kDqTab = kDqTiles > kDqRows * kPitch ? kDqTiles : kDqRows * kPitch;
     // dk/dv kernel: K staging (128 rows), aliased afterwards by two Q and two dO tiles; the
@@ -375,7 +377,7 @@ attn_bwd_dq_kernel(AttnBwdParams a) {
         for (int i = 0; i < kVPer; ++i) {
             const int idx = tid + kDqThreads * i;
             const int r = idx / G;
-            *reinterpret_cast<u32x4*>(vd + r * L::kVPitch + (((idx % G) ^ vswz<D>(r)) * 16)) =
+            *reinterpret_cast<u32x4*>(vd + r * L::kPitch + (idx % G) * 16) =
                 u32x4{vraw[i][0], vraw[i][1], vraw[i][2], vraw[i][3]};
         }
     };
@@ -384,11 +386,11 @@ attn_bwd_dq_kernel(AttnBwdParams a) {
     // by loads that write LDS directly.  The padded K tile is 17 pieces of 1 KiB: in piece p,
     // lane l fills granule 64 p + l, i.e. slot (64 p + l) mod 17 of row (64 p + l) div 17, with
     // the chunk that the pair-slot order puts there (slot 16, the pad, takes chunk 0 and is
-    // never read).  Wave w moves pieces w and w + 8, wave 0 also piece 16; the V tile's 16
-    // pieces go two per wave in the swizzled row order.
-    static_assert(!ROT || (kBwdKN * L::kPitch == 17 * 1024 && kBwdKN * L::kVPitch == 16 * 1024 && kDqThreads == 512),
+    // never read).  Wave w moves pieces w and w + 8, wave 0 also piece 16.  The V tile has the
+    // same pitch and pieces with each slot's own chunk; wave 1 moves its piece 16.
+    static_assert(!ROT || (kBwdKN * L::kPitch == 17 * 1024 && L::kVTile == 17 * 1024 && kDqThreads == 512),
                   "tile pieces of the direct loads");
-    int kdo[3], vdo[2];
+    int kdo[3], vdo[3];
     auto set_dma_rows = [&](int t) __attribute__((always_inline)) {
 #pragma unroll
         for (int j = 0; j < 3; ++j) {
@@ -399,9 +401,10 @@ attn_bwd_dq_kernel(AttnBwdParams a) {
             kdo[j] = (int)scope_token(t * kBwdKN + row, s, k_, a.mode) * row_bytes + c * 16;
         }
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int r = (2 * wave + j) * 4 + lane / G;
-            vdo[j] = (int)scope_token(t * kBwdKN + r, s, k_, a.mode) * row_bytes + (((lane % G) ^ vswz<D>(r)) * 16);
+        for (int j = 0; j < 3; ++j) {
+            const int gi = 64 * (j < 2 ? wave + 8 * j : 16) + lane;
+            const int row = gi / 17, slot = gi % 17;
+            vdo[j] = (int)scope_token(t * kBwdKN + row, s, k_, a.mode) * row_bytes + (slot == 16 ? 0 : slot) * 16;
         }
     };
     auto advance_dma_rows = [&](int t) __attribute__((always_inline)) {   // to tile t, from t - 1
@@ -409,7 +412,7 @@ attn_bwd_dq_kernel(AttnBwdParams a) {
 #pragma unroll
             for (int j = 0; j < 3; ++j) kdo[j] += tile_dn * row_bytes;
 #pragma unroll
-            for (int j = 0; j < 2; ++j) vdo[j] += tile_dn * row_bytes;
+            for (int j = 0; j < 3; ++j) vdo[j] += tile_dn * row_bytes;
         } else {
             set_dma_rows(t);
         }
@@ -420,8 +423,9 @@ attn_bwd_dq_kernel(AttnBwdParams a) {
         buffer_load_to_lds16(kbuf, kd + wave * 1024, kdo[0]);
         buffer_load_to_lds16(kbuf, kd + (wave + 8) * 1024, kdo[1]);
         if (wave == 0) buffer_load_to_lds16(kbuf, kd + 16 * 1024, kdo[2]);
-        buffer_load_to_lds16(vbuf, vd + (2 * wave) * 1024, vdo[0]);
-        buffer_load_to_lds16(vbuf, vd + (2 * wave + 1) * 1024, vdo[1]);
+        buffer_load_to_lds16(vbuf, vd + wave * 1024, vdo[0]);
+        buffer_load_to_lds16(vbuf, vd + (wave + 8) * 1024, vdo[1]);
+        if (wave == 1) buffer_load_to_lds16(vbuf, vd + 16 * 1024, vdo[2]);
     };
 
     const TrLane tr(lane);
@@ -441,7 +445,7 @@ attn_bwd_dq_kernel(AttnBwdParams a) {
         store_kv(0);
     }
     __syncthreads();
-    constexpr int kR = 3;   // depth of the operand rings
+    constexpr int kR = 4;   // depth of the operand rings
     // one key tile; `masked`: the last tile, whose keys past the end of the scope start at -inf
     // (a separate instantiation, peeled out of the loop, so the other tiles carry no masking)
     auto tile = [&](int t, auto masked) __attribute__((always_inline)) {
@@ -476,7 +480,7 @@ attn_bwd_dq_kernel(AttnBwdParams a) {
                     return *reinterpret_cast<const bf16x8*>(kc + r * L::kPitch + (2 * ks + hf) * 16);
                 };
                 auto vop = [&](int ks) __attribute__((always_inline)) {
-                    return *reinterpret_cast<const bf16x8*>(vc + r * L::kVPitch + (((2 * ks + hf) ^ vswz<D>(r)) * 16));
+                    return *reinterpret_cast<const bf16x8*>(vc + r * L::kPitch + (2 * ks + hf) * 16);
                 };
                 bf16x8 ka[kR], va[kR];
 #pragma unroll
