@@ -52,24 +52,22 @@ constexpr int kBwdQN = 64;         // queries per query tile of the dk/dv kernel
 
 template <int D>
 struct BwdLds {
-    static constexpr int kPitch = D * 2 + 16;   // rotated Q/K rows, pair-slot order, one pad granule
-    static constexpr int kVPitch = D * 2;       // V / dO rows of the dk/dv kernel, swizzled granules
-    // dq kernel: two K tiles and two V tiles (aliased first by the Q staging of 256 rows), the
-    // table; its V rows keep natural granule order in the padded pitch of the K rows, which is
-    // conflict-free without a swizzle and lets the K and V operand reads share one address
+    // Every tile row has this pitch: rotated Q/K rows in pair-slot order, V/dO rows in natural
+    // granule order, one pad granule each.  The pad spreads 16 consecutive rows over all banks
+    // (no swizzle needed), and tiles of one pitch share their operand-read addresses.
+    static constexpr int kPitch = D * 2 + 16;
+    // dq kernel: two K tiles and two V tiles (aliased first by the Q staging of 256 rows), the table
     static constexpr int kKTile = kBwdKN * kPitch;
     static constexpr int kVTile = kBwdKN * kPitch;
     static constexpr int kDqTiles = 2 * kKTile + 2 * kVTile;
     static constexpr int kDqTab = kDqTiles > kDqRows * kPitch ? kDqTiles : kDqRows * kPitch;
-    // dk/dv kernel: K staging (128 rows), aliased afterwards by two Q and two dO tiles; the
-    // log2-sum-exp and D of two query tiles; the table
     static constexpr int kQTile = kBwdQN * kPitch;
-    static constexpr int kOTile = kBwdQN * kVPitch;
-    // dk/dv kernel: resident K' and V rows of the workgroup's keys, one Q' and one dO tile, the
+    static constexpr int kOTile = kBwdQN * kPitch;
+    // dk/dv kernel (query tiles of kQTile, kOTile): resident K' and V rows of the workgroup's keys, one Q' and one dO tile, the
     // log2-sum-exp and D of the tile, the table (the reduction at the end reuses the tiles)
     static constexpr int kKvK = 0;
     static constexpr int kKvV = kKvK + kBwdRows * kPitch;
-    static constexpr int kKvQ = kKvV + kBwdRows * kVPitch;
+    static constexpr int kKvQ = kKvV + kBwdRows * kPitch;
     static constexpr int kKvO = kKvQ + kQTile;
     static constexpr int kKvLd = kKvO + kOTile;
     static constexpr int kKvTab = kKvLd + 2 * kBwdQN * 4;
@@ -621,7 +619,7 @@ attn_bwd_dkdv_kernel(AttnBwdParams a) {
         const int n = (int)scope_token(kt * kBwdRows + r, s, k_, a.mode);
         uint32_t w[4];
         buffer_load_8_as_bf16x2<E>(vbuf, n * row_bytes + (idx % G) * 8 * ES, w);
-        *reinterpret_cast<u32x4*>(vres + r * L::kVPitch + (((idx % G) ^ vswz<D>(r)) * 16)) = u32x4{w[0], w[1], w[2], w[3]};
+        *reinterpret_cast<u32x4*>(vres + r * L::kPitch + (idx % G) * 16) = u32x4{w[0], w[1], w[2], w[3]};
     }
     const int pk = kt * kBwdRows + kgrp * 32 + l32;   // this lane's key (the B-operand column)
     const int nk = (int)scope_token(pk, s, k_, a.mode);
@@ -696,7 +694,7 @@ attn_bwd_dkdv_kernel(AttnBwdParams a) {
         for (int j = 0; j < kOPer; ++j) {
             const int idx = tid + kKvThreads * j;
             const int r = idx / G;
-            *reinterpret_cast<u32x4*>(otile + r * L::kVPitch + (((idx % G) ^ vswz<D>(r)) * 16)) =
+            *reinterpret_cast<u32x4*>(otile + r * L::kPitch + (idx % G) * 16) =
                 u32x4{oraw[j][0], oraw[j][1], oraw[j][2], oraw[j][3]};
         }
         if (tid < 2 * kBwdQN) ldt[tid] = ldv;
@@ -711,7 +709,7 @@ attn_bwd_dkdv_kernel(AttnBwdParams a) {
             dvacc[db][x] = 0.f;
             dkacc[db][x] = 0.f;
         }
-    constexpr int kR = 2;   // depth of the operand rings
+    constexpr int kR = 3;   // depth of the operand rings
     const int qb0 = 32 * qhalf;   // this wavefront's query rows in each tile
     const int nq = (a.L + kBwdQN - 1) / kBwdQN;
     set_rows(0);
@@ -746,13 +744,13 @@ attn_bwd_dkdv_kernel(AttnBwdParams a) {
                 return *reinterpret_cast<const bf16x8*>(qtile + r * L::kPitch + (2 * ks + hf) * 16);
             };
             auto oop = [&](int ks) __attribute__((always_inline)) {
-                return *reinterpret_cast<const bf16x8*>(otile + r * L::kVPitch + (((2 * ks + hf) ^ vswz<D>(r)) * 16));
+                return *reinterpret_cast<const bf16x8*>(otile + r * L::kPitch + (2 * ks + hf) * 16);
             };
             auto kop = [&](int ks) __attribute__((always_inline)) {
                 return *reinterpret_cast<const bf16x8*>(kres + kr * L::kPitch + (2 * ks + hf) * 16);
             };
             auto vop = [&](int ks) __attribute__((always_inline)) {
-                return *reinterpret_cast<const bf16x8*>(vres + kr * L::kVPitch + (((2 * ks + hf) ^ vswz<D>(kr)) * 16));
+                return *reinterpret_cast<const bf16x8*>(vres + kr * L::kPitch + (2 * ks + hf) * 16);
             };
             bf16x8 qa[kR], oa[kR], kb_[kR], vb_[kR];
 #pragma unroll
@@ -787,9 +785,8 @@ attn_bwd_dkdv_kernel(AttnBwdParams a) {
             constexpr int NST = 2 * DB;
             auto dop = [&](int st) __attribute__((always_inline)) {
                 const int kk = st / DB, db = st % DB;
-                const int r0 = qb0 + 16 * kk + tr.row, r8 = r0 + 8;
-                return tr_operand(otile + r0 * L::kVPitch + (((4 * db + tr.gran) ^ vswz<D>(r0)) * 16) + tr.byte,
-                                  otile + r8 * L::kVPitch + (((4 * db + tr.gran) ^ vswz<D>(r8)) * 16) + tr.byte);
+                const char* ob = otile + (qb0 + 16 * kk + tr.row) * L::kPitch + (4 * db + tr.gran) * 16 + tr.byte;
+                return tr_operand(ob, ob + 8 * L::kPitch);
             };
             auto qtop = [&](int st) __attribute__((always_inline)) {
                 const int kk = st / DB, db = st % DB;
