@@ -263,6 +263,80 @@ def test_rope_1d_special_case_is_textbook_complex_rotation():
     assert np.array_equal(y[..., :o], x[..., :o])   # t and h chunks at position 0 are untouched
 
 
+def _read_position_golden():
+    grids = []
+    with open(os.path.join(GOLDEN, "positions_hand_derived.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            parts = line.split()
+            if parts[0] == "grid":
+                grids.append((int(parts[1]), int(parts[2]), int(parts[3]), []))
+            else:
+                grids[-1][3].append(tuple(int(p) for p in parts))
+    return grids
+
+
+POSITION_GOLDEN = _read_position_golden()
+
+
+@pytest.mark.parametrize("T,H,W,rows", POSITION_GOLDEN)
+def test_token_positions_match_hand_derived_golden(T, H, W, rows):
+    # Frame-major flattening with T, H > 1: a dropped "mod H" on h, or h and w in
+    # swapped roles, changes several of these hand-written rows.
+    t, h, w = oracle.token_positions(T, H, W)
+    assert [r[0] for r in rows] == list(range(T * H * W))
+    assert t.tolist() == [r[1] for r in rows]
+    assert h.tolist() == [r[2] for r in rows]
+    assert w.tolist() == [r[3] for r in rows]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_rope_3d_worked_values_on_a_3d_grid(d):
+    # Token 23 of the 2 x 3 x 4 grid sits at (t, h, w) = (1, 2, 3) (hand-derived golden).
+    # A unit vector on slot j of an axis chunk of size d_a turns by pos * 10000^(-2j/d_a):
+    # j = 0 gives the position itself, j = 1 the hand-evaluated powers of ten below.
+    T, H, W, n = 2, 3, 4, 23
+    assert POSITION_GOLDEN[0][3][n] == (23, 1, 2, 3)
+    if d == 64:   # chunks 16 / 24 / 24
+        chunks = {"t": (0, 16, 1, 10.0 ** -0.5), "h": (16, 24, 2, 10.0 ** (-1.0 / 3.0)),
+                  "w": (40, 24, 3, 10.0 ** (-1.0 / 3.0))}
+    else:         # chunks 32 / 48 / 48
+        chunks = {"t": (0, 32, 1, 10.0 ** -0.25), "h": (32, 48, 2, 10.0 ** (-1.0 / 6.0)),
+                  "w": (80, 48, 3, 10.0 ** (-1.0 / 6.0))}
+    for axis, (o, da, pos, freq1) in chunks.items():
+        for j, angle in ((0, float(pos)), (1, pos * freq1)):
+            x = np.zeros((1, T * H * W, 1, d))
+            x[0, n, 0, o + j] = 1.0
+            y = oracle.rope_3d(x, T, H, W)[0, n, 0]
+            expect = np.zeros(d)
+            expect[o + j] = math.cos(angle)
+            expect[o + j + da // 2] = math.sin(angle)
+            assert np.allclose(y, expect, atol=1e-15, rtol=0), (axis, j)
+
+
+@pytest.mark.parametrize("T,H,W,rows", POSITION_GOLDEN)
+def test_rope_3d_is_per_axis_complex_rotation_at_golden_positions(T, H, W, rows):
+    # On every token of the grid, each axis chunk is 1-D RoPE along that axis: the pair
+    # (x1, x2) read as x1 + i x2 is multiplied by e^{i pos theta_j}, with the token's grid
+    # position taken from the hand-derived golden rather than from the oracle.
+    rng = np.random.default_rng(10)
+    d = 64
+    x = rng.standard_normal((2, T * H * W, 3, d))
+    y = oracle.rope_3d(x, T, H, W)
+    pos = np.array([[r[1], r[2], r[3]] for r in rows], dtype=np.float64)   # (N, 3)
+    o = 0
+    for a, da in enumerate((16, 24, 24)):
+        half = da // 2
+        z = x[..., o:o + half] + 1j * x[..., o + half:o + da]
+        inv_freq = np.array([10000.0 ** (-(2.0 * j) / da) for j in range(half)])
+        rot = np.exp(1j * pos[:, a][:, None] * inv_freq[None, :])[None, :, None, :]
+        assert np.allclose(y[..., o:o + half], (z * rot).real, atol=1e-13)
+        assert np.allclose(y[..., o + half:o + da], (z * rot).imag, atol=1e-13)
+        o += da
+
+
 # ---------------------------------------------------------------------------
 # Attention
 # ---------------------------------------------------------------------------
