@@ -12,8 +12,6 @@ from .skiparse_oracle import (  # noqa: F401
     SINGLE,
     attention,
     attention_backward,
-    group_skip_rearrange,
-    group_skip_reverse,
     rearrange,
     reverse,
     reverse_rows,
@@ -23,8 +21,6 @@ from .skiparse_oracle import (  # noqa: F401
     rope_axis_sizes,
     rope_rearrange,
     scope_table,
-    single_skip_rearrange,
-    single_skip_reverse,
     skiparse_attention,
     skiparse_attention_backward,
     skiparse_attention_backward_scope,
@@ -32,4 +28,5 @@ from .skiparse_oracle import (  # noqa: F401
     skiparse_attention_rows,
     skiparse_flops,
     token_positions,
+    token_scope,
 )

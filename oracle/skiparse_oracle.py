@@ -13,13 +13,14 @@ Open-Sora Plan documentation, section "Skiparse Attention":
 * The attention sequence of a Full-3D-attention block is split into ``k``
   scopes; attention runs inside each scope only.  Only the attention part of
   the transformer block changes.
-* "Single Skip Mode": token ``n`` joins scope ``n mod k``; each scope holds
-  every k-th token.  The page's code is the einops pattern
-  ``'b (g k) d -> (k b) g d'`` and its inverse ``'(k b) g d -> b (g k) d'``.
-* "Group Skip Mode": adjacent tokens are grouped in runs of ``k``; group
-  ``j`` joins scope ``j mod k``.  The page's code is
-  ``'b (n m k) d -> (m b) (n k) d'`` with ``m = k = sparse_k`` and its inverse
-  ``'(m b) (n k) d -> b (n m k) d'``.
+* "Single Skip Mode": a token shares its scope with the tokens k positions
+  away from it, so token ``n`` is in scope ``n mod k``.
+* "Group Skip Mode": runs of ``k`` adjacent tokens form groups, and a group
+  shares its scope with the groups k groups away from it, so group
+  ``j = n div k`` (and each of its tokens) is in scope ``j mod k``.
+* Inside a scope the tokens keep their original order; the page's code puts
+  the scope axis in front of the batch axis of the rearranged tensor
+  (row ``s*B + b`` holds scope ``s`` of batch ``b``).
 * Implementation note: RoPE is applied to q and k *before* the rearrange,
   because the rearrange loses the original positions.
 * The forward snippet runs ``F.scaled_dot_product_attention(q, k, v)`` on the
@@ -139,80 +140,66 @@ def rope_3d_transpose_at(x, t, h, w, base: float = ROPE_BASE):
 
 
 # ---------------------------------------------------------------------------
-# Skiparse rearrange / reverse (the pages' einops patterns, written out)
+# Scope map (Open-Sora Plan documentation, "Skiparse Attention": Single Skip
+# Mode, Group Skip Mode)
 # ---------------------------------------------------------------------------
 
 SINGLE = 0
 GROUP = 1
 
 
-def single_skip_rearrange(x, k: int):
-    """(B, N, C) -> (k*B, N/k, C): pattern 'b (g k) d -> (k b) g d'.
+def token_scope(n, k: int, mode: int):
+    """Scope index of token(s) ``n`` (int64 array or int).
 
-    Split the token axis as (g, k) with k innermost, then move k in front of b.
+    Single Skip: token n is in scope n mod k.  Group Skip: token n belongs to
+    group n div k, and that group is in scope (n div k) mod k.
     """
-    B, N, C = x.shape
-    if N % k:
+    n = np.asarray(n, dtype=np.int64)
+    if mode == SINGLE:
+        return n % k
+    if mode == GROUP:
+        return (n // k) % k
+    raise ValueError("mode must be SINGLE (0) or GROUP (1)")
+
+
+def _check_divisible(N: int, k: int, mode: int):
+    # Every scope must hold the same number of tokens; Group Skip also needs whole
+    # groups in every scope (the page's code rejects other lengths).
+    if mode == SINGLE and N % k:
         raise ValueError("single skip needs N % k == 0")
-    g = N // k
-    return x.reshape(B, g, k, C).transpose(2, 0, 1, 3).reshape(k * B, g, C)
-
-
-def single_skip_reverse(x, k: int):
-    """(k*B, N/k, C) -> (B, N, C): pattern '(k b) g d -> b (g k) d'."""
-    kB, g, C = x.shape
-    B = kB // k
-    return x.reshape(k, B, g, C).transpose(1, 2, 0, 3).reshape(B, g * k, C)
-
-
-def group_skip_rearrange(x, k: int):
-    """(B, N, C) -> (k*B, N/k, C): pattern 'b (n m k) d -> (m b) (n k) d', m = k.
-
-    Split the token axis as (n, m, k) with k innermost (position inside a
-    group of k adjacent tokens) and m the group index modulo k; m becomes
-    the scope and moves in front of b; (n, k) stays as the in-scope order.
-    """
-    B, N, C = x.shape
-    if N % (k * k):
+    if mode == GROUP and N % (k * k):
         raise ValueError("group skip needs N % k**2 == 0")
-    n = N // (k * k)
-    return x.reshape(B, n, k, k, C).transpose(2, 0, 1, 3, 4).reshape(k * B, n * k, C)
-
-
-def group_skip_reverse(x, k: int):
-    """(k*B, N/k, C) -> (B, N, C): pattern '(m b) (n k) d -> b (n m k) d', m = k."""
-    kB, L, C = x.shape
-    B = kB // k
-    n = L // k
-    return x.reshape(k, B, n, k, C).transpose(1, 2, 0, 3, 4).reshape(B, n * k * k, C)
-
-
-def rearrange(x, k: int, mode: int):
-    """Skiparse rearrange of (B, N, C) in the given mode (SINGLE or GROUP)."""
-    if mode == SINGLE:
-        return single_skip_rearrange(x, k)
-    if mode == GROUP:
-        return group_skip_rearrange(x, k)
-    raise ValueError("mode must be SINGLE (0) or GROUP (1)")
-
-
-def reverse(x, k: int, mode: int):
-    """Inverse of :func:`rearrange` for the same mode."""
-    if mode == SINGLE:
-        return single_skip_reverse(x, k)
-    if mode == GROUP:
-        return group_skip_reverse(x, k)
-    raise ValueError("mode must be SINGLE (0) or GROUP (1)")
 
 
 def scope_table(N: int, k: int, mode: int):
-    """int64 (k, N/k): entry [s, p] is the token index placed at position p of scope s.
+    """int64 (k, N/k): row s lists the tokens of scope s in their original order.
 
-    Obtained by applying :func:`rearrange` to the token indices themselves,
-    so it is the same permutation the data goes through.
+    Entry [s, p] is the token at in-scope position p of scope s.
     """
-    idx = np.arange(N, dtype=np.int64).reshape(1, N, 1)
-    return rearrange(idx, k, mode)[:, :, 0]
+    _check_divisible(N, k, mode)
+    n = np.arange(N, dtype=np.int64)
+    s = token_scope(n, k, mode)
+    return np.stack([n[s == i] for i in range(k)])
+
+
+def rearrange(x, k: int, mode: int):
+    """(B, N, C) -> (k*B, N/k, C): row s*B + b, position p holds x[b, table[s, p]]."""
+    x = np.asarray(x)
+    B, N, C = x.shape
+    table = scope_table(N, k, mode)                 # (k, L)
+    gathered = x[:, table, :]                       # (B, k, L, C)
+    return np.ascontiguousarray(gathered.transpose(1, 0, 2, 3)).reshape(k * B, N // k, C)
+
+
+def reverse(x, k: int, mode: int):
+    """Inverse of :func:`rearrange`: (k*B, N/k, C) -> (B, N, C), each row back to its token."""
+    x = np.asarray(x)
+    kB, L, C = x.shape
+    B, N = kB // k, L * k
+    table = scope_table(N, k, mode)
+    out = np.empty((B, N, C), dtype=x.dtype)
+    out[:, table, :] = x.reshape(k, B, L, C).transpose(1, 0, 2, 3)
+    return out
 
 
 # ---------------------------------------------------------------------------
@@ -274,8 +261,8 @@ def attention_backward(q, k, v, do):
 def rope_rearrange(x, T, H, W, sparse_k, mode, apply_rope=True, base=ROPE_BASE):
     """(B, N, heads, d) -> (k*B, N/k, heads, d): optional 3D RoPE, then the Skiparse rearrange.
 
-    Row s*B + b of the result holds scope s of batch b (the '(k b)' / '(m b)'
-    batch order of the page's patterns).
+    Row s*B + b of the result holds scope s of batch b, its tokens in their
+    original order (the layout of the page's rearranged tensors).
     """
     x = np.asarray(x, dtype=np.float64)
     B, N, heads, d = x.shape
@@ -295,21 +282,25 @@ def reverse_rows(x, sparse_k, mode):
 def skiparse_attention(q, k, v, T, H, W, sparse_k, mode, base=ROPE_BASE):
     """Skiparse attention forward, float64.  q, k, v: (B, N, heads, d) with N = T*H*W.
 
-    Steps in the page's order: RoPE on q and k; rearrange q, k, v into
-    (k*B, N/k, ...); softmax attention per rearranged batch row and head;
-    reverse back to (B, N, heads, d).  With sparse_k == 1 this is dense
-    full-3D attention.
+    RoPE on q and k at every token's own grid position (the implementation
+    note: before the tokens are regrouped); then, for every batch, head and
+    scope, softmax attention of the scope's queries over the scope's keys and
+    values; each output row lands on the token its query came from.  With
+    sparse_k == 1 there is one scope and this is dense full-3D attention.
     """
     q = np.asarray(q, dtype=np.float64)
     B, N, heads, d = q.shape
     if N != T * H * W:
         raise ValueError("N must equal T*H*W")
-    rq = rope_rearrange(q, T, H, W, sparse_k, mode, True, base)
-    rk = rope_rearrange(k, T, H, W, sparse_k, mode, True, base)
-    rv = rope_rearrange(v, T, H, W, sparse_k, mode, False, base)
-    # (kB, L, heads, d) -> (kB, heads, L, d): one attention problem per (row, head)
-    o = attention(rq.transpose(0, 2, 1, 3), rk.transpose(0, 2, 1, 3), rv.transpose(0, 2, 1, 3))
-    return reverse_rows(o.transpose(0, 2, 1, 3), sparse_k, mode)
+    rq = rope_3d(q, T, H, W, base)
+    rk = rope_3d(np.asarray(k, dtype=np.float64), T, H, W, base)
+    v = np.asarray(v, dtype=np.float64)
+    out = np.empty_like(rq)
+    for members in scope_table(N, sparse_k, mode):
+        # (B, L, heads, d) -> (B, heads, L, d): one attention problem per (batch, head)
+        tr = lambda x: x[:, members].transpose(0, 2, 1, 3)
+        out[:, members] = attention(tr(rq), tr(rk), tr(v)).transpose(0, 2, 1, 3)
+    return out
 
 
 def skiparse_attention_rows(q, k, v, T, H, W, sparse_k, mode, batch_idx, token_idx,
@@ -351,27 +342,28 @@ def skiparse_attention_rows(q, k, v, T, H, W, sparse_k, mode, batch_idx, token_i
 def skiparse_attention_backward(q, k, v, do, T, H, W, sparse_k, mode, base=ROPE_BASE):
     """Gradients (dq, dk, dv) of sum(skiparse_attention(q, k, v) * do), float64.
 
-    All arrays (B, N, heads, d).  The forward's steps taken backwards:
-    the output gradient ``do`` goes through the same rearrange as v (the
-    reverse's adjoint is the forward rearrange, since the permutation is a
-    bijection); softmax attention is differentiated per rearranged batch row
-    and head (:func:`attention_backward`); the gradients are reversed to the
-    original token order; the q and k gradients are rotated back by the
-    transposed RoPE (:func:`rope_3d_transpose_at`).
+    All arrays (B, N, heads, d).  The forward's steps taken backwards: the
+    output gradient of a token belongs to the scope its query is in; softmax
+    attention is differentiated per batch, head and scope
+    (:func:`attention_backward`), each gradient row landing on its own token
+    (no token is in two scopes); the q and k gradients are then rotated back
+    by the transposed RoPE (:func:`rope_3d_transpose_at`).
     """
     q = np.asarray(q, dtype=np.float64)
     B, N, heads, d = q.shape
     if N != T * H * W:
         raise ValueError("N must equal T*H*W")
-    rq = rope_rearrange(q, T, H, W, sparse_k, mode, True, base)
-    rk = rope_rearrange(k, T, H, W, sparse_k, mode, True, base)
-    rv = rope_rearrange(v, T, H, W, sparse_k, mode, False, base)
-    rdo = rope_rearrange(do, T, H, W, sparse_k, mode, False, base)
-    tr = lambda x: x.transpose(0, 2, 1, 3)
-    dq, dk, dv = attention_backward(tr(rq), tr(rk), tr(rv), tr(rdo))
-    dq = reverse_rows(tr(dq), sparse_k, mode)
-    dk = reverse_rows(tr(dk), sparse_k, mode)
-    dv = reverse_rows(tr(dv), sparse_k, mode)
+    rq = rope_3d(q, T, H, W, base)
+    rk = rope_3d(np.asarray(k, dtype=np.float64), T, H, W, base)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    dq, dk, dv = np.empty_like(rq), np.empty_like(rq), np.empty_like(rq)
+    for members in scope_table(N, sparse_k, mode):
+        tr = lambda x: x[:, members].transpose(0, 2, 1, 3)
+        gq, gk, gv = attention_backward(tr(rq), tr(rk), tr(v), tr(do))
+        dq[:, members] = gq.transpose(0, 2, 1, 3)
+        dk[:, members] = gk.transpose(0, 2, 1, 3)
+        dv[:, members] = gv.transpose(0, 2, 1, 3)
     t, h, w = token_positions(T, H, W)
     return rope_3d_transpose_at(dq, t, h, w, base), rope_3d_transpose_at(dk, t, h, w, base), dv
 

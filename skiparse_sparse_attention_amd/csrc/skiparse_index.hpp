@@ -1,12 +1,12 @@
 // Index arithmetic of the Skiparse permutation and of the 3D-RoPE layout,
 // shared by the host API and the HIP kernels.
 //
-// Scopes (Open-Sora Plan documentation, "Skiparse Attention"):
-//   Single Skip: token n is in scope n mod k; the page's pattern
-//     'b (g k) d -> (k b) g d' makes its in-scope position n div k.
-//   Group Skip: adjacent tokens form groups of k and group j is in scope
-//     j mod k; the page's pattern 'b (n m k) d -> (m b) (n k) d' (m = k) makes
-//     the in-scope position (n div k^2)*k + n mod k.
+// Scopes (Open-Sora Plan documentation, "Skiparse Attention", Single Skip Mode
+// and Group Skip Mode); inside a scope the tokens keep their original order:
+//   Single Skip: token n is in scope n mod k, at in-scope position n div k.
+//   Group Skip: adjacent tokens form groups of k and group j = n div k is in
+//     scope j mod k; token n sits at in-scope position (n div k^2)*k + n mod k
+//     (the scope's earlier whole groups, then its offset inside its own group).
 // Positions (Wan 2.1 report, section 4.2.1): n = (t*H + h)*W + w.
 // RoPE split: head_dim is divided 2:3:3 over t, h, w; every axis chunk is a
 //   whole number of the 16 equal "RoPE chunks" of head_dim/16 elements, so the
