@@ -113,13 +113,13 @@ def _check(status: int, where: str):
         raise SkiparseError(status, where)
 
 
-def _dtype_code(t):
+def _dtype_code(dtype):
     import torch
-    if t.dtype == torch.bfloat16:
+    if dtype == torch.bfloat16:
         return BF16
-    if t.dtype == torch.float32:
+    if dtype == torch.float32:
         return FP32
-    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+    raise ValueError(f"unsupported dtype {dtype} (bfloat16 or float32)")
 
 
 def _stream_ptr(stream):
@@ -128,29 +128,72 @@ def _stream_ptr(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def _dims(x, grid):
-    if x.dim() != 4:
-        raise ValueError("expected a (B, N, heads, head_dim) tensor")
-    if not x.is_contiguous():
-        raise ValueError("expected a contiguous tensor")
+def _grid(grid):
     T, H, W = (int(g) for g in grid)
-    B, N, heads, d = x.shape
+    return T, H, W
+
+
+def _sparse_k(sparse_k):
+    k = int(sparse_k)
+    if k < 1:
+        raise ValueError(f"sparse_k must be >= 1 (got {k})")
+    return k
+
+
+def _lead_dims(x, grid, name):
+    """(B, T, H, W, heads, d) of the call's first (B, N, heads, head_dim) operand."""
+    import torch
+    if not isinstance(x, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor")
+    if x.dim() != 4:
+        raise ValueError(f"{name} must be a (B, N, heads, head_dim) tensor")
+    T, H, W = _grid(grid)
+    B, N, heads, d = (int(e) for e in x.shape)
     if N != T * H * W:
-        raise ValueError(f"N={N} does not match the grid {T}x{H}x{W}")
+        raise ValueError(f"{name}: N={N} does not match the grid {T}x{H}x{W}")
     return B, T, H, W, heads, d
+
+
+def _validate(specs):
+    """Check every tensor a call hands to the library: (tensor, name, shape, dtype) each.
+
+    The library takes raw device pointers and cannot check them, so anything else (a host
+    tensor, a tensor on another GPU, a short, mistyped or strided buffer) is rejected here
+    with ValueError before the library is called.  Shapes, dtypes and contiguity are checked
+    for all tensors first, then that all of them live on the same GPU.
+    """
+    import torch
+    for t, name, shape, dtype in specs:
+        if not isinstance(t, torch.Tensor):
+            raise ValueError(f"{name} must be a torch.Tensor")
+        if tuple(t.shape) != tuple(int(e) for e in shape):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+        if t.dtype != dtype:
+            raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    device = specs[0][0].device
+    for t, name, _, _ in specs:
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor (it is on {t.device})")
+        if t.device != device:
+            raise ValueError(f"{name} is on {t.device}, the call's first operand on {device}")
+
+
+def _alloc(t, shape, dtype, like):
+    import torch
+    return t if t is not None else torch.empty(tuple(shape), dtype=dtype, device=like.device)
 
 
 def attn(q, k, v, grid, sparse_k, mode, out=None, stream=None):
     """Fused Skiparse attention: q, k, v (B, N, heads, d) on the GPU -> out, same shape/dtype."""
-    import torch
-    B, T, H, W, heads, d = _dims(q, grid)
-    for t in (k, v):
-        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
-            raise ValueError("q, k, v must share shape, dtype and be contiguous")
-    if out is None:
-        out = torch.empty_like(q)
+    B, T, H, W, heads, d = _lead_dims(q, grid, "q")
+    code = _dtype_code(q.dtype)
+    out = _alloc(out, q.shape, q.dtype, q)
+    _validate([(q, "q", q.shape, q.dtype), (k, "k", q.shape, q.dtype), (v, "v", q.shape, q.dtype),
+               (out, "out", q.shape, q.dtype)])
     _check(lib().skiparse_attn(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, T, H, W, heads, d,
-                               int(sparse_k), int(mode), _dtype_code(q), out.data_ptr(),
+                               int(sparse_k), int(mode), code, out.data_ptr(),
                                _stream_ptr(stream)), "skiparse_attn")
     return out
 
@@ -158,70 +201,79 @@ def attn(q, k, v, grid, sparse_k, mode, out=None, stream=None):
 def rope_qk(q, k, grid, outs=None, stream=None):
     """3D RoPE of q and k once (bf16, head_dim 128): returns (qr, kr), qr with the softmax
     scale log2(e)/sqrt(d) folded in -- the operands of attn_rotated."""
-    import torch
-    B, T, H, W, heads, d = _dims(q, grid)
-    if k.shape != q.shape or k.dtype != q.dtype or not k.is_contiguous():
-        raise ValueError("q, k must share shape, dtype and be contiguous")
-    qr, kr = outs if outs is not None else (torch.empty_like(q), torch.empty_like(k))
-    for t in (qr, kr):
-        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
-            raise ValueError("qr, kr must match q's shape and dtype and be contiguous")
-    _check(lib().skiparse_rope_qk(q.data_ptr(), k.data_ptr(), B, T, H, W, heads, d, _dtype_code(q),
+    B, T, H, W, heads, d = _lead_dims(q, grid, "q")
+    code = _dtype_code(q.dtype)
+    qr, kr = outs if outs is not None else (None, None)
+    qr, kr = _alloc(qr, q.shape, q.dtype, q), _alloc(kr, q.shape, q.dtype, q)
+    _validate([(q, "q", q.shape, q.dtype), (k, "k", q.shape, q.dtype),
+               (qr, "qr", q.shape, q.dtype), (kr, "kr", q.shape, q.dtype)])
+    _check(lib().skiparse_rope_qk(q.data_ptr(), k.data_ptr(), B, T, H, W, heads, d, code,
                                   qr.data_ptr(), kr.data_ptr(), _stream_ptr(stream)), "skiparse_rope_qk")
     return qr, kr
 
 
 def attn_rotated(qr, kr, v, grid, sparse_k, mode, out=None, stream=None):
     """Skiparse attention on rope_qk's outputs; equals attn(q, k, v, ...) bit for bit."""
-    import torch
-    B, T, H, W, heads, d = _dims(qr, grid)
-    for t in (kr, v):
-        if t.shape != qr.shape or t.dtype != qr.dtype or not t.is_contiguous():
-            raise ValueError("qr, kr, v must share shape, dtype and be contiguous")
-    if out is None:
-        out = torch.empty_like(v)
+    B, T, H, W, heads, d = _lead_dims(qr, grid, "qr")
+    code = _dtype_code(qr.dtype)
+    out = _alloc(out, qr.shape, qr.dtype, qr)
+    _validate([(qr, "qr", qr.shape, qr.dtype), (kr, "kr", qr.shape, qr.dtype),
+               (v, "v", qr.shape, qr.dtype), (out, "out", qr.shape, qr.dtype)])
     _check(lib().skiparse_attn_rotated(qr.data_ptr(), kr.data_ptr(), v.data_ptr(), B, T, H, W, heads, d,
-                                       int(sparse_k), int(mode), _dtype_code(qr), out.data_ptr(),
+                                       int(sparse_k), int(mode), code, out.data_ptr(),
                                        _stream_ptr(stream)), "skiparse_attn_rotated")
     return out
+
+
+def _lse_shape(B, heads, T, H, W):
+    return (B, heads, T * H * W)
 
 
 def attn_rotated_lse(qr, kr, v, grid, sparse_k, mode, out=None, lse=None, stream=None):
     """attn_rotated that also returns each row's log2-sum-exp (B, heads, N) fp32; equals
     attn_lse(q, k, v, ...) bit for bit."""
     import torch
-    B, T, H, W, heads, d = _dims(qr, grid)
-    for t in (kr, v):
-        if t.shape != qr.shape or t.dtype != qr.dtype or not t.is_contiguous():
-            raise ValueError("qr, kr, v must share shape, dtype and be contiguous")
-    if out is None:
-        out = torch.empty_like(v)
-    if lse is None:
-        lse = torch.empty((B, heads, T * H * W), dtype=torch.float32, device=v.device)
+    B, T, H, W, heads, d = _lead_dims(qr, grid, "qr")
+    code = _dtype_code(qr.dtype)
+    ls = _lse_shape(B, heads, T, H, W)
+    out = _alloc(out, qr.shape, qr.dtype, qr)
+    lse = _alloc(lse, ls, torch.float32, qr)
+    _validate([(qr, "qr", qr.shape, qr.dtype), (kr, "kr", qr.shape, qr.dtype),
+               (v, "v", qr.shape, qr.dtype), (out, "out", qr.shape, qr.dtype),
+               (lse, "lse", ls, torch.float32)])
     _check(lib().skiparse_attn_rotated_lse(qr.data_ptr(), kr.data_ptr(), v.data_ptr(), B, T, H, W, heads, d,
-                                           int(sparse_k), int(mode), _dtype_code(qr), out.data_ptr(),
+                                           int(sparse_k), int(mode), code, out.data_ptr(),
                                            lse.data_ptr(), _stream_ptr(stream)), "skiparse_attn_rotated_lse")
     return out, lse
+
+
+def _bwd_args(q, k, v, out, dout, lse, grid, grads, delta, names):
+    import torch
+    B, T, H, W, heads, d = _lead_dims(q, grid, names[0])
+    code = _dtype_code(q.dtype)
+    ls = _lse_shape(B, heads, T, H, W)
+    if grads is None:
+        grads = (None, None, None)
+    if len(grads) != 3:
+        raise ValueError("grads must be a (dq, dk, dv) triple")
+    dq, dk, dv = (_alloc(g, q.shape, q.dtype, q) for g in grads)
+    delta = _alloc(delta, ls, torch.float32, q)
+    specs = [(t, n, q.shape, q.dtype) for t, n in zip((q, k, v, out, dout), names)]
+    specs += [(lse, "lse", ls, torch.float32), (dq, "dq", q.shape, q.dtype),
+              (dk, "dk", q.shape, q.dtype), (dv, "dv", q.shape, q.dtype),
+              (delta, "delta", ls, torch.float32)]
+    _validate(specs)
+    return (B, T, H, W, heads, d), code, (dq, dk, dv), delta
 
 
 def attn_bwd_rotated(qr, kr, v, out, dout, lse, grid, sparse_k, mode, grads=None, delta=None, stream=None):
     """attn_bwd on rope_qk's outputs: (dq, dk, dv) with respect to the unrotated q, k and v;
     equals attn_bwd(q, k, v, ...) bit for bit."""
-    import torch
-    B, T, H, W, heads, d = _dims(qr, grid)
-    for t in (kr, v, out, dout):
-        if t.shape != qr.shape or t.dtype != qr.dtype or not t.is_contiguous():
-            raise ValueError("qr, kr, v, out, dout must share shape, dtype and be contiguous")
-    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, heads, T * H * W) or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous (B, heads, N) float32 tensor")
-    if grads is None:
-        grads = tuple(torch.empty_like(v) for _ in range(3))
-    if delta is None:
-        delta = torch.empty((B, heads, T * H * W), dtype=torch.float32, device=v.device)
-    dq, dk, dv = grads
+    dims, code, (dq, dk, dv), delta = _bwd_args(qr, kr, v, out, dout, lse, grid, grads, delta,
+                                                ("qr", "kr", "v", "out", "dout"))
     _check(lib().skiparse_attn_bwd_rotated(qr.data_ptr(), kr.data_ptr(), v.data_ptr(), out.data_ptr(),
-                                           dout.data_ptr(), lse.data_ptr(), B, T, H, W, heads, d,
-                                           int(sparse_k), int(mode), _dtype_code(qr), dq.data_ptr(),
+                                           dout.data_ptr(), lse.data_ptr(), *dims,
+                                           int(sparse_k), int(mode), code, dq.data_ptr(),
                                            dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
                                            _stream_ptr(stream)), "skiparse_attn_bwd_rotated")
     return dq, dk, dv
@@ -238,20 +290,34 @@ def u_schedule(n_layers, k_max, modes=(SINGLE, GROUP)):
     return out
 
 
-def attn_schedule(layers, grid, stream=None):
-    """Run a schedule: `layers` is a list of (q, k, v, out, sparse_k, mode); all layers share
-    shape and dtype.  One validation pass, then one launch per layer on one stream."""
+def _schedule_specs(layers, grid):
     if not layers:
         raise ValueError("empty schedule")
     q0 = layers[0][0]
-    B, T, H, W, heads, d = _dims(q0, grid)
+    B, T, H, W, heads, d = _lead_dims(q0, grid, "layer 0 q")
+    code = _dtype_code(q0.dtype)
+    specs = []
+    for i, layer in enumerate(layers):
+        if len(layer) != 6:
+            raise ValueError(f"layer {i} must be (q, k, v, out, sparse_k, mode)")
+        for t, n in zip(layer[:4], ("q", "k", "v", "out")):
+            specs.append((t, f"layer {i} {n}", q0.shape, q0.dtype))
+    return specs, (B, T, H, W, heads, d), code, q0
+
+
+def _schedule_array(layers):
     arr = (Layer * len(layers))()
     for i, (q, k, v, out, sk_, mode) in enumerate(layers):
-        for t in (q, k, v, out):
-            if t.shape != q0.shape or t.dtype != q0.dtype or not t.is_contiguous():
-                raise ValueError("every layer's q, k, v, out must share shape, dtype and be contiguous")
         arr[i] = Layer(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), int(sk_), int(mode))
-    _check(lib().skiparse_attn_schedule(arr, len(layers), B, T, H, W, heads, d, _dtype_code(q0),
+    return arr
+
+
+def attn_schedule(layers, grid, stream=None):
+    """Run a schedule: `layers` is a list of (q, k, v, out, sparse_k, mode); all layers share
+    shape and dtype.  One validation pass, then one launch per layer on one stream."""
+    specs, dims, code, _ = _schedule_specs(layers, grid)
+    _validate(specs)
+    _check(lib().skiparse_attn_schedule(_schedule_array(layers), len(layers), *dims, code,
                                         _stream_ptr(stream)), "skiparse_attn_schedule")
     return [layer[3] for layer in layers]
 
@@ -260,22 +326,11 @@ def attn_schedule_rotated(layers, grid, scratch=None, stream=None):
     """attn_schedule with every layer run as the RoPE pass into `scratch` (qr, kr: two tensors
     shaped like q, reused by all layers) and the attention on the rotated operands; equals
     attn_schedule bit for bit (head_dim 128, bf16, every sparse_k dividing 64)."""
-    import torch
-    if not layers:
-        raise ValueError("empty schedule")
-    q0 = layers[0][0]
-    B, T, H, W, heads, d = _dims(q0, grid)
-    arr = (Layer * len(layers))()
-    for i, (q, k, v, out, sk_, mode) in enumerate(layers):
-        for t in (q, k, v, out):
-            if t.shape != q0.shape or t.dtype != q0.dtype or not t.is_contiguous():
-                raise ValueError("every layer's q, k, v, out must share shape, dtype and be contiguous")
-        arr[i] = Layer(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), int(sk_), int(mode))
-    qr, kr = scratch if scratch is not None else (torch.empty_like(q0), torch.empty_like(q0))
-    for t in (qr, kr):
-        if t.shape != q0.shape or t.dtype != q0.dtype or not t.is_contiguous():
-            raise ValueError("scratch tensors must match the layers' shape and dtype and be contiguous")
-    _check(lib().skiparse_attn_schedule_rotated(arr, len(layers), B, T, H, W, heads, d, _dtype_code(q0),
+    specs, dims, code, q0 = _schedule_specs(layers, grid)
+    qr, kr = scratch if scratch is not None else (None, None)
+    qr, kr = _alloc(qr, q0.shape, q0.dtype, q0), _alloc(kr, q0.shape, q0.dtype, q0)
+    _validate(specs + [(qr, "scratch qr", q0.shape, q0.dtype), (kr, "scratch kr", q0.shape, q0.dtype)])
+    _check(lib().skiparse_attn_schedule_rotated(_schedule_array(layers), len(layers), *dims, code,
                                                 qr.data_ptr(), kr.data_ptr(), _stream_ptr(stream)),
            "skiparse_attn_schedule_rotated")
     return [layer[3] for layer in layers]
@@ -284,16 +339,15 @@ def attn_schedule_rotated(layers, grid, scratch=None, stream=None):
 def attn_lse(q, k, v, grid, sparse_k, mode, out=None, lse=None, stream=None):
     """Fused Skiparse attention that also returns each row's log2-sum-exp (B, heads, N) fp32."""
     import torch
-    B, T, H, W, heads, d = _dims(q, grid)
-    for t in (k, v):
-        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
-            raise ValueError("q, k, v must share shape, dtype and be contiguous")
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, heads, T * H * W), dtype=torch.float32, device=q.device)
+    B, T, H, W, heads, d = _lead_dims(q, grid, "q")
+    code = _dtype_code(q.dtype)
+    ls = _lse_shape(B, heads, T, H, W)
+    out = _alloc(out, q.shape, q.dtype, q)
+    lse = _alloc(lse, ls, torch.float32, q)
+    _validate([(q, "q", q.shape, q.dtype), (k, "k", q.shape, q.dtype), (v, "v", q.shape, q.dtype),
+               (out, "out", q.shape, q.dtype), (lse, "lse", ls, torch.float32)])
     _check(lib().skiparse_attn_lse(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, T, H, W, heads, d,
-                                   int(sparse_k), int(mode), _dtype_code(q), out.data_ptr(),
+                                   int(sparse_k), int(mode), code, out.data_ptr(),
                                    lse.data_ptr(), _stream_ptr(stream)), "skiparse_attn_lse")
     return out, lse
 
@@ -304,28 +358,18 @@ def attn_bwd(q, k, v, out, dout, lse, grid, sparse_k, mode, grads=None, delta=No
     ``out`` and ``lse`` come from :func:`attn_lse` on the same inputs; ``delta`` is an
     optional (B, heads, N) fp32 workspace.
     """
-    import torch
-    B, T, H, W, heads, d = _dims(q, grid)
-    for t in (k, v, out, dout):
-        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
-            raise ValueError("q, k, v, out, dout must share shape, dtype and be contiguous")
-    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, heads, T * H * W) or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous (B, heads, N) float32 tensor")
-    if grads is None:
-        grads = tuple(torch.empty_like(q) for _ in range(3))
-    if delta is None:
-        delta = torch.empty((B, heads, T * H * W), dtype=torch.float32, device=q.device)
-    dq, dk, dv = grads
+    dims, code, (dq, dk, dv), delta = _bwd_args(q, k, v, out, dout, lse, grid, grads, delta,
+                                                ("q", "k", "v", "out", "dout"))
     _check(lib().skiparse_attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                                   dout.data_ptr(), lse.data_ptr(), B, T, H, W, heads, d,
-                                   int(sparse_k), int(mode), _dtype_code(q), dq.data_ptr(),
+                                   dout.data_ptr(), lse.data_ptr(), *dims,
+                                   int(sparse_k), int(mode), code, dq.data_ptr(),
                                    dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
                                    _stream_ptr(stream)), "skiparse_attn_bwd")
     return dq, dk, dv
 
 
 def attn_bwd_flops(B, grid, heads, head_dim, sparse_k):
-    T, H, W = (int(g) for g in grid)
+    T, H, W = _grid(grid)
     return float(lib().skiparse_attn_bwd_flops(int(B), T, H, W, int(heads), int(head_dim), int(sparse_k)))
 
 
@@ -334,33 +378,37 @@ Q8_KEYS = ("q8", "q_amax", "k8", "k_amax", "vt8", "v_amax")
 
 def q8_scope_pitch(grid, sparse_k):
     """Lp: the channel-row pitch (keys) of vt8, L rounded up to a multiple of 64."""
-    T, H, W = (int(g) for g in grid)
+    T, H, W = _grid(grid)
     lp = lib().skiparse_q8_scope_pitch(T, H, W, int(sparse_k))
     if lp < 0:
         raise SkiparseError(-lp, "skiparse_q8_scope_pitch")
     return lp
 
 
+def _q8_specs(B, N, heads, d, grid, sparse_k):
+    import torch
+    lp = q8_scope_pitch(grid, sparse_k)
+    return {"q8": ((B, N, heads, d), torch.int8), "q_amax": ((B, N, heads), torch.float32),
+            "k8": ((B, N, heads, d), torch.int8), "k_amax": ((B, heads), torch.float32),
+            "vt8": ((B, heads, _sparse_k(sparse_k), d, lp), torch.uint8),
+            "v_amax": ((B, heads, d), torch.float32)}
+
+
 def quant8(q, k, v, grid, sparse_k, mode, outs=None, stream=None):
     """8-bit operands of q, k, v for :func:`attn8`: a dict with q8 (int8), q_amax, k8 (int8),
     k_amax, vt8 (uint8 E4M3 codes) and v_amax (float32), in the layouts of include/skiparse.h."""
-    import torch
-    B, T, H, W, heads, d = _dims(q, grid)
-    for t in (k, v):
-        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
-            raise ValueError("q, k, v must share shape, dtype and be contiguous")
-    N = T * H * W
+    B, T, H, W, heads, d = _lead_dims(q, grid, "q")
+    code = _dtype_code(q.dtype)
+    specs = _q8_specs(B, T * H * W, heads, d, grid, sparse_k)
     if outs is None:
-        lp = q8_scope_pitch(grid, sparse_k)
-        dev = q.device
-        outs = {"q8": torch.empty((B, N, heads, d), dtype=torch.int8, device=dev),
-                "q_amax": torch.empty((B, N, heads), dtype=torch.float32, device=dev),
-                "k8": torch.empty((B, N, heads, d), dtype=torch.int8, device=dev),
-                "k_amax": torch.empty((B, heads), dtype=torch.float32, device=dev),
-                "vt8": torch.empty((B, heads, int(sparse_k), d, lp), dtype=torch.uint8, device=dev),
-                "v_amax": torch.empty((B, heads, d), dtype=torch.float32, device=dev)}
+        outs = {key: _alloc(None, shape, dt, q) for key, (shape, dt) in specs.items()}
+    missing = [key for key in Q8_KEYS if key not in outs]
+    if missing:
+        raise ValueError(f"outs lacks {missing}")
+    _validate([(q, "q", q.shape, q.dtype), (k, "k", q.shape, q.dtype), (v, "v", q.shape, q.dtype)]
+              + [(outs[key], key, *specs[key]) for key in Q8_KEYS])
     _check(lib().skiparse_quant8(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, T, H, W, heads, d,
-                                 int(sparse_k), int(mode), _dtype_code(q),
+                                 int(sparse_k), int(mode), code,
                                  *(outs[key].data_ptr() for key in Q8_KEYS), _stream_ptr(stream)),
            "skiparse_quant8")
     return outs
@@ -369,29 +417,44 @@ def quant8(q, k, v, grid, sparse_k, mode, outs=None, stream=None):
 def attn8(qz, grid, sparse_k, mode, out_dtype=None, out=None, stream=None):
     """8-bit Skiparse attention of :func:`quant8`'s operands -> (B, N, heads, d) bf16 (or fp32)."""
     import torch
+    missing = [key for key in Q8_KEYS if key not in qz]
+    if missing:
+        raise ValueError(f"qz lacks {missing}")
     q8 = qz["q8"]
-    B, T, H, W, heads, d = _dims(q8, grid)
-    for key in Q8_KEYS:
-        if not qz[key].is_contiguous():
-            raise ValueError(f"{key} must be contiguous")
+    B, T, H, W, heads, d = _lead_dims(q8, grid, "q8")
+    specs = _q8_specs(B, T * H * W, heads, d, grid, sparse_k)
     if out is None:
-        out = torch.empty(q8.shape, dtype=out_dtype or torch.bfloat16, device=q8.device)
+        out = _alloc(None, q8.shape, out_dtype or torch.bfloat16, q8)
+    code = _dtype_code(out.dtype)
+    _validate([(qz[key], key, *specs[key]) for key in Q8_KEYS] + [(out, "out", q8.shape, out.dtype)])
     _check(lib().skiparse_attn8(*(qz[key].data_ptr() for key in Q8_KEYS), B, T, H, W, heads, d,
-                                int(sparse_k), int(mode), _dtype_code(out), out.data_ptr(),
+                                int(sparse_k), int(mode), code, out.data_ptr(),
                                 _stream_ptr(stream)), "skiparse_attn8")
     return out
 
 
+def _rearranged_shape(B, T, H, W, heads, d, sparse_k):
+    k = _sparse_k(sparse_k)
+    N = T * H * W
+    if N % k:
+        raise ValueError(f"N={N} is not divisible by sparse_k={k}")
+    return (k * B, N // k, heads, d)
+
+
 def rope_remap(q, k, v, grid, sparse_k, mode, outs=None, stream=None):
     """RoPE(q), RoPE(k), v rearranged to (k*B, N/k, heads, d); returns (rq, rk, rv)."""
-    import torch
-    B, T, H, W, heads, d = _dims(q, grid)
-    shape = (sparse_k * B, (T * H * W) // sparse_k, heads, d)
+    B, T, H, W, heads, d = _lead_dims(q, grid, "q")
+    code = _dtype_code(q.dtype)
+    shape = _rearranged_shape(B, T, H, W, heads, d, sparse_k)
     if outs is None:
-        outs = tuple(torch.empty(shape, dtype=q.dtype, device=q.device) for _ in range(3))
-    rq, rk, rv = outs
+        outs = (None, None, None)
+    if len(outs) != 3:
+        raise ValueError("outs must be an (rq, rk, rv) triple")
+    rq, rk, rv = (_alloc(o, shape, q.dtype, q) for o in outs)
+    _validate([(q, "q", q.shape, q.dtype), (k, "k", q.shape, q.dtype), (v, "v", q.shape, q.dtype),
+               (rq, "rq", shape, q.dtype), (rk, "rk", shape, q.dtype), (rv, "rv", shape, q.dtype)])
     _check(lib().skiparse_rope_remap(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, T, H, W, heads, d,
-                                     int(sparse_k), int(mode), _dtype_code(q), rq.data_ptr(),
+                                     int(sparse_k), int(mode), code, rq.data_ptr(),
                                      rk.data_ptr(), rv.data_ptr(), _stream_ptr(stream)),
            "skiparse_rope_remap")
     return rq, rk, rv
@@ -399,12 +462,13 @@ def rope_remap(q, k, v, grid, sparse_k, mode, outs=None, stream=None):
 
 def rearrange(x, grid, sparse_k, mode, apply_rope=False, out=None, stream=None):
     """One tensor (B, N, heads, d) -> (k*B, N/k, heads, d), optionally rotated by 3D RoPE."""
-    import torch
-    B, T, H, W, heads, d = _dims(x, grid)
-    if out is None:
-        out = torch.empty((sparse_k * B, (T * H * W) // sparse_k, heads, d), dtype=x.dtype, device=x.device)
+    B, T, H, W, heads, d = _lead_dims(x, grid, "x")
+    code = _dtype_code(x.dtype)
+    shape = _rearranged_shape(B, T, H, W, heads, d, sparse_k)
+    out = _alloc(out, shape, x.dtype, x)
+    _validate([(x, "x", x.shape, x.dtype), (out, "out", shape, x.dtype)])
     _check(lib().skiparse_rearrange(x.data_ptr(), B, T, H, W, heads, d, int(sparse_k), int(mode),
-                                    _dtype_code(x), int(bool(apply_rope)), out.data_ptr(),
+                                    code, int(bool(apply_rope)), out.data_ptr(),
                                     _stream_ptr(stream)), "skiparse_rearrange")
     return out
 
@@ -412,13 +476,20 @@ def rearrange(x, grid, sparse_k, mode, apply_rope=False, out=None, stream=None):
 def reverse(x, grid, sparse_k, mode, out=None, stream=None):
     """(k*B, N/k, heads, d) -> (B, N, heads, d), the inverse of :func:`rearrange`."""
     import torch
-    T, H, W = (int(g) for g in grid)
-    kB, L, heads, d = x.shape
-    B = kB // sparse_k
-    if out is None:
-        out = torch.empty((B, T * H * W, heads, d), dtype=x.dtype, device=x.device)
-    _check(lib().skiparse_reverse(x.data_ptr(), B, T, H, W, heads, d, int(sparse_k), int(mode),
-                                  _dtype_code(x), out.data_ptr(), _stream_ptr(stream)),
+    if not isinstance(x, torch.Tensor) or x.dim() != 4:
+        raise ValueError("x must be a (k*B, N/k, heads, head_dim) tensor")
+    T, H, W = _grid(grid)
+    k = _sparse_k(sparse_k)
+    kB, L, heads, d = (int(e) for e in x.shape)
+    if kB % k or L * k != T * H * W:
+        raise ValueError(f"x of shape {tuple(x.shape)} is not a sparse_k={k} rearrangement of the "
+                         f"grid {T}x{H}x{W}")
+    B = kB // k
+    code = _dtype_code(x.dtype)
+    out = _alloc(out, (B, T * H * W, heads, d), x.dtype, x)
+    _validate([(x, "x", x.shape, x.dtype), (out, "out", (B, T * H * W, heads, d), x.dtype)])
+    _check(lib().skiparse_reverse(x.data_ptr(), B, T, H, W, heads, d, k, int(mode),
+                                  code, out.data_ptr(), _stream_ptr(stream)),
            "skiparse_reverse")
     return out
 
