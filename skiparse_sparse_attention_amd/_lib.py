@@ -12,7 +12,9 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libskiparse_amd.so")
+# SKIPARSE_AMD_LIB names another build of the same library (the host-sanitizer build of the
+# CPU tests); by default the in-tree build is loaded.
+LIB_PATH = os.environ.get("SKIPARSE_AMD_LIB") or os.path.join(HERE, "libskiparse_amd.so")
 
 SINGLE = 0
 GROUP = 1
