@@ -50,6 +50,8 @@ def parse_args():
     ap.add_argument("--no-schedule", action="store_true", help="skip the per-layer schedule timing")
     ap.add_argument("--no-fused", action="store_true",
                     help="skip the timing of the single-launch fused path (skiparse_attn)")
+    ap.add_argument("--no-probes", action="store_true",
+                    help="skip the measured ceilings (matrix-product stream, streaming copy)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -76,17 +78,31 @@ def measured_traffic(per_launch_flops):
     return float(m_b.group(1))
 
 
-def cpu_baseline(w, q, k, v, budget_s=15.0):
-    """Time the fp64 oracle on a bounded sample of the same workload (host cores)."""
+def host_cores():
+    """Host threads the oracle may use: this process's CPU affinity, capped at 16 (one GPU's
+    share of the host on the boxes this runs on)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def cpu_baseline(w, q, k, v, gpu_out, budget_s=15.0):
+    """Time the fp64 oracle on a bounded sample of the same workload on the host cores, and
+    compare the GPU output with it on that sample.
+
+    The sample's query rows are split over a pool of host_cores() threads, each running the
+    oracle's row function with one BLAS thread (numpy releases the interpreter lock inside
+    its kernels).  gpu_out is the GPU result for the same inputs (CPU tensor)."""
+    import concurrent.futures
+
     import numpy as np
+    from threadpoolctl import threadpool_limits
 
     import oracle
 
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
+    cores = host_cores()
     qn, kn, vn = (x.float().numpy() for x in (q, k, v))
     table = oracle.scope_table(w.N, w.sparse_k, w.mode)
     rng = np.random.default_rng(0)
@@ -99,29 +115,117 @@ def cpu_baseline(w, q, k, v, budget_s=15.0):
             parts.append(table[full, np.sort(rng.choice(w.L, size=rest, replace=False))])
         return np.concatenate(parts), full + (1 if rest else 0)
 
+    def rows(toks):
+        return oracle.skiparse_attention_rows(qn, kn, vn, w.T, w.H, w.W, w.sparse_k, w.mode,
+                                              np.zeros_like(toks), toks)
+
     def run(nrows):
         toks, _ = pick(nrows)
-        b = np.zeros_like(toks)
-        t0 = time.perf_counter()
-        oracle.skiparse_attention_rows(qn, kn, vn, w.T, w.H, w.W, w.sparse_k, w.mode, b, toks)
-        return time.perf_counter() - t0
+        chunks = np.array_split(toks, cores)
+        with threadpool_limits(limits=1), concurrent.futures.ThreadPoolExecutor(cores) as pool:
+            t0 = time.perf_counter()
+            parts = list(pool.map(rows, chunks))
+            t = time.perf_counter() - t0
+        return t, toks, np.concatenate(parts)
 
-    # fixed cost (rotating a scope's keys) plus a per-row cost, from two short runs
-    t1, t2 = run(64), run(256)
-    per_row = max((t2 - t1) / 192.0, 1e-6)
-    fixed = max(t1 - 64 * per_row, 0.0)
-    nrows = int(min(w.sparse_k * w.L, max(256, (budget_s - fixed) / per_row)))
+    # cost per row from one calibration run of 64 rows per thread; it includes each thread's
+    # fixed cost (rotating its scope's keys), so the sized run stays inside the budget
+    t1, _, _ = run(64 * cores)
+    per_row = max(t1 / (64.0 * cores), 1e-7)
+    nrows = int(min(w.sparse_k * w.L, max(64 * cores, budget_s / per_row)))
     _, nscopes = pick(nrows)
-    t = run(nrows)
+    t, toks, want = run(nrows)
     flops = 4.0 * nrows * w.heads * w.L * w.head_dim
+    got = gpu_out[0, torch_index(toks)].double().numpy()
+    err = np.abs(got - want)
+    rel = float(np.sqrt((err ** 2).sum() / (want ** 2).sum()))
     return {
         "value": flops / t / 1e12,
         "unit": "TFLOP/s",
-        "cores": int(threads),
+        "cores": cores,
         "kind": "oracle",
         "sample": (f"{nrows} query tokens of {nscopes} of the {w.sparse_k} scopes (all {w.heads} heads, all "
-                   f"{w.L} keys of each scope) of {w.name}, fp64 numpy, {t:.1f} s"),
+                   f"{w.L} keys of each scope) of {w.name}, fp64 numpy, {cores} threads with one BLAS "
+                   f"thread each, {t:.1f} s"),
+        "gpu_vs_oracle": {"rows": int(nrows), "max_abs": float(err.max()), "mean_abs": float(err.mean()),
+                          "rel_rms": rel, "bar_max_abs": 2e-2, "bar_mean_abs": 2e-3,
+                          "output": "RoPE pass + rotated attention, Single Skip, last timed step"},
     }
+
+
+def torch_index(toks):
+    import torch
+    return torch.from_numpy(toks)
+
+
+def probes(sk, stream, rope_bytes, remap_bytes, reps=10):
+    """Measured ceilings: the pure bf16 matrix-product stream at 1, 2 and 4 wavefronts per
+    SIMD, and the plain 16-byte nontemporal streaming copy moving the same bytes as the RoPE
+    pass and the RoPE+remap pass (half read, half written) over a sweep of grid sizes.  Each
+    the median of `reps` launches after warm-up, HIP events on the launch stream."""
+    import torch
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev[0].record(stream)
+        for i in range(reps):
+            fn()
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        return sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(reps))[reps // 2]
+
+    mfma = {}
+    for waves_per_simd in (1, 2, 4):
+        blocks = 256 * waves_per_simd        # 256 CUs, four wavefronts (one per SIMD) per block
+        out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+        _, flops = sk.probe_mfma(blocks, 2048, out=out, stream=stream)
+        ms = timed(lambda: sk.probe_mfma(blocks, 2048, out=out, stream=stream))
+        mfma[str(waves_per_simd)] = round(flops / (ms * 1e-3) / 1e12, 1)
+    stream_res = {}
+    for name, nbytes in (("rope_pass_bytes", rope_bytes), ("remap_pass_bytes", remap_bytes)):
+        n = nbytes // 2 // 16 * 4              # fp32 elements of the copied half
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        best = 0.0
+        per_grid = {}
+        for blocks in (1024, 2048, 4096, 8192, 16384):
+            ms = timed(lambda: sk.probe_stream(src, dst, blocks, stream=stream))
+            gbs = 2 * n * 4 / (ms * 1e-3) / 1e9
+            per_grid[str(blocks)] = round(gbs, 1)
+            best = max(best, gbs)
+        stream_res[name] = {"bytes_moved": 2 * n * 4, "best_gbs": round(best, 1), "per_grid_gbs": per_grid}
+        del src, dst
+    return {"mfma_bf16_tflops_by_waves_per_simd": mfma,
+            "mfma_bf16_measured_peak": max(mfma.values()),
+            "stream_copy": stream_res}
+
+
+def provenance():
+    """Seed, ROCm / torch versions, git revision (when the tree is a checkout) and a digest of
+    every library source, so a line can be tied to the code that produced it."""
+    import subprocess
+
+    import torch
+    h = hashlib.sha256()
+    for sub in ("skiparse_sparse_attention_amd/csrc", "include"):
+        d = os.path.join(ROOT, sub)
+        for f in sorted(os.listdir(d)):
+            with open(os.path.join(d, f), "rb") as fh:
+                h.update(f.encode() + fh.read())
+    try:
+        rev = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], capture_output=True, text=True,
+                             timeout=10).stdout.strip() or None
+    except Exception:
+        rev = None
+    rocm = None
+    for path in ("/opt/rocm/.info/version",):
+        if os.path.exists(path):
+            rocm = open(path).read().strip()
+    return {"seed": 0, "rocm_version": rocm, "torch_hip": torch.version.hip, "torch": torch.__version__,
+            "git_rev": rev, "library_source_sha16": h.hexdigest()[:16],
+            "device": torch.cuda.get_device_name(0)}
 
 
 def sweep(sk, wl, stream, reps=3):
@@ -450,13 +554,25 @@ def main():
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
             "avg_launch_ms": round(avg_launch_ms, 4),
+            "min_launch_ms": round(min(single_durs + group_durs), 4),
+            "algorithmic_flop_per_launch": flops_launch,
         },
         "rope_pass": {
             "kernel": "rope_qk_kernel", "bound": "hbm", "achieved": round(rope_gbs, 1), "peak": PEAK_HBM_GBS,
             "unit": "GB/s", "frac": round(rope_gbs / PEAK_HBM_GBS, 4), "avg_launch_ms": round(rope_ms, 4),
             "bytes_per_launch": rope_bytes, "launches_per_step": 2,
+            "min_launch_ms": round(min(rope_durs), 4),
         },
+        "provenance": provenance(),
     }
+
+    remap_bytes = 6 * qg.numel() * qg.element_size()
+    if not args.no_probes:
+        result["probes"] = probes(sk, stream, rope_bytes, remap_bytes)
+        ceiling = result["probes"]["stream_copy"]["rope_pass_bytes"]["best_gbs"]
+        result["rope_pass"]["frac_of_stream_copy"] = round(rope_gbs / ceiling, 4)
+        result["roofline"]["frac_of_measured_mfma_peak"] = round(
+            achieved / result["probes"]["mfma_bf16_measured_peak"], 4)
 
     if not args.no_remap:
         rq, rk, rv = (torch.empty((ws.sparse_k * ws.B, ws.L, ws.heads, ws.head_dim),
@@ -493,6 +609,10 @@ def main():
             "bytes_per_launch": nbytes,
             "device_copy_same_bytes_gbs": round(copy_gbs, 1),
         }
+        if "probes" in result:
+            ceiling = result["probes"]["stream_copy"]["remap_pass_bytes"]["best_gbs"]
+            result["remap_pass"]["stream_copy_same_bytes_gbs"] = ceiling
+            result["remap_pass"]["frac_of_stream_copy"] = round(gbs / ceiling, 4)
         del rq, rk, rv
 
     if not args.no_backward:
@@ -512,7 +632,7 @@ def main():
         result["sweep"] = sweep(sk, wl, stream)
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(ws, q, k, v)
+        result["cpu_baseline"] = cpu_baseline(ws, q, k, v, out_s.cpu())
 
     print(json.dumps(result), flush=True)
 

@@ -31,8 +31,9 @@
  * Scopes.  Single Skip (mode 0): token n is in scope s = n mod k at in-scope
  *   position p = n div k.  Group Skip (mode 1): token n is in scope
  *   s = (n div k) mod k at position p = (n div k^2)*k + n mod k.  In-scope order
- *   is increasing token index (the page's patterns 'b (g k) d -> (k b) g d' and
- *   'b (n m k) d -> (m b) (n k) d', m = k).
+ *   is increasing token index; a rearranged tensor puts the scope axis in front
+ *   of the batch axis (row s*B + b), the layout of the page's Single Skip and
+ *   Group Skip code.
  * 3D RoPE.  head_dim is split 2:3:3 over the t, h, w axes (16/24/24 at
  *   head_dim 64, 32/48/48 at 128), in that order.  Inside an axis chunk of size
  *   d_a, slot j and slot j + d_a/2 form a rotate-half pair rotated by
@@ -386,6 +387,24 @@ int skiparse_scope_table(int64_t N, int sparse_k, int mode, int64_t* token_of);
  */
 double skiparse_attn_flops(int B, int T, int H, int W, int heads, int head_dim,
                            int sparse_k);
+
+/*
+ * Measurement probes (not part of the method).  They measure, on the part
+ * itself, the two ceilings the kernels above are compared against: the
+ * matrix-core rate and the streaming copy rate of HBM.
+ *
+ * skiparse_probe_mfma -- `blocks` workgroups of 256 threads, each wavefront
+ *   issuing `iters` x 4 independent bf16 32x32x16 matrix products (no memory
+ *   traffic in the loop); out (blocks*256 fp32, device) receives one checksum
+ *   per thread.  skiparse_probe_mfma_flops gives the FLOPs of one launch.
+ * skiparse_probe_stream -- copies `bytes` (a multiple of 16, > 0) from src to
+ *   dst (16-byte aligned, not overlapping) with 16-byte nontemporal loads and
+ *   stores in a grid-stride loop over `blocks` workgroups of 256 threads.
+ * One launch each on `stream`; SKIPARSE_E_* on bad arguments.
+ */
+int skiparse_probe_mfma(int blocks, int iters, float* out, void* stream);
+double skiparse_probe_mfma_flops(int blocks, int iters);
+int skiparse_probe_stream(const void* src, void* dst, int64_t bytes, int blocks, void* stream);
 
 /* Static English text for a status code (never NULL). */
 const char* skiparse_status_string(int status);

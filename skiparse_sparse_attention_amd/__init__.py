@@ -34,6 +34,8 @@ from ._lib import (  # noqa: F401
     attn_rotated,
     attn_rotated_lse,
     lib,
+    probe_mfma,
+    probe_stream,
     q8_scope_pitch,
     quant8,
     rearrange,

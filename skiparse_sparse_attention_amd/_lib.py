@@ -94,6 +94,12 @@ def lib():
         L.skiparse_attn_bwd_rotated.restype = i
         L.skiparse_attn_schedule_rotated.argtypes = [ctypes.POINTER(Layer), i] + dims + [i, vp, vp, vp]
         L.skiparse_attn_schedule_rotated.restype = i
+        L.skiparse_probe_mfma.argtypes = [i, i, vp, vp]
+        L.skiparse_probe_mfma.restype = i
+        L.skiparse_probe_mfma_flops.argtypes = [i, i]
+        L.skiparse_probe_mfma_flops.restype = ctypes.c_double
+        L.skiparse_probe_stream.argtypes = [vp, vp, i64, i, vp]
+        L.skiparse_probe_stream.restype = i
         L.skiparse_status_string.argtypes = [i]
         L.skiparse_status_string.restype = ctypes.c_char_p
         L.skiparse_version.argtypes = []
@@ -509,3 +515,25 @@ def scope_table(N, sparse_k, mode):
 def attn_flops(B, grid, heads, head_dim, sparse_k):
     T, H, W = (int(g) for g in grid)
     return lib().skiparse_attn_flops(int(B), T, H, W, int(heads), int(head_dim), int(sparse_k))
+
+
+def probe_mfma(blocks, iters, out=None, stream=None):
+    """Measurement probe: one launch of `blocks` x 256 threads issuing only bf16 matrix
+    products; returns (out, FLOPs of the launch).  `out` holds blocks*256 fp32 checksums."""
+    import torch
+    if out is None:
+        out = torch.empty(int(blocks) * 256, dtype=torch.float32, device="cuda")
+    _validate([(out, "out", (int(blocks) * 256,), torch.float32)])
+    _check(lib().skiparse_probe_mfma(int(blocks), int(iters), out.data_ptr(), _stream_ptr(stream)),
+           "skiparse_probe_mfma")
+    return out, float(lib().skiparse_probe_mfma_flops(int(blocks), int(iters)))
+
+
+def probe_stream(src, dst, blocks, stream=None):
+    """Measurement probe: copy src to dst (same size, contiguous, a multiple of 16 bytes) with
+    16-byte nontemporal loads and stores over `blocks` workgroups."""
+    nbytes = src.numel() * src.element_size()
+    _validate([(src, "src", src.shape, src.dtype), (dst, "dst", src.shape, src.dtype)])
+    _check(lib().skiparse_probe_stream(src.data_ptr(), dst.data_ptr(), nbytes, int(blocks), _stream_ptr(stream)),
+           "skiparse_probe_stream")
+    return dst

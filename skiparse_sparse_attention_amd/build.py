@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libskiparse_amd.so")
 SOURCES = ["skiparse_api.cpp", "rope_remap.hip", "attn_fwd.hip", "attn_bwd.hip", "quant8.hip", "attn8_fwd.hip",
-           "attn_rot.hip"]
+           "attn_rot.hip", "probes.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -489,6 +489,26 @@ double skiparse_attn_flops(int B, int T, int H, int W, int heads, int head_dim, 
     return 4.0 * B * heads * N * std::floor(N / sparse_k) * head_dim;
 }
 
+int skiparse_probe_mfma(int blocks, int iters, float* out, void* stream) {
+    if (!out) return SKIPARSE_E_NULL;
+    if (blocks < 1 || iters < 1 || blocks > (1 << 20)) return SKIPARSE_E_SHAPE;
+    return to_status(skiparse::launch_probe_mfma(blocks, iters, out, static_cast<hipStream_t>(stream)));
+}
+
+double skiparse_probe_mfma_flops(int blocks, int iters) {
+    if (blocks < 1 || iters < 1) return -1.0;
+    // waves per block x products per wave (four chains) x 2*32*32*16 FLOP
+    return (double)blocks * (skiparse::probe_threads() / 64) * 4.0 * iters * (2.0 * 32 * 32 * 16);
+}
+
+int skiparse_probe_stream(const void* src, void* dst, int64_t bytes, int blocks, void* stream) {
+    if (!src || !dst) return SKIPARSE_E_NULL;
+    if (bytes < 16 || bytes % 16 || blocks < 1 || blocks > (1 << 20)) return SKIPARSE_E_SHAPE;
+    if ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15) return SKIPARSE_E_UNSUPPORTED;
+    if (overlaps(src, dst, bytes)) return SKIPARSE_E_ALIAS;
+    return to_status(skiparse::launch_probe_stream(src, dst, bytes / 16, blocks, static_cast<hipStream_t>(stream)));
+}
+
 const char* skiparse_status_string(int status) {
     switch (status) {
         case SKIPARSE_OK: return "ok";

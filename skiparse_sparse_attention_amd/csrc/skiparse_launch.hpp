@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/skiparse.h"
+
 namespace skiparse {
 
 struct RemapParams {
@@ -117,5 +119,9 @@ int attn8_block_rows();     // query rows per 8-bit attention workgroup
 hipError_t launch_rope_qk(const RopeQkParams& a, hipStream_t stream);
 hipError_t launch_attn_rot(const AttnParams& a, hipStream_t stream);   // a.lse set: also writes it
 hipError_t launch_attn_bwd_rot(const AttnBwdParams& a, hipStream_t stream);
+// measurement probes
+hipError_t launch_probe_mfma(int blocks, int iters, float* out, hipStream_t stream);
+hipError_t launch_probe_stream(const void* src, void* dst, int64_t pieces, int blocks, hipStream_t stream);
+int probe_threads();
 
 }  // namespace skiparse

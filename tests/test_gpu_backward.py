@@ -119,10 +119,16 @@ def test_backward_uniform_softmax_probe_bit_exact():
     assert np.array_equal(dv.cpu().double().numpy(), want)
 
 
-@pytest.mark.parametrize("w", [wl.OSP_SINGLE, wl.OSP_GROUP], ids=lambda w: w.name)
-def test_full_size_scope_sample(w):
-    """The 24x22x40 workload at its full size: every member token of the first and the last
-    scope, two heads, against the oracle restricted to that scope."""
+FULL_BWD = [(wl.OSP_SINGLE, 0, (0, 3)), (wl.OSP_GROUP, 0, (0, 3)), (wl.HC_GROUP, 0, (2,)),
+            (wl.LONG_GROUP, 1, (5,))]
+
+
+@pytest.mark.parametrize("w,b,scopes", FULL_BWD, ids=[f"{w.name}_b{b}" for w, b, _ in FULL_BWD])
+def test_full_size_scope_sample(w, b, scopes):
+    """Full-size workloads: every member token of the listed scopes of batch b, two heads,
+    against the oracle restricted to that scope (the 24x22x40 grid in both modes, one scope
+    of the 36864-token grid and one of the second batch of the 46080-token grid)."""
+    print(f"case {w.name} b{b} scopes {scopes}", flush=True)
     q, kk, v = wl.make_inputs(w, seed=0, device="cuda")
     do = wl.make_output_grad(w, seed=1, device="cuda")
     out, lse = sk.attn_lse(q, kk, v, w.grid, w.sparse_k, w.mode)
@@ -131,7 +137,8 @@ def test_full_size_scope_sample(w):
     heads = [0, w.heads - 1]
     host = [x.cpu().float() for x in (q, kk, v, do)]   # exact copies of the bf16 values
     got = [x.cpu() for x in (dq, dk, dv)]
-    for s in (0, w.sparse_k - 1):
-        toks, rq, rk, rv = oracle.skiparse_attention_backward_scope(*host, w.T, w.H, w.W, w.sparse_k, w.mode, 0, s, heads)
+    del q, kk, v, do, out, lse, dq, dk, dv
+    for s in scopes:
+        toks, rq, rk, rv = oracle.skiparse_attention_backward_scope(*host, w.T, w.H, w.W, w.sparse_k, w.mode, b, s, heads)
         for name, g_, r in zip(("dq", "dk", "dv"), got, (rq, rk, rv)):
-            _check(g_[0][toks][:, heads].double().numpy(), r, f"{name} {w.name} scope {s}")
+            _check(g_[b][toks][:, heads].double().numpy(), r, f"{name} {w.name} b{b} scope {s}")

@@ -301,14 +301,18 @@ def test_attn_errors_surface_as_exceptions():
 # ---------------------------------------------------------------------------
 
 def _sample_rows(w, rng):
-    """(batch, token) pairs: two scopes (first and last), 12 positions each including the
-    first and last in-scope positions and rows of the ragged last q tile."""
+    """(batch, token) pairs covering every scope of the first and the last batch.
+
+    Per (batch, scope): in-scope positions 0, 1, L/2, the first row of the last 256-row
+    query tile (ragged whenever 256 does not divide L), L-2 and L-1, plus three positions
+    drawn from ``rng`` (numpy default_rng seeded 0 by the caller), mapped to their tokens by
+    the oracle's scope table."""
     table = oracle.scope_table(w.N, w.sparse_k, w.mode)
     picks_b, picks_t = [], []
     for b in sorted({0, w.B - 1}):
-        for s in sorted({0, w.sparse_k - 1}):
-            pos = {0, w.L - 1, w.L - 2, (w.L // 256) * 256, w.L // 2}
-            pos |= set(rng.integers(0, w.L, size=7).tolist())
+        for s in range(w.sparse_k):
+            pos = {0, 1, w.L // 2, ((w.L - 1) // 256) * 256, w.L - 2, w.L - 1}
+            pos |= set(rng.integers(0, w.L, size=3).tolist())
             for p in sorted(pos):
                 if 0 <= p < w.L:
                     picks_b.append(b)
@@ -316,22 +320,64 @@ def _sample_rows(w, rng):
     return np.array(picks_b), np.array(picks_t)
 
 
-FULL = [wl.OSP_SINGLE, wl.OSP_GROUP, wl.HC_GROUP, wl.WAN_DENSE, wl.LONG_GROUP, wl.LONG_SINGLE]
+OSP_K2_SINGLE = wl.OSP_SINGLE.with_mode(oracle.SINGLE, sparse_k=2)
+OSP_K2_GROUP = wl.OSP_SINGLE.with_mode(oracle.GROUP, sparse_k=2)
+OSP_K8_SINGLE = wl.OSP_SINGLE.with_mode(oracle.SINGLE, sparse_k=8)
+OSP_K8_GROUP = wl.OSP_SINGLE.with_mode(oracle.GROUP, sparse_k=8)
+FULL = [wl.OSP_SINGLE, wl.OSP_GROUP, OSP_K2_SINGLE, OSP_K2_GROUP, OSP_K8_SINGLE, OSP_K8_GROUP,
+        wl.HC_GROUP, wl.WAN_DENSE, wl.LONG_GROUP, wl.LONG_SINGLE]
 
 
-@pytest.mark.parametrize("w", FULL, ids=[w.name for w in FULL])
+def _full_id(w):
+    return f"{w.name}_k{w.sparse_k}_{'group' if w.mode else 'single'}"
+
+
+@pytest.mark.parametrize("w", FULL, ids=[_full_id(w) for w in FULL])
 def test_full_size_config_sampled_rows(w):
-    print(f"case {w.name}", flush=True)
+    """Both forward forms at the full size: the fused kernel and the RoPE pass + rotated
+    attention (the launch pair the bench times) are equal bit for bit, every output element
+    is written, and sampled rows of every scope match the oracle."""
+    print(f"case {_full_id(w)}", flush=True)
     q, k, v = wl.make_inputs(w, seed=0, device="cpu")
     qg, kg, vg = q.cuda(), k.cuda(), v.cuda()
     out = torch.full_like(qg, float("nan"))
     sk.attn(qg, kg, vg, w.grid, w.sparse_k, w.mode, out=out)
+    rot = torch.full_like(qg, float("nan"))
+    qr, kr = sk.rope_qk(qg, kg, w.grid)
+    sk.attn_rotated(qr, kr, vg, w.grid, w.sparse_k, w.mode, out=rot)
     torch.cuda.synchronize()
     assert not torch.isnan(out).any().item(), "some output element was not written"
+    assert torch.equal(out.view(torch.int16), rot.view(torch.int16)), "rotated path differs from the fused one"
+    del qr, kr, rot
     rng = np.random.default_rng(0)
     b_idx, t_idx = _sample_rows(w, rng)
     # exact fp32 views of the bf16 inputs; the oracle widens the rows it uses to fp64
     qn, kn, vn = (x.float().numpy() for x in (q, k, v))
     want = oracle.skiparse_attention_rows(qn, kn, vn, w.T, w.H, w.W, w.sparse_k, w.mode, b_idx, t_idx)
     got = out[torch.from_numpy(b_idx).cuda(), torch.from_numpy(t_idx).cuda()]
-    _assert_close(_np64(got), want, f"{w.name} ({len(t_idx)} rows)")
+    _assert_close(_np64(got), want, f"{_full_id(w)} ({len(t_idx)} rows)")
+
+
+@pytest.mark.parametrize("mode", [oracle.SINGLE, oracle.GROUP], ids=["single", "group"])
+def test_full_size_rope_remap(mode):
+    """The materialised RoPE + rearrange at the 24x22x40 / 24-head / k = 4 size the bench
+    times: v moves bit-exactly (whole tensor), q and k are within one bf16 ulp of the fp64
+    RoPE on a row sample of every scope (positions 0, 1, L/2, L-1 and four drawn from
+    numpy default_rng(1))."""
+    w = wl.OSP_SINGLE.with_mode(mode)
+    q, k, v = wl.make_inputs(w, seed=0, device="cpu")
+    rq, rk, rv = sk.rope_remap(q.cuda(), k.cuda(), v.cuda(), w.grid, w.sparse_k, w.mode)
+    torch.cuda.synchronize()
+    vbits = v.view(torch.int16).numpy().reshape(w.B, w.N, w.heads * w.head_dim)
+    want_v = oracle.rearrange(vbits, w.sparse_k, w.mode).reshape(rv.shape)
+    assert np.array_equal(rv.cpu().view(torch.int16).numpy(), want_v)
+    table = oracle.scope_table(w.N, w.sparse_k, w.mode)
+    t_all, h_all, w_all = oracle.token_positions(w.T, w.H, w.W)
+    rng = np.random.default_rng(1)
+    for s in range(w.sparse_k):
+        pos = np.array(sorted({0, 1, w.L // 2, w.L - 1} | set(rng.integers(0, w.L, size=4).tolist())))
+        toks = table[s, pos]
+        for x, r in ((q, rq), (k, rk)):
+            exact = oracle.rope_3d_at(x[0, toks].double().numpy(), t_all[toks], h_all[toks], w_all[toks])
+            got = r[s * w.B, torch.from_numpy(pos).cuda()]
+            assert int(_bf16_ulps(got, exact).max()) <= 1, (s, pos)
