@@ -47,7 +47,9 @@
  *   rearrange/reverse calls keep fp32 throughout.
  * Pointers.  All array pointers are device pointers (hipMalloc'd or torch CUDA
  *   tensors' data_ptr), 16-byte aligned.  The caller owns every buffer; the
- *   library allocates nothing and keeps no state between calls.
+ *   library allocates nothing and keeps no state between calls, except the
+ *   static workspace of skiparse_attn_bwd_rotated_static (one per GPU, for the
+ *   life of the process).
  * Streams.  `stream` is a hipStream_t passed as void* (NULL: the default
  *   stream).  Calls are asynchronous: they return once the kernels are
  *   enqueued; execution errors surface at the caller's next synchronization.
@@ -73,7 +75,9 @@ enum skiparse_status {
     SKIPARSE_E_DIVISIBILITY = 3,  /* Single: N % k != 0; Group: N % k^2 != 0 (no padding)     */
     SKIPARSE_E_UNSUPPORTED = 4,   /* head_dim not 64/128, bad mode/dtype, grid too large     */
     SKIPARSE_E_ALIAS = 5,         /* an output buffer overlaps an input buffer               */
-    SKIPARSE_E_DEVICE = 6         /* a HIP call failed (launch error, no device, ...)        */
+    SKIPARSE_E_DEVICE = 6,        /* a HIP call failed (launch error, no device, ...)        */
+    SKIPARSE_E_WORKSPACE = 7      /* B*heads*N exceeds SKIPARSE_STATIC_DELTA_MAX (the static
+                                     workspace of skiparse_attn_bwd_rotated_static only)    */
 };
 
 /* Largest T + H + W: every kernel keeps a 3D-RoPE cos/sin table with one row per
@@ -214,6 +218,33 @@ int skiparse_attn_bwd_rotated(const void* qr, const void* kr, const void* v,
                               int B, int T, int H, int W, int heads, int head_dim,
                               int sparse_k, int mode, int dtype,
                               void* dq, void* dk, void* dv, float* delta, void* stream);
+
+/* Capacity of skiparse_attn_bwd_rotated_static's workspace: B*heads*N fp32
+ * values (16 MiB per GPU). */
+#define SKIPARSE_STATIC_DELTA_MAX 4194304
+
+/*
+ * skiparse_attn_bwd_rotated_static -- skiparse_attn_bwd_rotated without the
+ * delta argument, for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving or training loops, harnesses that forbid
+ * hipMalloc).  The delta vector lives in a static device array of the library
+ * (SKIPARSE_STATIC_DELTA_MAX fp32 values, 256-byte aligned), one per GPU,
+ * held from the library's load until the process ends; its address on each
+ * device is looked up once, on the first call with that device current.  The
+ * call allocates nothing (no hipMalloc, no allocating library routine).
+ * Everything else -- arguments, layouts, limits, results (bit for bit) -- is
+ * skiparse_attn_bwd_rotated's.  B*heads*N above SKIPARSE_STATIC_DELTA_MAX
+ * returns SKIPARSE_E_WORKSPACE before any device call.
+ * Every call on one GPU shares that GPU's workspace: each call writes all of
+ * the delta it reads (nothing needs to start at zero), but calls that overlap
+ * in time on one GPU -- on different streams, or from different threads --
+ * race on it and must be serialised by the caller.
+ */
+int skiparse_attn_bwd_rotated_static(const void* qr, const void* kr, const void* v,
+                                     const void* out, const void* dout, const float* lse,
+                                     int B, int T, int H, int W, int heads, int head_dim,
+                                     int sparse_k, int mode, int dtype,
+                                     void* dq, void* dk, void* dv, void* stream);
 
 /*
  * skiparse_attn_bwd_flops -- FLOPs counted for one skiparse_attn_bwd call:

@@ -14,6 +14,7 @@ from ._lib import (  # noqa: F401
     E_NULL,
     E_SHAPE,
     E_UNSUPPORTED,
+    E_WORKSPACE,
     FP32,
     GROUP,
     LIB_PATH,
@@ -21,11 +22,13 @@ from ._lib import (  # noqa: F401
     MAX_GRID_SUM,
     OK,
     SINGLE,
+    STATIC_DELTA_MAX,
     SkiparseError,
     attn,
     attn8,
     attn_bwd,
     attn_bwd_rotated,
+    attn_bwd_rotated_static,
     attn_schedule,
     attn_schedule_rotated,
     attn_bwd_flops,

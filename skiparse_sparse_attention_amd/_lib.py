@@ -28,6 +28,10 @@ E_DIVISIBILITY = 3
 E_UNSUPPORTED = 4
 E_ALIAS = 5
 E_DEVICE = 6
+E_WORKSPACE = 7
+
+# capacity of attn_bwd_rotated_static's workspace: B*heads*N fp32 values
+STATIC_DELTA_MAX = 4194304
 
 MAX_GRID_SUM = 192
 
@@ -92,6 +96,8 @@ def lib():
         L.skiparse_attn_rotated_lse.restype = i
         L.skiparse_attn_bwd_rotated.argtypes = [vp] * 6 + dims + [i, i, i] + [vp] * 5
         L.skiparse_attn_bwd_rotated.restype = i
+        L.skiparse_attn_bwd_rotated_static.argtypes = [vp] * 6 + dims + [i, i, i] + [vp] * 4
+        L.skiparse_attn_bwd_rotated_static.restype = i
         L.skiparse_attn_schedule_rotated.argtypes = [ctypes.POINTER(Layer), i] + dims + [i, vp, vp, vp]
         L.skiparse_attn_schedule_rotated.restype = i
         L.skiparse_probe_mfma.argtypes = [i, i, vp, vp]
@@ -284,6 +290,21 @@ def attn_bwd_rotated(qr, kr, v, out, dout, lse, grid, sparse_k, mode, grads=None
                                            int(sparse_k), int(mode), code, dq.data_ptr(),
                                            dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
                                            _stream_ptr(stream)), "skiparse_attn_bwd_rotated")
+    return dq, dk, dv
+
+
+def attn_bwd_rotated_static(qr, kr, v, out, dout, lse, grid, sparse_k, mode, grads=None, stream=None):
+    """attn_bwd_rotated with its delta workspace in the library's static per-GPU array (the
+    call allocates nothing when ``grads`` are given); equal to attn_bwd_rotated bit for bit.
+    B*heads*N must not exceed STATIC_DELTA_MAX, and calls that overlap on one GPU race on
+    the shared workspace."""
+    dims, code, (dq, dk, dv), _ = _bwd_args(qr, kr, v, out, dout, lse, grid, grads, lse,
+                                            ("qr", "kr", "v", "out", "dout"))
+    _check(lib().skiparse_attn_bwd_rotated_static(qr.data_ptr(), kr.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                                  dout.data_ptr(), lse.data_ptr(), *dims,
+                                                  int(sparse_k), int(mode), code, dq.data_ptr(),
+                                                  dk.data_ptr(), dv.data_ptr(), _stream_ptr(stream)),
+           "skiparse_attn_bwd_rotated_static")
     return dq, dk, dv
 
 

@@ -31,6 +31,7 @@
 // On operands that skiparse_rope_qk already rotated, the dq kernel copies its tiles into LDS
 // with direct loads (template flag ROT) and attn_bwd_dkdv_rot_kernel replaces the dk/dv kernel:
 // K' and V held in registers, the query tiles streamed into a three-deep LDS ring.
+#include <mutex>
 #include <type_traits>
 
 #include "attn_common.hpp"
@@ -1224,5 +1225,40 @@ hipError_t launch_attn_bwd_rot(const AttnBwdParams& a, hipStream_t stream) {
 
 int attn_bwd_block_rows() { return kBwdRows; }
 int attn_bwd_dq_rows() { return kDqRows; }
+
+}  // namespace skiparse
+
+// Workspace of skiparse_attn_bwd_rotated_static: the backward's delta vector (rowsum of
+// dout * out per (batch, head, token), fp32), written by the dq launch and read by the dk/dv
+// launch of the same call.  Every GPU that loads the library holds one copy until the process
+// ends; every call on that GPU shares it.  In host code the name below is only a host-side
+// stand-in: its device address comes from hipGetSymbolAddress, per device.
+static __device__ __align__(256) float scratch[skiparse::kStaticDeltaFloats];
+
+namespace skiparse {
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_static_mutex;
+float* g_static_delta[kMaxDevices] = {};
+}  // namespace
+
+hipError_t static_delta_workspace(float** ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_static_mutex);
+    if (g_static_delta[dev] == nullptr) {
+        // looked up once per device, with that device current: each GPU has its own copy
+        // of the array at its own address
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_static_delta[dev] = static_cast<float*>(p);
+    }
+    *ptr = g_static_delta[dev];
+    return hipSuccess;
+}
 
 }  // namespace skiparse

@@ -263,12 +263,14 @@ int skiparse_attn_lse(const void* q, const void* k, const void* v, int B, int T,
     return attn_forward(q, k, v, B, T, H, W, heads, head_dim, sparse_k, mode, dtype, out, lse, stream);
 }
 
-// skiparse_attn_bwd and skiparse_attn_bwd_rotated (q, k already rotated, q scaled)
+// skiparse_attn_bwd, skiparse_attn_bwd_rotated (q, k already rotated, q scaled) and
+// skiparse_attn_bwd_rotated_static (delta == nullptr: the library's static workspace)
 static int attn_backward(const void* q, const void* k, const void* v, const void* out, const void* dout,
                          const float* lse, int B, int T, int H, int W, int heads, int head_dim,
                          int sparse_k, int mode, int dtype, void* dq, void* dk, void* dv, float* delta,
-                         bool rotated, void* stream) {
-    if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv || !delta) return SKIPARSE_E_NULL;
+                         bool rotated, bool static_delta, void* stream) {
+    if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv || (!delta && !static_delta))
+        return SKIPARSE_E_NULL;
     const int st = skiparse_validate(q, k, v, B, T, H, W, heads, head_dim, sparse_k, mode, dtype, out);
     if (st != SKIPARSE_OK) return st;
     if (rotated && (head_dim != 128 || dtype != SKIPARSE_BF16)) return SKIPARSE_E_UNSUPPORTED;
@@ -276,7 +278,7 @@ static int attn_backward(const void* q, const void* k, const void* v, const void
     check_dims(B, T, H, W, heads, head_dim, sparse_k, mode, dtype, &d);
     const int64_t vec_bytes = (int64_t)B * heads * d.N * 4;
     // outputs: dq, dk, dv (tensor-sized) and delta (vector-sized) must not overlap any input or
-    // each other
+    // each other (the static workspace is a buffer of its own)
     const void* ins[5] = {q, k, v, out, dout};
     void* outs[3] = {dq, dk, dv};
     for (int i = 0; i < 3; ++i) {
@@ -284,12 +286,14 @@ static int attn_backward(const void* q, const void* k, const void* v, const void
             if (overlaps(outs[i], ins[j], d.bytes)) return SKIPARSE_E_ALIAS;
         for (int j = i + 1; j < 3; ++j)
             if (overlaps(outs[i], outs[j], d.bytes)) return SKIPARSE_E_ALIAS;
-        if (ranges_overlap(outs[i], d.bytes, lse, vec_bytes) || ranges_overlap(outs[i], d.bytes, delta, vec_bytes))
-            return SKIPARSE_E_ALIAS;
+        if (ranges_overlap(outs[i], d.bytes, lse, vec_bytes)) return SKIPARSE_E_ALIAS;
+        if (!static_delta && ranges_overlap(outs[i], d.bytes, delta, vec_bytes)) return SKIPARSE_E_ALIAS;
     }
-    for (int j = 0; j < 5; ++j)
-        if (ranges_overlap(delta, vec_bytes, ins[j], d.bytes)) return SKIPARSE_E_ALIAS;
-    if (overlaps(delta, lse, vec_bytes)) return SKIPARSE_E_ALIAS;
+    if (!static_delta) {
+        for (int j = 0; j < 5; ++j)
+            if (ranges_overlap(delta, vec_bytes, ins[j], d.bytes)) return SKIPARSE_E_ALIAS;
+        if (overlaps(delta, lse, vec_bytes)) return SKIPARSE_E_ALIAS;
+    }
     skiparse::AttnBwdParams a;
     a.q = q; a.k = k; a.v = v; a.o = out; a.dout = dout; a.lse = lse; a.delta = delta;
     a.dq = dq; a.dk = dk; a.dv = dv;
@@ -306,6 +310,10 @@ static int attn_backward(const void* q, const void* k, const void* v, const void
     a.scale = (float)(1.0 / std::sqrt((double)head_dim));
     a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)head_dim));
     a.phi_mul = phi_mul_of(mode, sparse_k);
+    if (static_delta) {
+        if ((int64_t)B * heads * d.N > skiparse::kStaticDeltaFloats) return SKIPARSE_E_WORKSPACE;
+        if (to_status(skiparse::static_delta_workspace(&a.delta)) != SKIPARSE_OK) return SKIPARSE_E_DEVICE;
+    }
     const hipStream_t hs = static_cast<hipStream_t>(stream);
     return to_status(rotated ? skiparse::launch_attn_bwd_rot(a, hs) : skiparse::launch_attn_bwd(a, head_dim, dtype, hs));
 }
@@ -315,7 +323,7 @@ int skiparse_attn_bwd(const void* q, const void* k, const void* v, const void* o
                       int sparse_k, int mode, int dtype, void* dq, void* dk, void* dv, float* delta,
                       void* stream) {
     return attn_backward(q, k, v, out, dout, lse, B, T, H, W, heads, head_dim, sparse_k, mode, dtype, dq, dk, dv,
-                         delta, false, stream);
+                         delta, false, false, stream);
 }
 
 int skiparse_attn_bwd_rotated(const void* qr, const void* kr, const void* v, const void* out, const void* dout,
@@ -323,7 +331,15 @@ int skiparse_attn_bwd_rotated(const void* qr, const void* kr, const void* v, con
                               int sparse_k, int mode, int dtype, void* dq, void* dk, void* dv, float* delta,
                               void* stream) {
     return attn_backward(qr, kr, v, out, dout, lse, B, T, H, W, heads, head_dim, sparse_k, mode, dtype, dq, dk, dv,
-                         delta, true, stream);
+                         delta, true, false, stream);
+}
+
+int skiparse_attn_bwd_rotated_static(const void* qr, const void* kr, const void* v, const void* out,
+                                     const void* dout, const float* lse, int B, int T, int H, int W, int heads,
+                                     int head_dim, int sparse_k, int mode, int dtype, void* dq, void* dk,
+                                     void* dv, void* stream) {
+    return attn_backward(qr, kr, v, out, dout, lse, B, T, H, W, heads, head_dim, sparse_k, mode, dtype, dq, dk, dv,
+                         nullptr, true, true, stream);
 }
 
 double skiparse_attn_bwd_flops(int B, int T, int H, int W, int heads, int head_dim, int sparse_k) {
@@ -518,6 +534,7 @@ const char* skiparse_status_string(int status) {
         case SKIPARSE_E_UNSUPPORTED: return "unsupported head_dim, mode, dtype or grid size";
         case SKIPARSE_E_ALIAS: return "an output buffer overlaps an input buffer";
         case SKIPARSE_E_DEVICE: return "a HIP call failed";
+        case SKIPARSE_E_WORKSPACE: return "B*heads*N exceeds the static workspace";
         default: return "unknown status";
     }
 }

@@ -119,6 +119,9 @@ int attn8_block_rows();     // query rows per 8-bit attention workgroup
 hipError_t launch_rope_qk(const RopeQkParams& a, hipStream_t stream);
 hipError_t launch_attn_rot(const AttnParams& a, hipStream_t stream);   // a.lse set: also writes it
 hipError_t launch_attn_bwd_rot(const AttnBwdParams& a, hipStream_t stream);
+// Capacity (fp32 elements) of the static delta workspace and its address on the current device.
+constexpr int64_t kStaticDeltaFloats = SKIPARSE_STATIC_DELTA_MAX;   // 16 MiB per GPU
+hipError_t static_delta_workspace(float** ptr);
 // measurement probes
 hipError_t launch_probe_mfma(int blocks, int iters, float* out, hipStream_t stream);
 hipError_t launch_probe_stream(const void* src, void* dst, int64_t pieces, int blocks, hipStream_t stream);

@@ -33,7 +33,7 @@ def test_header_declares_the_boundary():
                  "skiparse_attn_bwd", "skiparse_attn_bwd_flops", "skiparse_quant8", "skiparse_attn8",
                  "skiparse_q8_scope_pitch", "skiparse_attn_schedule", "skiparse_rope_qk",
                  "skiparse_attn_rotated", "skiparse_attn_rotated_lse", "skiparse_attn_bwd_rotated",
-                 "skiparse_attn_schedule_rotated"):
+                 "skiparse_attn_schedule_rotated", "skiparse_attn_bwd_rotated_static"):
         assert want in names
 
 
@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     assert "gfx950" in sk.version()
-    for st in range(0, 7):
+    for st in range(0, 8):
         assert sk.status_string(st)
     assert sk.status_string(99) == "unknown status"
 
@@ -257,6 +257,27 @@ def test_rotated_lse_and_backward_reject_before_any_device_call():
     assert L.skiparse_attn_bwd_rotated(*bad) == sk.E_ALIAS
     bad = list(base); bad[5] = None
     assert L.skiparse_attn_bwd_rotated(*bad) == sk.E_NULL
+
+
+def test_static_workspace_backward_rejects_before_any_device_call():
+    L = sk.lib()
+    # skiparse_attn_bwd_rotated_static(qr, kr, v, out, dout, lse, B, T, H, W, heads, head_dim, sparse_k,
+    #                                  mode, dtype, dq, dk, dv, stream): no delta argument
+    base = [Q, K, V, OUT, DO, LSE, 1, 4, 8, 8, 2, 128, 2, 0, 0, DQ, DK, DV, None]   # valid: never called as is
+    bad = list(base); bad[11] = 64
+    assert L.skiparse_attn_bwd_rotated_static(*bad) == sk.E_UNSUPPORTED
+    bad = list(base); bad[16] = V
+    assert L.skiparse_attn_bwd_rotated_static(*bad) == sk.E_ALIAS
+    bad = list(base); bad[17] = LSE
+    assert L.skiparse_attn_bwd_rotated_static(*bad) == sk.E_ALIAS
+    bad = list(base); bad[0] = None
+    assert L.skiparse_attn_bwd_rotated_static(*bad) == sk.E_NULL
+    # B*heads*N = 5 * 32 * 32768 > SKIPARSE_STATIC_DELTA_MAX: rejected before the workspace is
+    # looked up (a valid size otherwise; the fake addresses are 1 TiB apart)
+    big = [Q, K, V, OUT, DO, LSE, 5, 8, 64, 64, 32, 128, 1, 0, 0, DQ, DK, DV, None]
+    assert 5 * 32 * 32768 > sk.STATIC_DELTA_MAX
+    assert L.skiparse_attn_bwd_rotated_static(*big) == sk.E_WORKSPACE
+    assert "static workspace" in sk.status_string(sk.E_WORKSPACE)
 
 
 def test_rotated_schedule_rejects_before_any_device_call():
