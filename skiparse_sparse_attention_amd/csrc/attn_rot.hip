@@ -40,8 +40,7 @@ constexpr int kRVOff = kRBufs * kRTile;
 constexpr int kRLds = 2 * kRBufs * kRTile;
 constexpr float kRRescaleLog2 = 8.0f;
 
-constexpr int kRopeThreads = 1024;         // one workgroup per CU: the table is built once per CU
-constexpr int kRopeGrid = 256;            // rotation workgroups (one per CU of a 256-CU part)
+constexpr int kRopeWaves = 4;             // rotation pass: wavefronts (tokens) per workgroup
 
 // K tile row r: logical granule g of the row is stored at granule g ^ krswz(r).  The QK operand
 // reads fetch one granule of 16 consecutive rows per 16 lanes, which then fall on 16 distinct
@@ -56,67 +55,98 @@ __device__ __forceinline__ int qk_chunk(int ks, int hf) {
 
 }  // namespace
 
-// ---- the rotation pass: one (token, head) row per 16 lanes, one RoPE chunk per lane ----
-// Lane c of a row loads its own chunk c and its rotate-half partner (the partner load hits the
-// cache lines of the row that the own-chunk loads of the other 15 lanes fetch), rotates the
-// pair with the fused kernel's helper and keeps the half it owns, so each load and store
-// instruction moves 4 whole rows (1 KiB) and the values are the fused kernel's bit for bit.
-__global__ void __launch_bounds__(kRopeThreads) rope_qk_kernel(RopeQkParams a) {
-    extern __shared__ __attribute__((aligned(16))) char lds[];
-    build_banked_rope_table<kRD>(lds, a.T, a.H, a.W, 0);
-    __syncthreads();
-    const int c = threadIdx.x & 15;
+// ---- the rotation pass: one wavefront per token, one RoPE chunk per lane ----
+// A wavefront rotates every head row of one token of q and of k.  Lane l owns RoPE chunk
+// c = l % 16 of head rows l / 16, l / 16 + 4, ..., so the eight (cos, sin) pairs it needs are
+// the same for all its rows.  The token's 64 pairs (16 on the t axis, 24 on h, 24 on w) are
+// evaluated one per lane, with the float64 expressions of the attention kernels' table
+// (build_banked_rope_table) rounded to float32, so the rotated rows hold exactly the operands
+// the fused kernel computes; that evaluation runs while the first loads are in flight.  The
+// rotate-half partner chunk of c lies 2 (t axis) or 3 (h, w) chunks away in the same head
+// row, i.e. in a lane of the same group of 16, and is fetched with a cross-lane permute.
+// Loads are nontemporal (read once); stores are ordinary write-back stores, since the
+// attention that follows reads q' and k' right away.  One-shot grid: one wavefront per
+// token, no loop over tokens.
+__global__ void __launch_bounds__(64 * kRopeWaves) rope_qk_kernel(RopeQkParams a) {
+    __shared__ __attribute__((aligned(16))) float2 pairs[kRopeWaves][64];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t tok = (int64_t)blockIdx.x * kRopeWaves + wave;     // b * N + n
+    if (tok >= (int64_t)a.B * a.N) return;
+    const int n = (int)(tok % a.N);
+    const int c = lane & 15;
     // the chunk pair of chunk c (rope_pair order: t pairs 0-1, h pairs 2-4, w pairs 5-7)
     const int cp = c < 4 ? (c & 1) : (c < 10 ? 2 + (c - 4) % 3 : 5 + (c - 10) % 3);
     const RopePair rp = rope_pair(cp);
     const bool first = c == rp.c1;
-    const int other = first ? rp.c2 : rp.c1;
-    const int HW = a.H * a.W;
-    constexpr int kRows = kRopeThreads / 16;                // rows per workgroup step
-    const int tasks = a.B * a.N * a.heads;                  // (token row, head) rows
-    const int step = gridDim.x * kRows;
-#pragma unroll 2
-    for (int t = blockIdx.x * kRows + (threadIdx.x >> 4); t < tasks; t += step) {
-        const int n = (t / a.heads) % a.N;
-        const int pos = rp.axis == 0 ? n / HW : (rp.axis == 1 ? (n / a.W) % a.H : n % a.W);
-        const char* trow = lds + rope_tab_offset<kRD>(a.T, a.H, rp.axis, pos, rp.jchunk * kRCH, 0);
-        f32x4 cs[kRCH / 2];
+    const int partner = (lane & ~15) + (first ? rp.c2 : rp.c1);
+    const int base = (rp.axis == 0 ? 0 : (rp.axis == 1 ? 16 : 40)) + rp.jchunk * kRCH;
+    const int64_t row0 = tok * a.heads * kRRow;         // byte offset of the token's first head row
+    const int hrows = (a.heads + 3) / 4;                // head rows per lane
+    constexpr int kU = 6;                               // head rows per lane per round
+    u32x4 w[2][kU];
+    auto load_round = [&](int i0) __attribute__((always_inline)) {
 #pragma unroll
-        for (int j = 0; j < kRCH / 2; ++j) cs[j] = *reinterpret_cast<const f32x4*>(trow + 16 * j);
-        const int64_t row = (int64_t)t * kRRow;             // byte offset of the (token, head) row
-        u32x4 wown[2], woth[2];
+        for (int which = 0; which < 2; ++which)
 #pragma unroll
-        for (int which = 0; which < 2; ++which) {
-            const char* in = reinterpret_cast<const char*>(which == 0 ? a.q : a.k) + row;
-            wown[which] = *reinterpret_cast<const u32x4*>(in + c * 16);
-            woth[which] = *reinterpret_cast<const u32x4*>(in + other * 16);
-        }
-#pragma unroll
-        for (int which = 0; which < 2; ++which) {
-            ChunkRaw<BF16, kRCH> r1, r2;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                r1.w[i] = first ? wown[which][i] : woth[which][i];
-                r2.w[i] = first ? woth[which][i] : wown[which][i];
+            for (int u = 0; u < kU; ++u) {
+                const int h = min(4 * (i0 + u) + (lane >> 4), a.heads - 1);
+                const char* in = reinterpret_cast<const char*>(which == 0 ? a.q : a.k) + row0 + h * kRRow + c * 16;
+                w[which][u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(in));
             }
-            float x1[kRCH], x2[kRCH];
-            raw_to_f32(r1, x1);
-            raw_to_f32(r2, x2);
-            rope_rotate_cs<kRCH>(x1, x2, cs);
-            if (which == 0) {
+    };
+    load_round(0);
+    {
+        // pair `lane` of the token: t axis pairs 0-15 (d_t = 32), h 16-39, w 40-63 (d = 48)
+        const int axis = lane < 16 ? 0 : (lane < 40 ? 1 : 2);
+        const int j = lane - (axis == 0 ? 0 : (axis == 1 ? 16 : 40));
+        const int pos = axis == 0 ? n / (a.H * a.W) : (axis == 1 ? (n / a.W) % a.H : n % a.W);
+        const double da = axis == 0 ? (double)(kRD / 4) : (double)(3 * kRD / 8);
+        const double inv_freq = pow(10000.0, -2.0 * (double)j / da);
+        const double theta = (double)pos * inv_freq;
+        double sn, cs;
+        sincos(theta, &sn, &cs);
+        pairs[wave][lane] = make_float2((float)cs, (float)sn);
+    }
+    __builtin_amdgcn_wave_barrier();
+    f32x4 cs[kRCH / 2];
 #pragma unroll
-                for (int e = 0; e < kRCH; ++e) {
-                    x1[e] *= a.scale_log2;
-                    x2[e] *= a.scale_log2;
+    for (int i = 0; i < kRCH / 2; ++i) cs[i] = *reinterpret_cast<const f32x4*>(&pairs[wave][base + 2 * i]);
+    for (int i0 = 0; i0 < hrows; i0 += kU) {
+        if (i0 > 0) load_round(i0);
+#pragma unroll
+        for (int which = 0; which < 2; ++which)
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                const int h = 4 * (i0 + u) + (lane >> 4);
+                u32x4 oth;
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    oth[q] = (uint32_t)__builtin_amdgcn_ds_bpermute(partner * 4, (int)w[which][u][q]);
+                ChunkRaw<BF16, kRCH> r1, r2;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    r1.w[q] = first ? w[which][u][q] : oth[q];
+                    r2.w[q] = first ? oth[q] : w[which][u][q];
                 }
-            }
-            u32x4 w;
+                float x1[kRCH], x2[kRCH];
+                raw_to_f32(r1, x1);
+                raw_to_f32(r2, x2);
+                rope_rotate_cs<kRCH>(x1, x2, cs);
+                if (which == 0) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                w[i] = first ? pack_bf16x2(x1[2 * i], x1[2 * i + 1]) : pack_bf16x2(x2[2 * i], x2[2 * i + 1]);
-            char* out = reinterpret_cast<char*>(which == 0 ? a.qr : a.kr) + row;
-            *reinterpret_cast<u32x4*>(out + c * 16) = w;
-        }
+                    for (int e = 0; e < kRCH; ++e) {
+                        x1[e] *= a.scale_log2;
+                        x2[e] *= a.scale_log2;
+                    }
+                }
+                u32x4 o;
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    o[q] = first ? pack_bf16x2(x1[2 * q], x1[2 * q + 1]) : pack_bf16x2(x2[2 * q], x2[2 * q + 1]);
+                char* out = reinterpret_cast<char*>(which == 0 ? a.qr : a.kr) + row0 + h * kRRow + c * 16;
+                if (i0 + u < hrows && h < a.heads) *reinterpret_cast<u32x4*>(out) = o;
+            }
     }
 }
 
@@ -479,11 +509,9 @@ attn_rot_kernel(AttnParams a) {
 }
 
 hipError_t launch_rope_qk(const RopeQkParams& a, hipStream_t stream) {
-    const size_t lds = (size_t)(a.T + a.H + a.W) * 256;
-    const int64_t tasks = (int64_t)a.B * a.N * a.heads;
-    const int64_t blocks = (tasks + kRopeThreads / 16 - 1) / (kRopeThreads / 16);
-    const int grid = (int)(blocks < kRopeGrid ? blocks : kRopeGrid);
-    hipLaunchKernelGGL(rope_qk_kernel, dim3(grid), dim3(kRopeThreads), lds, stream, a);
+    const int64_t tokens = (int64_t)a.B * a.N;
+    const int64_t blocks = (tokens + kRopeWaves - 1) / kRopeWaves;
+    hipLaunchKernelGGL(rope_qk_kernel, dim3((unsigned)blocks), dim3(64 * kRopeWaves), 0, stream, a);
     return hipGetLastError();
 }
 
