@@ -101,7 +101,8 @@ __device__ __forceinline__ bf16x8 load8(__amdgpu_buffer_rsrc_t r, int off, float
 // each of those 4 rows.  Lanes 0-31 take rows {0-3, 8-11} and lanes 32-63 rows {4-7, 12-15}
 // of every 16-row step (the order in which a 32x32 accumulator holds its rows for the B
 // operand of the next product), columns 32 db + lane % 32.  Row 8 h8 + tr_row, granule
-// 4 db + tr_gran (XOR the row swizzle of V/dO tiles), byte tr_byte.
+// 4 db + tr_gran, byte tr_byte; every tile row sits at BwdLds::kPitch in natural granule
+// order (no swizzle).
 struct TrLane {
     int row, gran, byte;
     __device__ __forceinline__ TrLane(int lane) {
