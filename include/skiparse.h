@@ -80,9 +80,15 @@ enum skiparse_status {
                                      workspace of skiparse_attn_bwd_rotated_static only)    */
 };
 
-/* Largest T + H + W: every kernel keeps a 3D-RoPE cos/sin table with one row per
- * axis position in LDS (the attention kernel: 256 bytes per row, beside its K/V tile
- * buffers).  Larger grids return SKIPARSE_E_UNSUPPORTED. */
+/* Largest T + H + W for the calls whose kernels keep the whole 3D-RoPE cos/sin table,
+ * one row per axis position, in LDS (the fused attention: 256 bytes per row beside its
+ * K/V tile buffers): skiparse_attn, skiparse_attn_lse, skiparse_attn_schedule, both
+ * backward calls, skiparse_quant8, and skiparse_rope_remap / skiparse_rearrange with RoPE
+ * at a dtype or head_dim other than bf16 / 128.  They return SKIPARSE_E_UNSUPPORTED for
+ * larger grids.  skiparse_rope_qk, skiparse_attn_rotated(_lse),
+ * skiparse_attn_schedule_rotated, skiparse_attn8, skiparse_reverse and the bf16 /
+ * head_dim 128 remap evaluate each token's RoPE pairs themselves (or apply none) and take
+ * any grid within the other size limits. */
 #define SKIPARSE_MAX_GRID_SUM 192
 
 /*

@@ -33,6 +33,7 @@ E_WORKSPACE = 7
 # capacity of attn_bwd_rotated_static's workspace: B*heads*N fp32 values
 STATIC_DELTA_MAX = 4194304
 
+# largest T + H + W of the calls that keep the whole RoPE table in LDS (include/skiparse.h)
 MAX_GRID_SUM = 192
 
 _lib = None

@@ -22,9 +22,12 @@ struct Dims {
     int esize = 0;
 };
 
-// Checks shared by every device entry point.  Fills `d` on success.
+// Checks shared by every device entry point.  Fills `d` on success.  `table`: the call runs a
+// kernel that keeps the whole 3D-RoPE table (one LDS row per axis position) in LDS, which bounds
+// T + H + W; the kernels that evaluate a token's RoPE pairs themselves, or apply none, take any
+// grid.
 int check_dims(int B, int T, int H, int W, int heads, int head_dim, int sparse_k,
-               int mode, int dtype, Dims* d) {
+               int mode, int dtype, Dims* d, bool table = true) {
     if (B < 1 || T < 1 || H < 1 || W < 1 || heads < 1 || head_dim < 1 || sparse_k < 1)
         return SKIPARSE_E_SHAPE;
     if (mode != SKIPARSE_SINGLE && mode != SKIPARSE_GROUP) return SKIPARSE_E_UNSUPPORTED;
@@ -42,7 +45,7 @@ int check_dims(int B, int T, int H, int W, int heads, int head_dim, int sparse_k
         const int64_t k2 = (int64_t)sparse_k * sparse_k;
         if (k2 > N || N % k2) return SKIPARSE_E_DIVISIBILITY;
     }
-    if ((int64_t)T + H + W > SKIPARSE_MAX_GRID_SUM) return SKIPARSE_E_UNSUPPORTED;
+    if (table && (int64_t)T + H + W > SKIPARSE_MAX_GRID_SUM) return SKIPARSE_E_UNSUPPORTED;
     d->N = N;
     d->L = N / sparse_k;
     d->esize = dtype == SKIPARSE_BF16 ? 2 : 4;
@@ -76,11 +79,14 @@ int remap_grid(int64_t rows) {
 
 extern "C" {
 
-int skiparse_validate(const void* q, const void* k, const void* v, int B, int T, int H, int W,
-                      int heads, int head_dim, int sparse_k, int mode, int dtype, const void* out) {
+namespace {
+
+// skiparse_validate's checks; `table` as for check_dims
+int validate_attn(const void* q, const void* k, const void* v, int B, int T, int H, int W, int heads,
+                  int head_dim, int sparse_k, int mode, int dtype, const void* out, bool table) {
     if (!q || !k || !v || !out) return SKIPARSE_E_NULL;
     Dims d;
-    const int st = check_dims(B, T, H, W, heads, head_dim, sparse_k, mode, dtype, &d);
+    const int st = check_dims(B, T, H, W, heads, head_dim, sparse_k, mode, dtype, &d, table);
     if (st != SKIPARSE_OK) return st;
     // The attention kernel addresses one batch's (N, heads, head_dim) slab with 32-bit
     // offsets token*row_bytes; tokens of rows past the end of a scope (up to one
@@ -91,6 +97,13 @@ int skiparse_validate(const void* q, const void* k, const void* v, int B, int T,
     if (overlaps(out, q, d.bytes) || overlaps(out, k, d.bytes) || overlaps(out, v, d.bytes))
         return SKIPARSE_E_ALIAS;
     return SKIPARSE_OK;
+}
+
+}  // namespace
+
+int skiparse_validate(const void* q, const void* k, const void* v, int B, int T, int H, int W,
+                      int heads, int head_dim, int sparse_k, int mode, int dtype, const void* out) {
+    return validate_attn(q, k, v, B, T, H, W, heads, head_dim, sparse_k, mode, dtype, out, true);
 }
 
 namespace {
@@ -138,7 +151,7 @@ int skiparse_rope_qk(const void* q, const void* k, int B, int T, int H, int W, i
                      int dtype, void* qr, void* kr, void* stream) {
     if (!q || !k || !qr || !kr) return SKIPARSE_E_NULL;
     Dims d;
-    const int st = check_dims(B, T, H, W, heads, head_dim, 1, SKIPARSE_SINGLE, dtype, &d);
+    const int st = check_dims(B, T, H, W, heads, head_dim, 1, SKIPARSE_SINGLE, dtype, &d, false);
     if (st != SKIPARSE_OK) return st;
     if (head_dim != 128 || dtype != SKIPARSE_BF16) return SKIPARSE_E_UNSUPPORTED;
     if (overlaps(qr, q, d.bytes) || overlaps(qr, k, d.bytes) || overlaps(kr, q, d.bytes) ||
@@ -155,12 +168,12 @@ int skiparse_rope_qk(const void* q, const void* k, int B, int T, int H, int W, i
 static int attn_rotated_impl(const void* qr, const void* kr, const void* v, int B, int T, int H, int W,
                              int heads, int head_dim, int sparse_k, int mode, int dtype, void* out,
                              float* lse, void* stream) {
-    const int st = skiparse_validate(qr, kr, v, B, T, H, W, heads, head_dim, sparse_k, mode, dtype, out);
+    const int st = validate_attn(qr, kr, v, B, T, H, W, heads, head_dim, sparse_k, mode, dtype, out, false);
     if (st != SKIPARSE_OK) return st;
     if (head_dim != 128 || dtype != SKIPARSE_BF16 || skiparse::attn_tile_keys() % sparse_k != 0)
         return SKIPARSE_E_UNSUPPORTED;
     Dims d;
-    check_dims(B, T, H, W, heads, head_dim, sparse_k, mode, dtype, &d);
+    check_dims(B, T, H, W, heads, head_dim, sparse_k, mode, dtype, &d, false);
     if (lse) {
         const int64_t lse_bytes = (int64_t)B * heads * d.N * 4;
         if (ranges_overlap(lse, lse_bytes, qr, d.bytes) || ranges_overlap(lse, lse_bytes, kr, d.bytes) ||
@@ -221,13 +234,14 @@ int skiparse_attn_schedule_rotated(const skiparse_layer* layers, int n_layers, i
     if (n_layers < 1 || n_layers > 4096) return SKIPARSE_E_SHAPE;
     for (int i = 0; i < n_layers; ++i) {
         const skiparse_layer& l = layers[i];
-        const int st = skiparse_validate(l.q, l.k, l.v, B, T, H, W, heads, head_dim, l.sparse_k, l.mode, dtype, l.out);
+        const int st = validate_attn(l.q, l.k, l.v, B, T, H, W, heads, head_dim, l.sparse_k, l.mode, dtype, l.out,
+                                     false);
         if (st != SKIPARSE_OK) return st;
         if (head_dim != 128 || dtype != SKIPARSE_BF16 || skiparse::attn_tile_keys() % l.sparse_k != 0)
             return SKIPARSE_E_UNSUPPORTED;
     }
     Dims d;
-    check_dims(B, T, H, W, heads, head_dim, 1, SKIPARSE_SINGLE, dtype, &d);
+    check_dims(B, T, H, W, heads, head_dim, 1, SKIPARSE_SINGLE, dtype, &d, false);
     // the scratch rows are rewritten by every layer: they may not overlap each other or any
     // layer's buffers
     if (overlaps(qr, kr, d.bytes)) return SKIPARSE_E_ALIAS;
@@ -358,8 +372,8 @@ namespace {
 
 // Checks shared by the 8-bit calls: the attention's size limits, head_dim 128, sparse_k | 64.
 int check_q8(int B, int T, int H, int W, int heads, int head_dim, int sparse_k, int mode, int dtype,
-             Dims* d, int64_t* lp) {
-    const int st = check_dims(B, T, H, W, heads, head_dim, sparse_k, mode, dtype, d);
+             Dims* d, int64_t* lp, bool table) {
+    const int st = check_dims(B, T, H, W, heads, head_dim, sparse_k, mode, dtype, d, table);
     if (st != SKIPARSE_OK) return st;
     if (head_dim != 128 || 64 % sparse_k != 0) return SKIPARSE_E_UNSUPPORTED;
     if ((int64_t)B * heads > 65535) return SKIPARSE_E_UNSUPPORTED;   // grid y of the statistics pass
@@ -379,7 +393,7 @@ int skiparse_quant8(const void* q, const void* k, const void* v, int B, int T, i
     if (!q || !k || !v || !q8 || !q_amax || !k8 || !k_amax || !vt8 || !v_amax) return SKIPARSE_E_NULL;
     Dims d;
     int64_t lp = 0;
-    const int st = check_q8(B, T, H, W, heads, head_dim, sparse_k, mode, dtype, &d, &lp);
+    const int st = check_q8(B, T, H, W, heads, head_dim, sparse_k, mode, dtype, &d, &lp, true);
     if (st != SKIPARSE_OK) return st;
     const int64_t codes = (int64_t)B * d.N * heads * head_dim;
     const int64_t sizes[6] = {codes, (int64_t)B * d.N * heads * 4, codes, (int64_t)B * heads * 4,
@@ -406,7 +420,7 @@ int skiparse_attn8(const void* q8, const float* q_amax, const void* k8, const fl
     if (!q8 || !q_amax || !k8 || !k_amax || !vt8 || !v_amax || !out) return SKIPARSE_E_NULL;
     Dims d;
     int64_t lp = 0;
-    const int st = check_q8(B, T, H, W, heads, head_dim, sparse_k, mode, out_dtype, &d, &lp);
+    const int st = check_q8(B, T, H, W, heads, head_dim, sparse_k, mode, out_dtype, &d, &lp, false);
     if (st != SKIPARSE_OK) return st;
     const int64_t codes = (int64_t)B * d.N * heads * head_dim;
     const int64_t sizes[6] = {codes, (int64_t)B * d.N * heads * 4, codes, (int64_t)B * heads * 4,
@@ -432,7 +446,8 @@ int skiparse_rope_remap(const void* q, const void* k, const void* v, int B, int 
                         void* rk, void* rv, void* stream) {
     if (!q || !k || !v || !rq || !rk || !rv) return SKIPARSE_E_NULL;
     Dims d;
-    const int st = check_dims(B, T, H, W, heads, head_dim, sparse_k, mode, dtype, &d);
+    const bool pairs_per_row = head_dim == 128 && dtype == SKIPARSE_BF16;
+    const int st = check_dims(B, T, H, W, heads, head_dim, sparse_k, mode, dtype, &d, !pairs_per_row);
     if (st != SKIPARSE_OK) return st;
     const void* ins[3] = {q, k, v};
     void* outs[3] = {rq, rk, rv};
@@ -456,7 +471,8 @@ int skiparse_rearrange(const void* x, int B, int T, int H, int W, int heads, int
                        int sparse_k, int mode, int dtype, int apply_rope, void* out, void* stream) {
     if (!x || !out) return SKIPARSE_E_NULL;
     Dims d;
-    const int st = check_dims(B, T, H, W, heads, head_dim, sparse_k, mode, dtype, &d);
+    const bool pairs_per_row = head_dim == 128 && dtype == SKIPARSE_BF16;
+    const int st = check_dims(B, T, H, W, heads, head_dim, sparse_k, mode, dtype, &d, apply_rope && !pairs_per_row);
     if (st != SKIPARSE_OK) return st;
     if (overlaps(out, x, d.bytes)) return SKIPARSE_E_ALIAS;
     skiparse::RemapParams a;
@@ -475,7 +491,7 @@ int skiparse_reverse(const void* x, int B, int T, int H, int W, int heads, int h
                      int sparse_k, int mode, int dtype, void* out, void* stream) {
     if (!x || !out) return SKIPARSE_E_NULL;
     Dims d;
-    const int st = check_dims(B, T, H, W, heads, head_dim, sparse_k, mode, dtype, &d);
+    const int st = check_dims(B, T, H, W, heads, head_dim, sparse_k, mode, dtype, &d, false);
     if (st != SKIPARSE_OK) return st;
     if (overlaps(out, x, d.bytes)) return SKIPARSE_E_ALIAS;
     skiparse::ReverseParams a;

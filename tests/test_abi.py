@@ -295,3 +295,25 @@ def test_rotated_schedule_rejects_before_any_device_call():
     k3 = (sk.Layer * 1)(sk.Layer(Q, K, V, OUT, 3, 0))
     assert L.skiparse_attn_schedule_rotated(k3, 1, 1, 3, 8, 8, 2, 128, 0, QR, KR, None) == sk.E_UNSUPPORTED  # 3 does not divide 64
     assert L.skiparse_attn_schedule_rotated(arr, 0, 1, 4, 8, 8, 2, 128, 0, QR, KR, None) == sk.E_SHAPE
+
+
+def test_grid_limit_applies_only_to_the_table_kernels():
+    # T + H + W = 205 > SKIPARSE_MAX_GRID_SUM.  Every call below also has an output that
+    # overlaps an input: a call that applies the grid limit returns E_UNSUPPORTED first, a call
+    # that takes any grid reaches its alias check and returns E_ALIAS (no device call either way).
+    L = sk.lib()
+    T, H, W = 2, 3, 200
+    assert T + H + W > sk.MAX_GRID_SUM
+    dims = (1, T, H, W, 2, 128)
+    # table kernels: the fused forward (and its validation) and the 8-bit quantisation pass
+    assert L.skiparse_validate(Q, K, V, *dims, 4, 1, 0, Q) == sk.E_UNSUPPORTED
+    assert L.skiparse_attn(Q, K, V, *dims, 4, 1, 0, Q, None) == sk.E_UNSUPPORTED
+    assert L.skiparse_quant8(Q, K, V, *dims, 4, 1, 0, Q, DO, DQ, DK, DV, DELTA, None) == sk.E_UNSUPPORTED
+    # RoPE+remap outside bf16 / head_dim 128 keeps the table
+    assert L.skiparse_rope_remap(Q, K, V, 1, T, H, W, 2, 64, 4, 1, 0, Q, DQ, DK, None) == sk.E_UNSUPPORTED
+    # per-token RoPE pairs or no RoPE: any grid
+    assert L.skiparse_rope_qk(Q, K, *dims, 0, Q, DK, None) == sk.E_ALIAS
+    assert L.skiparse_attn_rotated(Q, K, V, *dims, 4, 1, 0, K, None) == sk.E_ALIAS
+    assert L.skiparse_rope_remap(Q, K, V, *dims, 4, 1, 0, Q, DQ, DK, None) == sk.E_ALIAS
+    assert L.skiparse_rearrange(Q, *dims, 4, 1, 0, 1, Q, None) == sk.E_ALIAS          # bf16, with RoPE
+    assert L.skiparse_reverse(Q, *dims, 4, 1, 0, Q, None) == sk.E_ALIAS

@@ -381,3 +381,31 @@ def test_full_size_rope_remap(mode):
             exact = oracle.rope_3d_at(x[0, toks].double().numpy(), t_all[toks], h_all[toks], w_all[toks])
             got = r[s * w.B, torch.from_numpy(pos).cuda()]
             assert int(_bf16_ulps(got, exact).max()) <= 1, (s, pos)
+
+
+@pytest.mark.parametrize("k,mode", [(4, oracle.GROUP), (2, oracle.SINGLE)], ids=["k4_group", "k2_single"])
+def test_grid_beyond_the_table_limit(k, mode):
+    """T + H + W = 205, above the limit of the calls that keep the whole RoPE table in LDS: the
+    RoPE pass + rotated attention match the oracle, the bf16 RoPE+remap is within one ulp (v
+    bit-exact), the reverse restores v, and the fused forward rejects the grid."""
+    T, H, W, heads, d = 2, 3, 200, 2, 128
+    assert T + H + W > sk.MAX_GRID_SUM
+    print(f"case grid {T}x{H}x{W} k{k} m{mode}", flush=True)
+    q, kk, v = _inputs(1, T, H, W, heads, d, torch.bfloat16, seed=5)
+    qr, kr = sk.rope_qk(q, kk, (T, H, W))
+    out = torch.full_like(q, float("nan"))
+    sk.attn_rotated(qr, kr, v, (T, H, W), k, mode, out=out)
+    rq, rk, rv = sk.rope_remap(q, kk, v, (T, H, W), k, mode)
+    back = sk.reverse(rv, (T, H, W), k, mode)
+    torch.cuda.synchronize()
+    want = oracle.skiparse_attention(_np64(q), _np64(kk), _np64(v), T, H, W, k, mode)
+    _assert_close(_np64(out), want, f"grid {T}x{H}x{W} k{k} m{mode}")
+    eq = oracle.rope_rearrange(_np64(q), T, H, W, k, mode, True)
+    ek = oracle.rope_rearrange(_np64(kk), T, H, W, k, mode, True)
+    assert int(_bf16_ulps(rq, eq).max()) <= 1
+    assert int(_bf16_ulps(rk, ek).max()) <= 1
+    assert np.array_equal(_np64(rv), oracle.rope_rearrange(_np64(v), T, H, W, k, mode, False))
+    assert torch.equal(back.view(torch.int16), v.view(torch.int16))
+    with pytest.raises(sk.SkiparseError) as e:
+        sk.attn(q, kk, v, (T, H, W), k, mode)
+    assert e.value.status == sk.E_UNSUPPORTED
