@@ -186,6 +186,84 @@ __device__ __forceinline__ i16x4 ds_read_tr16(const char* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
 }
 
+// Online softmax of one 64-key tile for the forward kernels (Open-Sora Plan documentation,
+// "Skiparse Attention": softmax attention within each scope, taken tile by tile).  The wave
+// holds S'^T of 64 keys x 32 queries as two 32x32 MFMA accumulators: lane l holds query
+// l % 32 and, of each 32-key block kb, keys 32 kb + 8 g + 4 (l / 32) + jj in slot 4 g + jj.
+// Scores arrive as S' = s log2(e)/sqrt(d) - m_ref, m_ref being the row's reference (the QK
+// products start from s_init = -m_ref).  The weights are P = exp2(S'), rounded to bf16 into pb
+// (k-step 2 kb + g / 2, slots (g % 2) * 4 + jj: the B operand layout of the P V product), and
+// the row sum l_part gathers the unrounded fp32 weights of the lane's 32 keys (the two lane
+// halves are added at the end).  The reference is lazy: it is set on the first tile to the
+// tile's row max, and later moves (by the row max, if positive) only when some lane's 32
+// weights sum to more than 2^8, after which the tile's weights are recomputed.  So every
+// weight entering pb and l_part is at most 2^8, and O and l_part are rescaled only then.
+// On a partial tile (`partial`), keys at or past `valid` are masked to -inf (weight 0).
+template <int DB>
+__device__ __forceinline__ void softmax_tile(f32x16 (&sacc)[2], f32x16 (&o)[DB], bf16x8 (&pb)[4], f32x16& s_init,
+                                             float& m_ref, float& l_part, bool first, bool partial, int valid,
+                                             int hf) {
+    constexpr float kSumLimit = 256.0f;
+    if (partial) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj)
+                    if (kb * 32 + 8 * g + 4 * hf + jj >= valid) sacc[kb][4 * g + jj] = -__builtin_inff();
+    }
+    // row max of the tile relative to the reference: in-lane, then across the lane halves
+    auto tile_max = [&]() __attribute__((always_inline)) {
+        float mt = sacc[0][0];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int x = 0; x < 16; ++x) mt = fmaxf(mt, sacc[kb][x]);
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
+        return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    };
+    auto move_ref = [&](float delta) __attribute__((always_inline)) {
+        const float alpha = __builtin_amdgcn_exp2f(-delta);
+        m_ref += delta;
+        l_part *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int x = 0; x < 16; ++x) o[db][x] *= alpha;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int x = 0; x < 16; ++x) sacc[kb][x] -= delta;
+#pragma unroll
+        for (int x = 0; x < 16; ++x) s_init[x] = -m_ref;
+    };
+    // weights into pb; returns the lane's sum of its 32 unrounded weights (four chains)
+    auto weights = [&]() __attribute__((always_inline)) {
+        float ls[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int kk = 2 * kb + (g >> 1), sl = (g & 1) * 4;
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const float e = __builtin_amdgcn_exp2f(sacc[kb][4 * g + jj]);
+                    pb[kk][sl + jj] = (__bf16)e;
+                    ls[jj] += e;
+                }
+            }
+        return (ls[0] + ls[1]) + (ls[2] + ls[3]);
+    };
+    if (first) move_ref(tile_max());
+    float hs = weights();
+    if (__ballot(hs > kSumLimit) != 0ull) {
+        move_ref(fmaxf(tile_max(), 0.f));
+        hs = weights();
+    }
+    l_part += hs;
+}
+
 // Grid position of a token, tracked across tiles by adding a fixed token delta
 // decomposed as (dt, dh, dw) with carries.
 struct Pos {

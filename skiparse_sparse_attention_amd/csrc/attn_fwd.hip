@@ -61,7 +61,6 @@ constexpr int kWaves = 8;                 // wavefronts per workgroup (2 per SIM
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBM = 32 * kWaves;          // query rows per workgroup (32 per wavefront)
 constexpr int kBN = 64;                   // keys per tile
-constexpr float kRescaleLog2 = 8.0f;
 
 template <int D>
 struct Lds {
@@ -330,7 +329,6 @@ attn_fwd_kernel(AttnParams a) {
 #pragma unroll
     for (int x = 0; x < 16; ++x) s_init[x] = 0.f;
     const int nt = (a.L + kBN - 1) / kBN;
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
     // ---- the four blocks of work per key tile ----
     f32x16 sacc[KB];     // S'^T of the tile being processed
@@ -366,63 +364,10 @@ attn_fwd_kernel(AttnParams a) {
         __builtin_amdgcn_s_setprio(0);
     };
 
-    // online softmax of tile j: weights P = exp2(S'), row sums, lazy reference moves
+    // online softmax of tile j (softmax_tile: weights P = exp2(S'), row sums, lazy reference)
     auto softmax = [&](int j) __attribute__((always_inline)) {
-        if (j == nt - 1 && (a.L % kBN) != 0) {
-            // keys past the end of the scope
-            const int valid = a.L - j * kBN;
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                for (int g = 0; g < 4; ++g)
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj)
-                        if (kb * 32 + 8 * g + 4 * hf + jj >= valid) sacc[kb][4 * g + jj] = -__builtin_inff();
-        }
-        // tile max per query (in-lane, then across the two lane halves), relative to the
-        // reference.  The reference moves on the first tile (to this tile's max) and
-        // afterwards only when a tile exceeds it by more than 2^8.
-        float mt = sacc[0][0];
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-            for (int x = 0; x < 16; ++x) mt = fmaxf(mt, sacc[kb][x]);
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
-        mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-        if (j == 0 || __ballot(mt > kRescaleLog2) != 0ull) {
-            const float delta = j == 0 ? mt : fmaxf(mt, 0.f);
-            const float alpha = __builtin_amdgcn_exp2f(-delta);
-            m_ref += delta;
-            l_part *= alpha;
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int x = 0; x < 16; ++x) o[db][x] *= alpha;
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                for (int x = 0; x < 16; ++x) sacc[kb][x] -= delta;
-#pragma unroll
-            for (int x = 0; x < 16; ++x) s_init[x] = -m_ref;
-        }
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                // keys 32kb + 8g + 4hf + jj sit in k-step 2kb + g/2, slots (g%2)*4 + jj
-                const int kk = 2 * kb + (g >> 1), sl = (g & 1) * 4;
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) pb[kk][sl + jj] = (__bf16)__builtin_amdgcn_exp2f(sacc[kb][4 * g + jj]);
-            }
-        float lsum[2] = {l_part, 0.f};   // two independent chains
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk)
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                const bf16x2 pair = {pb[kk][2 * x], pb[kk][2 * x + 1]};
-                lsum[x & 1] = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, lsum[x & 1], false);
-            }
-        l_part = lsum[0] + lsum[1];
+        softmax_tile<DB>(sacc, o, pb, s_init, m_ref, l_part, j == 0,
+                         j == nt - 1 && (a.L % kBN) != 0, a.L - j * kBN, hf);
     };
 
     // O^T += V^T P^T; the V^T operands come transposed out of the row-major V tile, two

@@ -38,7 +38,6 @@ constexpr int kRBufs = 3;                 // K tiles and V tiles in LDS
 constexpr int kRKOff = 0;
 constexpr int kRVOff = kRBufs * kRTile;
 constexpr int kRLds = 2 * kRBufs * kRTile;
-constexpr float kRRescaleLog2 = 8.0f;
 
 constexpr int kRopeWaves = 4;             // rotation pass: wavefronts (tokens) per workgroup
 
@@ -257,7 +256,6 @@ attn_rot_kernel(AttnParams a) {
 #pragma unroll
     for (int x = 0; x < 16; ++x) s_init[x] = 0.f;
     const int nt = (a.L + kRBN - 1) / kRBN;
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
     f32x16 sacc[KB];
     bf16x8 pb[KK];
 
@@ -293,59 +291,10 @@ attn_rot_kernel(AttnParams a) {
         __builtin_amdgcn_s_setprio(0);
     };
 
-    // online softmax of tile j (the fused kernel's: lazy reference moves beyond 2^8)
+    // online softmax of tile j (softmax_tile, as in the fused kernel)
     auto softmax = [&](int j) __attribute__((always_inline)) {
-        if (j == nt - 1 && (a.L % kRBN) != 0) {
-            const int valid = a.L - j * kRBN;
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                for (int g = 0; g < 4; ++g)
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj)
-                        if (kb * 32 + 8 * g + 4 * hf + jj >= valid) sacc[kb][4 * g + jj] = -__builtin_inff();
-        }
-        float mt = sacc[0][0];
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-            for (int x = 0; x < 16; ++x) mt = fmaxf(mt, sacc[kb][x]);
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
-        mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-        if (j == 0 || __ballot(mt > kRRescaleLog2) != 0ull) {
-            const float delta = j == 0 ? mt : fmaxf(mt, 0.f);
-            const float alpha = __builtin_amdgcn_exp2f(-delta);
-            m_ref += delta;
-            l_part *= alpha;
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int x = 0; x < 16; ++x) o[db][x] *= alpha;
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                for (int x = 0; x < 16; ++x) sacc[kb][x] -= delta;
-#pragma unroll
-            for (int x = 0; x < 16; ++x) s_init[x] = -m_ref;
-        }
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                // keys 32kb + 8g + 4hf + jj sit in k-step 2kb + g/2, slots (g%2)*4 + jj
-                const int kk = 2 * kb + (g >> 1), sl = (g & 1) * 4;
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) pb[kk][sl + jj] = (__bf16)__builtin_amdgcn_exp2f(sacc[kb][4 * g + jj]);
-            }
-        float lsum[2] = {l_part, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk)
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                const bf16x2 pair = {pb[kk][2 * x], pb[kk][2 * x + 1]};
-                lsum[x & 1] = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, lsum[x & 1], false);
-            }
-        l_part = lsum[0] + lsum[1];
+        softmax_tile<DB>(sacc, o, pb, s_init, m_ref, l_part, j == 0,
+                         j == nt - 1 && (a.L % kRBN) != 0, a.L - j * kRBN, hf);
     };
 
     // O^T += V^T P^T, V^T operands by transpose reads through the ring

@@ -2,7 +2,8 @@
 
 A rounding model replays, in float64, the points where the kernels round to bfloat16:
   forward:  q' = bf16(RoPE(q) log2(e)/sqrt(d)), k' = bf16(RoPE(k)); weights P rounded to bf16
-            for the P V product and for the row sum; the output rounded to bf16;
+            for the P V product, the row sum taken over the unrounded weights; the output
+            rounded to bf16;
   backward: the same q', k'; P rounded to bf16 for dV = P^T dO; dZ = P (dP - D) rounded to
             bf16 for dQ = dZ k' and dK = dZ^T q'; D from the bf16 output the forward stored;
             the gradients rounded to the output dtype.
@@ -44,7 +45,7 @@ def _model_forward(q, k, v, T, H, W, sk_, mode, out_bf16):
     z = np.matmul(qs, np.swapaxes(ks, -1, -2))                    # base-2 scores
     p = np.exp2(z - z.max(axis=-1, keepdims=True))
     pb = _bf16(p)
-    o = np.matmul(pb, rv) / pb.sum(axis=-1, keepdims=True)
+    o = np.matmul(pb, rv) / p.sum(axis=-1, keepdims=True)
     if out_bf16:
         o = _bf16(o)
     return oracle.reverse_rows(o.transpose(0, 2, 1, 3), sk_, mode), qs, ks, rv
@@ -82,8 +83,8 @@ def test_forward_bars_at_the_full_size_scope_length():
     vv = sel(v, members)
     exact = oracle.attention(rq, rk, vv)
     z = _bf16(rq * c2) @ _bf16(rk).T
-    pb = _bf16(np.exp2(z - z.max(axis=-1, keepdims=True)))
-    model = _bf16((pb @ vv) / pb.sum(axis=-1, keepdims=True))
+    p = np.exp2(z - z.max(axis=-1, keepdims=True))
+    model = _bf16((_bf16(p) @ vv) / p.sum(axis=-1, keepdims=True))
     mx, mean, rel = _errors(model, exact)
     assert gpu_fwd.MAX_ABS >= 2 * mx and gpu_fwd.MEAN_ABS >= 2 * mean and gpu_fwd.REL_RMS >= 2 * rel, (mx, mean, rel)
 
