@@ -214,6 +214,38 @@ def test_attn_huge_scores_stay_finite_and_convex():
     assert np.abs(out - want).mean() < 0.1
 
 
+def test_rising_scores_move_the_reference_on_every_tile():
+    # T = 1 leaves the t-axis dimensions unrotated (every token has t = 0), so with q and k
+    # zero outside dimension 0 the scores are q0 * k0 exactly: q0 = 1 and k0 = 0.625 n give
+    # scores rising by about 10 (base-2 units) per 64-key tile along each scope.  Every tile's
+    # weights then exceed the lazy reference's budget and move it, and the last tiles' raw
+    # weights at the first tile's reference (up to 2^70) would overflow nothing only because the
+    # reference moved.  Checked against a float64 replay of the kernels' rounding points (the
+    # rounding model of the tolerance tests), and fused == rotated.
+    import test_tolerance_model as tm
+
+    B, T, H, W, heads, d, k, mode = 1, 1, 16, 64, 2, 128, 2, oracle.SINGLE
+    N = T * H * W
+    q = torch.zeros(B, N, heads, d)
+    kk = torch.zeros(B, N, heads, d)
+    q[..., 0] = 1.0
+    kk[..., 0] = 0.625 * torch.arange(N, dtype=torch.float32)[None, :, None]
+    v = torch.randn(B, N, heads, d, generator=torch.Generator().manual_seed(21))
+    q, kk, v = (x.to(torch.bfloat16) for x in (q, kk, v))
+    qd, kd, vd = (x.cuda() for x in (q, kk, v))
+    out = sk.attn(qd, kd, vd, (T, H, W), k, mode)
+    qr, kr = sk.rope_qk(qd, kd, (T, H, W))
+    rot = sk.attn_rotated(qr, kr, vd, (T, H, W), k, mode)
+    torch.cuda.synchronize()
+    assert torch.equal(out, rot)
+    model, _, _, _ = tm._model_forward(_np64(q), _np64(kk), _np64(v), T, H, W, k, mode, True)
+    mx, mean, rel = _errors(_np64(out), model)
+    print(f"rising scores vs rounding replay: max {mx:.3e} mean {mean:.3e} relrms {rel:.3e}", flush=True)
+    # the replay holds every bf16 rounding the kernels make, so the bar is far tighter than the
+    # oracle bars (measured: max 7.6e-6); a reference moved wrongly would miss it by orders
+    assert mx <= 1e-3 and mean <= 1e-4 and rel <= 1e-3
+
+
 def test_attn_uses_original_positions_for_rope():
     # RoPE before the rearrange: matches the oracle, and is far from the variant that
     # rotates by in-scope positions instead.
