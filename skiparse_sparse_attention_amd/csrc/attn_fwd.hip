@@ -18,8 +18,8 @@
 //     operand of v_mfma_f32_32x32x16_bf16;
 //   * K tiles of 64 keys are staged (rotated, bf16, row-major) in LDS and are the A operand,
 //     so the scores come out transposed: S^T = K Q^T.  In the 32x32 accumulator layout a
-//     lane then owns one query column and 16 of its keys per 32-key block, so the row max is
-//     an in-lane reduction plus one swap with the lane 32 away;
+//     lane then owns one query column and 16 of its keys per 32-key block, so row sums and
+//     maxima are in-lane reductions plus one swap with the lane 32 away;
 //   * P^T (bf16) is fed to O^T += V^T P^T straight from the accumulator registers as the B
 //     operand.  The MFMA contracts over whatever key order the operand slots carry; V is
 //     copied row-major into LDS by buffer loads that write LDS directly, and its V^T
@@ -28,12 +28,12 @@
 //     holds them;
 //   * online softmax in fp32 on exp2: the scale log2(e)/sqrt(d) is folded into q before its
 //     bf16 rounding and the QK MFMAs accumulate onto -m_ref, so the scores arrive already
-//     shifted and each weight costs one v_exp_f32.  The row sum is accumulated from the bf16
-//     P pairs with a 2-way dot instruction, so it sums exactly the weights the PV product
-//     uses.  The reference maximum m_ref is set from the first tile and afterwards only
-//     moved when a tile exceeds it by more than 2^8 (the result is identical up to rounding,
-//     since the same reference scales numerator and denominator), which skips almost every
-//     rescale of the O^T accumulator;
+//     shifted and each weight costs one v_exp_f32.  The tile softmax (softmax_tile, shared
+//     with the rotated kernel) sums the unrounded weights in fp32; the reference m_ref is set
+//     from the first tile's row maxima and afterwards moved only when some lane's 32 weights
+//     of a tile sum to more than 2^8 (the result is identical up to rounding, since the same
+//     reference scales numerator and denominator), which skips almost every rescale of the
+//     O^T accumulator and every tile maximum on the common path;
 //   * the two wavefronts of each SIMD belong to different groups (waves 0-3, waves 4-7), and
 //     the groups alternate between an MFMA block (PV of the previous tile, QK of the current
 //     one) and a VALU block (softmax, RoPE staging of the next K tile, load requests), one
