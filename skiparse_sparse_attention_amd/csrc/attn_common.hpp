@@ -255,7 +255,18 @@ __device__ __forceinline__ void softmax_tile(f32x16 (&sacc)[2], f32x16 (&o)[DB],
             }
         return (ls[0] + ls[1]) + (ls[2] + ls[3]);
     };
-    if (first) move_ref(tile_max());
+    if (first) {
+        // O and l_part are still zero: only the reference moves.  (Scaling them by
+        // exp2(-max) would turn 0 into NaN when a row's first-tile scores all lie below -128.)
+        const float mt = tile_max();
+        m_ref += mt;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int x = 0; x < 16; ++x) sacc[kb][x] -= mt;
+#pragma unroll
+        for (int x = 0; x < 16; ++x) s_init[x] = -m_ref;
+    }
     float hs = weights();
     if (__ballot(hs > kSumLimit) != 0ull) {
         move_ref(fmaxf(tile_max(), 0.f));

@@ -293,6 +293,36 @@ def test_uniform_softmax_probe_bit_exact(T, H, W, heads, d, k, mode, dtype):
                        want_t.view(torch.int16 if dtype == torch.bfloat16 else torch.int32))
 
 
+def test_equal_very_negative_scores_give_the_uniform_softmax():
+    # Every score equal and far below zero: T = 1 leaves the t-axis dimensions unrotated, and
+    # with q = e0 and k = -2000 e0 every score is bf16(log2(e)/sqrt(d)) * -2000, about -255 in
+    # base-2 units.  Softmax is then exactly uniform, so the output is the scope mean of v, as
+    # in the q = 0 probe, bit for bit.  (The first tile's reference move must not scale the
+    # still-empty accumulators by exp2(255) = inf.)
+    T, H, W, heads, d, k, mode = 1, 8, 32, 2, 128, 2, oracle.SINGLE    # L = 128: two key tiles
+    N = T * H * W
+    g = torch.Generator().manual_seed(29)
+    v = torch.randint(-4, 5, (1, N, heads, d), generator=g).to(torch.bfloat16)
+    q = torch.zeros(1, N, heads, d)
+    kk = torch.zeros(1, N, heads, d)
+    q[..., 0] = 1.0
+    kk[..., 0] = -2000.0
+    q, kk = q.to(torch.bfloat16), kk.to(torch.bfloat16)
+    qd, kd, vd = q.cuda(), kk.cuda(), v.cuda()
+    fused = sk.attn(qd, kd, vd, (T, H, W), k, mode)
+    qr, kr = sk.rope_qk(qd, kd, (T, H, W))
+    rot = sk.attn_rotated(qr, kr, vd, (T, H, W), k, mode)
+    torch.cuda.synchronize()
+    table = oracle.scope_table(N, k, mode)
+    vn = v.double().numpy()
+    want = np.empty_like(vn)
+    for s in range(k):
+        want[0, table[s]] = vn[0, table[s]].mean(axis=0)
+    want_t = torch.from_numpy(want).to(torch.bfloat16)
+    for got in (fused, rot):
+        assert torch.equal(got.cpu().view(torch.int16), want_t.view(torch.int16))
+
+
 @pytest.mark.parametrize("T,H,W,k,mode", [(1, 1, 8, 8, oracle.SINGLE), (1, 4, 16, 64, oracle.SINGLE),
                                           (1, 1, 64, 8, oracle.GROUP)])
 def test_degenerate_short_scopes(T, H, W, k, mode):
