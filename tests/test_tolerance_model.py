@@ -89,12 +89,9 @@ def test_forward_bars_at_the_full_size_scope_length():
     assert gpu_fwd.MAX_ABS >= 2 * mx and gpu_fwd.MEAN_ABS >= 2 * mean and gpu_fwd.REL_RMS >= 2 * rel, (mx, mean, rel)
 
 
-@pytest.mark.parametrize("B,T,H,W,heads,d,k,mode,dtype", gpu_bwd.CASES)
-def test_backward_bars_leave_headroom_over_the_rounding_model(B, T, H, W, heads, d, k, mode, dtype):
-    out_bf16 = dtype == torch.bfloat16
-    w = wl.Workload("case", B, T, H, W, heads, d, k, mode, "bf16" if out_bf16 else "fp32")
-    q, kk, v = (x.double().numpy() for x in wl.make_inputs(w, seed=0))
-    do = wl.make_output_grad(w, seed=1).double().numpy()
+def _model_backward(q, kk, v, do, T, H, W, k, mode, out_bf16):
+    """(modelled dq, dk, dv) with the kernels' rounding points, and the exact fp64 gradients."""
+    d = q.shape[-1]
     o_b, qs, ks, rv = _model_forward(q, kk, v, T, H, W, k, mode, True)   # the stored bf16 output
     rdo = oracle.rope_rearrange(do, T, H, W, k, mode, False).transpose(0, 2, 1, 3)
     ro = oracle.rope_rearrange(o_b, T, H, W, k, mode, False).transpose(0, 2, 1, 3)
@@ -115,8 +112,33 @@ def test_backward_bars_leave_headroom_over_the_rounding_model(B, T, H, W, heads,
     if out_bf16:
         model = [_bf16(x) for x in model]
     exact = oracle.skiparse_attention_backward(q, kk, v, do, T, H, W, k, mode)
+    return model, exact
+
+
+def _assert_backward_headroom(model, exact, rel_bar, max_bar):
     for name, m, e in zip(("dq", "dk", "dv"), model, exact):
         err = np.abs(m - e)
         rel = float(np.sqrt((err ** 2).sum() / (e ** 2).sum()))
         mrel = float(err.max() / np.abs(e).max())
-        assert gpu_bwd.REL_RMS >= 2 * rel and gpu_bwd.MAX_REL >= 2 * mrel, (name, rel, mrel)
+        assert rel_bar >= 2 * rel and max_bar >= 2 * mrel, (name, rel, mrel)
+
+
+@pytest.mark.parametrize("B,T,H,W,heads,d,k,mode,dtype", gpu_bwd.CASES)
+def test_backward_bars_leave_headroom_over_the_rounding_model(B, T, H, W, heads, d, k, mode, dtype):
+    out_bf16 = dtype == torch.bfloat16
+    w = wl.Workload("case", B, T, H, W, heads, d, k, mode, "bf16" if out_bf16 else "fp32")
+    q, kk, v = (x.double().numpy() for x in wl.make_inputs(w, seed=0))
+    do = wl.make_output_grad(w, seed=1).double().numpy()
+    model, exact = _model_backward(q, kk, v, do, T, H, W, k, mode, out_bf16)
+    _assert_backward_headroom(model, exact, gpu_bwd.REL_RMS, gpu_bwd.MAX_REL)
+
+
+def test_backward_peaked_bars_leave_headroom_over_the_rounding_model():
+    # the GPU test's peaked case (q x PEAKED_SCALE): the same replay on the scaled inputs
+    B, T, H, W, heads, d, k, mode = gpu_bwd.PEAKED_CASE
+    w = wl.Workload("case", B, T, H, W, heads, d, k, mode, "bf16")
+    q, kk, v = (x.double().numpy() for x in wl.make_inputs(w, seed=0))
+    q = _bf16(q * gpu_bwd.PEAKED_SCALE)
+    do = wl.make_output_grad(w, seed=1).double().numpy()
+    model, exact = _model_backward(q, kk, v, do, T, H, W, k, mode, True)
+    _assert_backward_headroom(model, exact, gpu_bwd.PEAKED_REL_RMS, gpu_bwd.PEAKED_MAX_REL)
