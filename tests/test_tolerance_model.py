@@ -11,6 +11,9 @@ Everything else (the float32 accumulations, the exponentials) is taken exact, so
 errors are the part the bf16 operands force.  Each test checks that the bar its GPU test uses
 leaves at least a factor 2 over the modelled error on that test's own inputs: the bars follow
 from the arithmetic, and a kernel that met only a much looser bar would fail.
+  8-bit path, bf16 output: the 8-bit oracle already quantises exactly as the kernel does, so
+            the floor is the rounding of its output to bf16; those bars sit 1.5x (RMS) and
+            2x (max) above it.
 """
 
 import math
@@ -20,8 +23,10 @@ import pytest
 import torch
 
 import oracle
+from oracle import skiparse_oracle8 as o8
 from skiparse_sparse_attention_amd import workloads as wl
 
+import test_gpu_attn8 as gpu_attn8
 import test_gpu_backward as gpu_bwd
 import test_gpu_parity as gpu_fwd
 
@@ -142,3 +147,23 @@ def test_backward_peaked_bars_leave_headroom_over_the_rounding_model():
     do = wl.make_output_grad(w, seed=1).double().numpy()
     model, exact = _model_backward(q, kk, v, do, T, H, W, k, mode, True)
     _assert_backward_headroom(model, exact, gpu_bwd.PEAKED_REL_RMS, gpu_bwd.PEAKED_MAX_REL)
+
+
+@pytest.mark.parametrize("case", [c for c in gpu_attn8.CASES if c[-1] == torch.bfloat16],
+                         ids=lambda c: f"{c[1]}x{c[2]}x{c[3]}_k{c[5]}_m{c[6]}")
+def test_attn8_bf16_bars_sit_above_the_output_rounding(case):
+    # With bf16 output, the 8-bit kernel's error against the 8-bit oracle is the rounding of
+    # its float32 result to bf16 (the float32-output cases show everything else below 4e-5).
+    # That rounding, applied to the oracle's float64 output on the test's own inputs, is the
+    # floor: 1.65e-3 .. 1.67e-3 relative RMS here.  The bars sit 1.5x (RMS) and >= 2x (max)
+    # above it.
+    B, T, H, W, heads, k, mode, dtype, out_dtype = case
+    w = wl.Workload("case", B, T, H, W, heads, 128, k, mode, "bf16" if dtype == torch.bfloat16 else "fp32")
+    q, kk, v = wl.make_inputs(w, seed=0, device="cpu")
+    qn, kn, vn = (x.float().numpy() for x in (q, kk, v))
+    want = o8.skiparse_attention_8bit(o8.quantize_8bit(qn, kn, vn, T, H, W, k, mode), T, H, W, k, mode)
+    floor = torch.from_numpy(want).to(torch.bfloat16).double().numpy()
+    err = np.abs(floor - want)
+    rel = float(np.sqrt((err ** 2).sum() / (want ** 2).sum()))
+    mx = float(err.max() / np.abs(want).max())
+    assert gpu_attn8.REL_RMS[torch.bfloat16] >= 1.4 * rel and gpu_attn8.MAX_REL[torch.bfloat16] >= 2 * mx, (rel, mx)
