@@ -90,6 +90,27 @@ def test_rotated_attention_equals_fused(B, T, H, W, heads, k, mode):
         assert err.max() <= 2e-2 and err.mean() <= 2e-3
 
 
+@pytest.mark.parametrize("T,H,W,k,mode", [
+    (1, 8, 8, 64, oracle.SINGLE),      # L = 1: every token attends only to itself
+    (1, 4, 16, 32, oracle.SINGLE),     # L = 2
+    (1, 1, 64, 8, oracle.GROUP),       # L = 8
+    (2, 4, 8, 8, oracle.GROUP),        # L = 8 over a T x H x W grid with T, H > 1
+])
+def test_short_scopes_equal_fused(T, H, W, k, mode):
+    w = wl.Workload("rot", 1, T, H, W, 2, 128, k, mode, "bf16")
+    q, kk, v = (x.cuda() for x in wl.make_inputs(w, seed=23, device="cpu"))
+    qr, kr = sk.rope_qk(q, kk, (T, H, W))
+    got = sk.attn_rotated(qr, kr, v, (T, H, W), k, mode)
+    ref = sk.attn(q, kk, v, (T, H, W), k, mode)
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref), (got.float() - ref.float()).abs().max().item()
+    if T * H * W == k:
+        assert torch.equal(got.view(torch.int16), v.view(torch.int16))
+    want = oracle.skiparse_attention(*(x.float().cpu().numpy() for x in (q, kk, v)), T, H, W, k, mode)
+    err = np.abs(got.float().cpu().numpy() - want)
+    assert err.max() <= 2e-2 and err.mean() <= 2e-3, (err.max(), err.mean())
+
+
 def test_peaked_scores_equal_fused():
     """q x 8: peaked softmax, the running reference moves between tiles."""
     T, H, W, heads, k, mode = 4, 8, 16, 2, 2, oracle.SINGLE
