@@ -169,6 +169,44 @@ def test_rotated_training_step_equals_fused(B, T, H, W, heads, k, mode):
         assert torch.equal(a, b), (name, (a.float() - b.float()).abs().max().item())
 
 
+@pytest.mark.parametrize("T,H,W,k,mode", [
+    (1, 8, 8, 64, oracle.SINGLE),      # L = 1
+    (1, 4, 16, 32, oracle.SINGLE),     # L = 2
+    (2, 4, 8, 8, oracle.GROUP),        # L = 8
+])
+def test_training_step_on_short_scopes(T, H, W, k, mode):
+    """Scopes of 1, 2 and 8 tokens: the rotated training step equals the fused one bit for
+    bit.  With L = 1 each weight is 1, so dZ = dP - D vanishes up to the rounding of two
+    float32 dot products of 128 terms: dq and dk stay below 1e-3 and dv equals dO within bf16
+    rounding.  Longer scopes against the oracle's chain rule."""
+    w = wl.Workload("rot", 1, T, H, W, 2, 128, k, mode, "bf16")
+    q, kk, v = (x.cuda() for x in wl.make_inputs(w, seed=31, device="cpu"))
+    do = wl.make_output_grad(w, seed=32, device="cuda")
+    qr, kr = sk.rope_qk(q, kk, (T, H, W))
+    out_r, lse_r = sk.attn_rotated_lse(qr, kr, v, (T, H, W), k, mode)
+    out_f, lse_f = sk.attn_lse(q, kk, v, (T, H, W), k, mode)
+    g_r = sk.attn_bwd_rotated(qr, kr, v, out_r, do, lse_r, (T, H, W), k, mode)
+    g_f = sk.attn_bwd(q, kk, v, out_f, do, lse_f, (T, H, W), k, mode)
+    torch.cuda.synchronize()
+    assert torch.equal(out_r, out_f) and torch.equal(lse_r, lse_f)
+    for name, a, b in zip(("dq", "dk", "dv"), g_r, g_f):
+        assert torch.equal(a, b), name
+    if T * H * W == k:
+        dq, dk, dv = (g.double().cpu().numpy() for g in g_r)
+        assert np.abs(dq).max() <= 1e-3 and np.abs(dk).max() <= 1e-3
+        don = do.double().cpu().numpy()
+        assert np.abs(dv - don).max() <= 2.0 ** -8 * np.abs(don).max()
+        return
+    host = [x.double().cpu().numpy() for x in (q, kk, v, do)]
+    want = oracle.skiparse_attention_backward(*host, T, H, W, k, mode)
+    for name, g, r in zip(("dq", "dk", "dv"), g_r, want):
+        got = g.double().cpu().numpy()
+        rel = np.linalg.norm(got - r) / np.linalg.norm(r)
+        mx = np.abs(got - r).max() / np.abs(r).max()
+        print(f"{name} L={T * H * W // k}: relrms {rel:.3e} max/maxref {mx:.3e}", flush=True)
+        assert rel <= 1e-2 and mx <= 2.5e-2, name
+
+
 @pytest.mark.parametrize("T,H,W,heads,k,mode", [
     (3, 8, 12, 2, 3, oracle.SINGLE),    # L = 96: two query tiles
     (3, 12, 18, 2, 3, oracle.GROUP),    # L = 216: four query tiles, the last ragged
