@@ -79,6 +79,9 @@ CASES = [
     (1, 8, 12, 16, 2, 4, oracle.GROUP, torch.bfloat16, torch.float32),      # L = 384
     (1, 4, 10, 16, 2, 8, oracle.SINGLE, torch.bfloat16, torch.bfloat16),    # L = 80
     (1, 4, 16, 16, 1, 8, oracle.GROUP, torch.bfloat16, torch.bfloat16),     # L = 128
+    (1, 1, 8, 8, 2, 64, oracle.SINGLE, torch.bfloat16, torch.bfloat16),     # L = 1 (one padded tile)
+    (1, 1, 4, 16, 2, 32, oracle.SINGLE, torch.bfloat16, torch.float32),     # L = 2
+    (1, 2, 4, 8, 2, 8, oracle.GROUP, torch.bfloat16, torch.bfloat16),       # L = 8, T and H > 1
 ]
 
 
