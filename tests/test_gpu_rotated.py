@@ -39,7 +39,8 @@ def _bf16_round(x64):
     return torch.from_numpy(x64.astype(np.float32)).to(torch.bfloat16).float().numpy().astype(np.float64)
 
 
-@pytest.mark.parametrize("B,T,H,W,heads", [(1, 4, 8, 16, 2), (2, 3, 10, 12, 3), (1, 24, 22, 40, 4)])
+@pytest.mark.parametrize("B,T,H,W,heads", [(1, 4, 8, 16, 2), (2, 3, 10, 12, 3), (1, 24, 22, 40, 4),
+                                           (1, 3, 4, 8, 1), (1, 2, 4, 8, 64)])   # 1 head; 64 heads: 3 rounds of rows
 def test_rope_qk_matches_the_oracle_rotation(B, T, H, W, heads):
     w = wl.Workload("rot", B, T, H, W, heads, 128, 1, oracle.SINGLE, "bf16")
     q, k, _ = wl.make_inputs(w, seed=1, device="cpu")
@@ -109,6 +110,20 @@ def test_short_scopes_equal_fused(T, H, W, k, mode):
     want = oracle.skiparse_attention(*(x.float().cpu().numpy() for x in (q, kk, v)), T, H, W, k, mode)
     err = np.abs(got.float().cpu().numpy() - want)
     assert err.max() <= 2e-2 and err.mean() <= 2e-3, (err.max(), err.mean())
+
+
+def test_group_skip_with_one_scope_is_dense_attention():
+    # k = 1: Single Skip and Group Skip both keep every token in one scope in token order
+    T, H, W, heads = 2, 10, 12, 2
+    w = wl.Workload("rot", 1, T, H, W, heads, 128, 1, oracle.SINGLE, "bf16")
+    q, kk, v = (x.cuda() for x in wl.make_inputs(w, seed=41, device="cpu"))
+    qr, kr = sk.rope_qk(q, kk, (T, H, W))
+    outs = [f(mode) for mode in (oracle.SINGLE, oracle.GROUP)
+            for f in (lambda m: sk.attn(q, kk, v, (T, H, W), 1, m),
+                      lambda m: sk.attn_rotated(qr, kr, v, (T, H, W), 1, m))]
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
 
 
 def test_peaked_scores_equal_fused():
