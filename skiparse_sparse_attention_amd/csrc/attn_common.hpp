@@ -199,7 +199,12 @@ __device__ __forceinline__ i16x4 ds_read_tr16(const char* p) {
 // weights sum to more than 2^8, after which the tile's weights are recomputed.  So every
 // weight entering pb and l_part is at most 2^8, and O and l_part are rescaled only then.
 // On a partial tile (`partial`), keys at or past `valid` are masked to -inf (weight 0).
-template <int DB>
+// kPinInit: s_init is made opaque to the compiler where it is written.  Left alone, the
+// compiler treats s_init as the splat of -m_ref and rebuilds its register copies after every
+// tile (31 moves per tile in the rotated kernel, whose QK products read s_init in place); with
+// the pin the copies are rewritten only when the reference moves (rotated kernel 1.2 % faster,
+// the fused kernel 2.9 % slower with it, so only the rotated kernel sets it).
+template <int DB, bool kPinInit = false>
 __device__ __forceinline__ void softmax_tile(f32x16 (&sacc)[2], f32x16 (&o)[DB], bf16x8 (&pb)[4], f32x16& s_init,
                                              float& m_ref, float& l_part, bool first, bool partial, int valid,
                                              int hf) {
@@ -237,6 +242,7 @@ __device__ __forceinline__ void softmax_tile(f32x16 (&sacc)[2], f32x16 (&o)[DB],
             for (int x = 0; x < 16; ++x) sacc[kb][x] -= delta;
 #pragma unroll
         for (int x = 0; x < 16; ++x) s_init[x] = -m_ref;
+        if constexpr (kPinInit) asm volatile("" : "+v"(s_init));
     };
     // weights into pb; returns the lane's sum of its 32 unrounded weights (four chains)
     auto weights = [&]() __attribute__((always_inline)) {
@@ -266,6 +272,7 @@ __device__ __forceinline__ void softmax_tile(f32x16 (&sacc)[2], f32x16 (&o)[DB],
             for (int x = 0; x < 16; ++x) sacc[kb][x] -= mt;
 #pragma unroll
         for (int x = 0; x < 16; ++x) s_init[x] = -m_ref;
+        if constexpr (kPinInit) asm volatile("" : "+v"(s_init));
     }
     float hs = weights();
     if (__ballot(hs > kSumLimit) != 0ull) {

@@ -293,7 +293,7 @@ attn_rot_kernel(AttnParams a) {
 
     // online softmax of tile j (softmax_tile, as in the fused kernel)
     auto softmax = [&](int j) __attribute__((always_inline)) {
-        softmax_tile<DB>(sacc, o, pb, s_init, m_ref, l_part, j == 0,
+        softmax_tile<DB, true>(sacc, o, pb, s_init, m_ref, l_part, j == 0,
                          j == nt - 1 && (a.L % kRBN) != 0, a.L - j * kRBN, hf);
     };
 
