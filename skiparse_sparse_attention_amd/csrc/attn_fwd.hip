@@ -212,7 +212,6 @@ attn_fwd_kernel(AttnParams a) {
     }
 
     // loop-invariant LDS addresses (the buffer base is added per tile)
-    const int k_rd = l32 * L::kRowPitch + hf * 16;                   // + kb*32 rows + ks*32 bytes
     const int k_wr1 = krow * L::kRowPitch + c1_off;
     const int k_wr2 = krow * L::kRowPitch + c2_off;
     // PV operand reads with ds_read_b64_tr_b16.  Within each group of 16 lanes, lane
@@ -340,8 +339,14 @@ attn_fwd_kernel(AttnParams a) {
     auto qk = [&](int buf) __attribute__((always_inline)) {
         const char* kcur = lds + L::kKOff + buf * L::kKTile;
         constexpr int NST = KS * KB;
+        // The lane's K read offset is recomputed here rather than held across the loop: at 256
+        // VGPRs the compiler otherwise spilled it and reloaded it at the start of every QK
+        // block, behind a wait for all of the wave's outstanding loads (the tile prefetch).
+        int lid = (int)threadIdx.x;
+        asm volatile("" : "+v"(lid));
+        const int k_rd_t = (lid & 31) * L::kRowPitch + ((lid >> 5) & 1) * 16;   // + kb*32 rows + ks*32 bytes
         auto kop = [&](int st) __attribute__((always_inline)) {
-            return *reinterpret_cast<const bf16x8*>(kcur + k_rd + (st % KB) * 32 * L::kRowPitch + (st / KB) * 32);
+            return *reinterpret_cast<const bf16x8*>(kcur + k_rd_t + (st % KB) * 32 * L::kRowPitch + (st / KB) * 32);
         };
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) sacc[kb] = s_init;
