@@ -123,6 +123,35 @@ def test_attn8_peaked_and_large_scores():
         _check_out(_np(out).astype(np.float64), want, torch.float32, f"attn8 q x{qs} k x{ks}")
 
 
+@pytest.mark.parametrize("scale", [1.0, 1.3, 1.7])
+def test_attn8_slowly_rising_scores(scale):
+    """Scores rising by about 0.5 * scale (base 2) per 64-key tile through each scope: q and k
+    are nonzero only on the t axis's rotate-half pairs (T = 1, so RoPE leaves them unchanged),
+    q constant, k growing linearly with the position in the scope.  The kernel's integer
+    reference then moves only on some tiles (when a tile's maximum passes it by more than 0.8)
+    and lags the rising ceiling in between, with weights up to 2^8.8 in E4M3's top binade; the
+    output must still match the 8-bit oracle, whose reference is the row's final ceiling."""
+    T, H, W, heads, k, mode = 1, 16, 64, 2, 2, oracle.SINGLE
+    N = T * H * W
+    L = N // k
+    tdims = list(range(0, 16)) + list(range(64, 80))
+    pos = torch.arange(N) // k                       # position in the scope (Single Skip)
+    q = torch.zeros(1, N, heads, 128)
+    kk = torch.zeros(1, N, heads, 128)
+    q[:, :, :, tdims] = scale
+    kk[:, :, :, tdims] = (0.02 + 0.98 * pos.float() / (L - 1))[None, :, None, None]
+    v = torch.randn(1, N, heads, 128, generator=torch.Generator().manual_seed(7))
+    q, kk, v = (x.to(torch.bfloat16) for x in (q, kk, v))
+    qn, kn, vn = (x.float().numpy() for x in (q, kk, v))
+    want_q = o8.quantize_8bit(qn, kn, vn, T, H, W, k, mode)
+    qz = sk.quant8(q.cuda(), kk.cuda(), v.cuda(), (T, H, W), k, mode)
+    out = sk.attn8(qz, (T, H, W), k, mode, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    _check_operands(qz, want_q, f"operands, rising scores x{scale}")
+    want = o8.skiparse_attention_8bit(want_q, T, H, W, k, mode)
+    _check_out(_np(out).astype(np.float64), want, torch.float32, f"attn8 rising scores x{scale}")
+
+
 def test_attn8_uniform_probe_is_exact():
     """q = 0: every score is 0, every weight exactly 2^8; v in {0, +-4} with each channel's
     amax 4 has exact E4M3 codes (v * 112 = +-448); the output is the scope mean of v over 128
