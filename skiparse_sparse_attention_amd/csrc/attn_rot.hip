@@ -340,6 +340,11 @@ attn_rot_kernel(AttnParams a) {
     // requested in the same phases, after PV(m-2) ended (phases 2m-1, 2m), and has landed
     // before PV(m+1) in phase 2m+5.
     const int grp = wave >= kRWaves / 2 ? 1 : 0;
+    // Wave-uniform: the wave has a query row inside the scope.  A wave of the scope's ragged
+    // last q tile whose 32 rows all lie past its end skips its products and softmax but still
+    // moves its share of every K/V tile and joins every barrier (k = 8 on the 24x22x40 grid:
+    // 5 of the last tile's 8 waves, 2 % of the kernel's time).
+    const bool busy = qt * kRBM + wave * 32 < a.L;
     load_k(0);
     if (nt > 1) load_k(1);
     load_v(0);
@@ -396,41 +401,41 @@ attn_rot_kernel(AttnParams a) {
         const bool lv = m + 1 < nt, lk = m + 2 < nt;
         if (lv) load_v(opaque((m + 1) % 3));
         if (lk) load_k(opaque((m + 2) % 3));
-        if (sm >= 0 && sm < nt) softmax(sm);
+        if (busy && sm >= 0 && sm < nt) softmax(sm);
         if (lk) wait_vm_loads_but<2 * kOps>();   // this block's requests may stay in flight
         else if (lv) wait_vm_loads_but<kOps>();
         else wait_vm_loads();
     };
     // The first and last MFMA blocks (QK(0) alone, PV(nt-1) alone) are peeled off the loops.
     if (grp == 0) {
-        qk(0);
+        if (busy) qk(0);
         __syncthreads();
         valu_block(0, 0);
         __syncthreads();
         for (int m = 1; m < nt; ++m) {
-            mfma_both(opaque((m - 1) % 3), opaque(m % 3));
+            if (busy) mfma_both(opaque((m - 1) % 3), opaque(m % 3));
             __syncthreads();
             valu_block(m, m);
             __syncthreads();
         }
-        pv(opaque((nt - 1) % 3));
+        if (busy) pv(opaque((nt - 1) % 3));
         __syncthreads();
         valu_block(nt, nt);
         __syncthreads();
     } else {
         valu_block(0, -1);
         __syncthreads();
-        qk(0);
+        if (busy) qk(0);
         __syncthreads();
         for (int m = 1; m < nt; ++m) {
             valu_block(m, m - 1);
             __syncthreads();
-            mfma_both(opaque((m - 1) % 3), opaque(m % 3));
+            if (busy) mfma_both(opaque((m - 1) % 3), opaque(m % 3));
             __syncthreads();
         }
         valu_block(nt, nt - 1);
         __syncthreads();
-        pv(opaque((nt - 1) % 3));
+        if (busy) pv(opaque((nt - 1) % 3));
         __syncthreads();
     }
 
