@@ -49,25 +49,29 @@ template <int D>
 __device__ __forceinline__ void build_banked_rope_table(char* tab, int T, int H, int W, int phi_mul) {
     constexpr int kT = D / 8;        // pairs per t position
     constexpr int kHW = 3 * D / 16;  // pairs per h or w position
-    const int nt = T * kT, nh = H * kHW, nw = W * kHW;
-    const int total = nt + nh + nw;
-    for (int e = threadIdx.x; e < total; e += blockDim.x) {
-        int pos, j, da, off;
-        if (e < nt) {
-            pos = e / kT; j = e - pos * kT; da = D / 4;
-            off = pos * 256;
-        } else if (e < nt + nh) {
-            const int r = e - nt; pos = r / kHW; j = r - pos * kHW; da = 3 * D / 8;
-            off = (T + pos) * 256 + RopeBank<D>::kOffH * 16;
-        } else {
-            const int r = e - nt - nh; pos = r / kHW; j = r - pos * kHW; da = 3 * D / 8;
-            off = (T + H + pos) * 256 + (RopeBank<D>::kOffW + rope_phi(pos, phi_mul)) * 16;
-        }
-        const double inv_freq = pow(10000.0, -2.0 * (double)j / (double)da);
+    const int tid = threadIdx.x, nthr = blockDim.x;   // nthr: a multiple of kT
+    auto put = [&](int off, int j, int pos, double inv_freq) __attribute__((always_inline)) {
         const double theta = (double)pos * inv_freq;
         double sn, cs;
         sincos(theta, &sn, &cs);
         *reinterpret_cast<float2*>(tab + off + 8 * j) = make_float2((float)cs, (float)sn);
+    };
+    // Each thread keeps one pair index per axis, so it evaluates the float64 frequency
+    // 10000^(-2j/d_a) once per axis instead of once per table entry (same expressions, same
+    // values).  t axis: pair tid % kT of positions tid / kT, tid / kT + nthr / kT, ...
+    {
+        const int j = tid % kT;
+        const double inv_freq = pow(10000.0, -2.0 * (double)j / (double)(D / 4));
+        for (int pos = tid / kT; pos < T; pos += nthr / kT) put(pos * 256, j, pos, inv_freq);
+    }
+    // h and w axes share their frequencies: pair tid % kHW, for the threads of whole groups of kHW
+    const int groups = nthr / kHW;
+    if (tid < groups * kHW) {
+        const int j = tid % kHW;
+        const double inv_freq = pow(10000.0, -2.0 * (double)j / (double)(3 * D / 8));
+        for (int pos = tid / kHW; pos < H; pos += groups) put((T + pos) * 256 + RopeBank<D>::kOffH * 16, j, pos, inv_freq);
+        for (int pos = tid / kHW; pos < W; pos += groups)
+            put((T + H + pos) * 256 + (RopeBank<D>::kOffW + rope_phi(pos, phi_mul)) * 16, j, pos, inv_freq);
     }
 }
 

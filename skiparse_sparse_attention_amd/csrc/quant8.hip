@@ -22,7 +22,9 @@
 // per-workgroup maxima of |k'| and |v| into k_amax and v_amax with atomic maxima (the bit
 // patterns of non-negative floats order like unsigned integers), and the quantisation pass,
 // one workgroup task per (batch, head, scope, 64 scope positions), which also transposes V
-// through LDS.
+// through LDS.  Both passes issue a lane's loads for several rows (the quantisation pass: all
+// of a task's q, k and v pieces) before using any of them: one row at a time left them
+// latency-bound at about half the HBM rate.
 #include "attn_common.hpp"
 #include "skiparse_device.hpp"
 #include "skiparse_launch.hpp"
@@ -57,21 +59,22 @@ __device__ __forceinline__ uint32_t int8_code(float x, float r) {
     return (uint32_t)(int)fminf(fmaxf(y, -127.f), 127.f) & 0xffu;
 }
 
-// kCH elements of E at byte offset `off` as floats (16-byte loads)
+// The raw chunk pair cp of the head row at `off`: chunk rp.c1 and its rotate-half partner
+// rp.c2 (the loads only, so that a lane can have several rows' loads in flight).
 template <typename E>
-__device__ __forceinline__ void load_chunk(__amdgpu_buffer_rsrc_t r, int off, float (&x)[kCH]) {
-    ChunkRaw<E, kCH> raw;
-    buffer_load_dwords(r, off, raw.w);
-    raw_to_f32(raw, x);
+__device__ __forceinline__ void load_pair(__amdgpu_buffer_rsrc_t r, int off, const RopePair& rp,
+                                          ChunkRaw<E, kCH>& w1, ChunkRaw<E, kCH>& w2) {
+    buffer_load_dwords(r, off + rp.c1 * kCH * E::kBytes, w1.w);
+    buffer_load_dwords(r, off + rp.c2 * kCH * E::kBytes, w2.w);
 }
 
-// The rotated chunk pair cp of the head row at `off` (token n at grid position q): x1 gets
-// chunk rp.c1, x2 its rotate-half partner rp.c2, both turned by RoPE at q.
+// A loaded chunk pair turned by RoPE at grid position q: x1 gets chunk rp.c1, x2 its partner.
 template <typename E>
-__device__ __forceinline__ void rotated_pair(__amdgpu_buffer_rsrc_t r, int off, const RopePair& rp, const char* tab,
-                                             int T, int H, const Pos& q, float (&x1)[kCH], float (&x2)[kCH]) {
-    load_chunk<E>(r, off + rp.c1 * kCH * E::kBytes, x1);
-    load_chunk<E>(r, off + rp.c2 * kCH * E::kBytes, x2);
+__device__ __forceinline__ void rotate_pair(const ChunkRaw<E, kCH>& w1, const ChunkRaw<E, kCH>& w2, const RopePair& rp,
+                                            const char* tab, int T, int H, const Pos& q, float (&x1)[kCH],
+                                            float (&x2)[kCH]) {
+    raw_to_f32(w1, x1);
+    raw_to_f32(w2, x2);
     const int pos = rp.axis == 0 ? q.t : (rp.axis == 1 ? q.h : q.w);
     const float* cs = reinterpret_cast<const float*>(tab + rope_tab_offset<kD>(T, H, rp.axis, pos, rp.jchunk * kCH, 0));
     float c[2 * kCH];
@@ -127,25 +130,48 @@ __global__ void __launch_bounds__(kQ8Threads) q8_stats_kernel(Q8Params a) {
     __syncthreads();
     const int n0 = blockIdx.x * kStatTokens;
     const int n1 = min(n0 + kStatTokens, a.N);
-    // k: row tid / 8 of each 32-row step, chunk pair tid % 8
+    // k: row tid / 8 of each 32-row step, chunk pair tid % 8; kStatK steps' loads are issued
+    // before any of them is used (rows past n1 read as zeros through the buffer range, and
+    // zeros leave the maxima unchanged)
+    constexpr int kStatK = 4, kStatV = 8;
     const RopePair rp = rope_pair(tid & 7);
     float km = 0.f;
-    for (int n = n0 + (tid >> 3); n < n1; n += kQ8Threads / 8) {
-        float x1[kCH], x2[kCH];
-        rotated_pair<E>(kbuf, n * row_bytes, rp, tab, a.T, a.H, grid_pos(n, a.H, a.W), x1, x2);
+    for (int n = n0 + (tid >> 3); n < n1; n += kStatK * (kQ8Threads / 8)) {
+        ChunkRaw<E, kCH> w1[kStatK], w2[kStatK];
 #pragma unroll
-        for (int e = 0; e < kCH; ++e) km = fmaxf(km, fmaxf(fabsf(x1[e]), fabsf(x2[e])));
+        for (int i = 0; i < kStatK; ++i) {
+            const int ni = n + i * (kQ8Threads / 8);
+            load_pair<E>(kbuf, (ni < n1 ? ni : a.N) * row_bytes, rp, w1[i], w2[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < kStatK; ++i) {
+            const int ni = n + i * (kQ8Threads / 8);
+            float x1[kCH], x2[kCH];
+            rotate_pair<E>(w1[i], w2[i], rp, tab, a.T, a.H, grid_pos(min(ni, a.N - 1), a.H, a.W), x1, x2);
+#pragma unroll
+            for (int e = 0; e < kCH; ++e) km = fmaxf(km, fmaxf(fabsf(x1[e]), fabsf(x2[e])));
+        }
     }
-    // v: row tid / 16 of each 16-row step, channels 8 (tid % 16) + [0, 8)
+    // v: row tid / 16 of each 16-row step, channels 8 (tid % 16) + [0, 8), kStatV steps' loads
+    // in flight at a time
     const int vc = tid & 15;
     float vm[kCH];
 #pragma unroll
     for (int e = 0; e < kCH; ++e) vm[e] = 0.f;
-    for (int n = n0 + (tid >> 4); n < n1; n += kQ8Threads / 16) {
-        float x[kCH];
-        load_chunk<E>(vbuf, n * row_bytes + vc * kCH * ES, x);
+    for (int n = n0 + (tid >> 4); n < n1; n += kStatV * (kQ8Threads / 16)) {
+        ChunkRaw<E, kCH> w[kStatV];
 #pragma unroll
-        for (int e = 0; e < kCH; ++e) vm[e] = fmaxf(vm[e], fabsf(x[e]));
+        for (int i = 0; i < kStatV; ++i) {
+            const int ni = n + i * (kQ8Threads / 16);
+            buffer_load_dwords(vbuf, (ni < n1 ? ni : a.N) * row_bytes + vc * kCH * ES, w[i].w);
+        }
+#pragma unroll
+        for (int i = 0; i < kStatV; ++i) {
+            float x[kCH];
+            raw_to_f32(w[i], x);
+#pragma unroll
+            for (int e = 0; e < kCH; ++e) vm[e] = fmaxf(vm[e], fabsf(x[e]));
+        }
     }
     float* wr = red + (tid >> 4) * kD + vc * kCH;
 #pragma unroll
@@ -211,14 +237,33 @@ __global__ void __launch_bounds__(kQ8Threads) q8_quant_kernel(Q8Params a) {
             (void*)(reinterpret_cast<char*>(a.k8) + slice8), (short)0, slice8_bytes, 0x00020000);
         const float k_amax = a.k_amax[bh];
         const float k_r = k_amax > 0.f ? __fdiv_rn(127.f, k_amax) : 0.f;
-        // q and k rows: rows tid / 8 + 32 i of the tile
-        for (int rr = tid >> 3; rr < kQ8Tile; rr += kQ8Threads / 8) {
-            const int p = pt * kQ8Tile + rr;
-            if (p >= L) break;                                   // uniform per group of 8 lanes
-            const int n = (int)scope_token(p, s, a.sparse_k, a.mode);
+        // Every load of the task is issued before any of its data is used: q and k rows
+        // tid / 8 + 32 i of the tile (one chunk pair each), v rows tid / 16 + 16 i (8 channels).
+        // Rows past L read as zeros (token a.N lies past the slice).
+        constexpr int kQK = kQ8Tile / (kQ8Threads / 8), kV = kQ8Tile / (kQ8Threads / 16);
+        int nqk[kQK];
+        ChunkRaw<E, kCH> wq1[kQK], wq2[kQK], wk1[kQK], wk2[kQK], wv[kV];
+#pragma unroll
+        for (int i = 0; i < kQK; ++i) {
+            const int p = pt * kQ8Tile + (tid >> 3) + i * (kQ8Threads / 8);
+            nqk[i] = p < L ? (int)scope_token(p, s, a.sparse_k, a.mode) : a.N;
+            load_pair<E>(qbuf, nqk[i] * row_bytes, rp, wq1[i], wq2[i]);
+            load_pair<E>(kbuf, nqk[i] * row_bytes, rp, wk1[i], wk2[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < kV; ++i) {
+            const int p = pt * kQ8Tile + (tid >> 4) + i * (kQ8Threads / 16);
+            const int n = p < L ? (int)scope_token(p, s, a.sparse_k, a.mode) : a.N;
+            buffer_load_dwords(vbuf, n * row_bytes + vc * kCH * ES, wv[i].w);
+        }
+        // q and k codes
+#pragma unroll
+        for (int i = 0; i < kQK; ++i) {
+            const int n = nqk[i];
+            if (n >= a.N) continue;                              // past L: uniform per group of 8 lanes
             const Pos q = grid_pos(n, a.H, a.W);
             float x1[kCH], x2[kCH];
-            rotated_pair<E>(qbuf, n * row_bytes, rp, tab, a.T, a.H, q, x1, x2);
+            rotate_pair<E>(wq1[i], wq2[i], rp, tab, a.T, a.H, q, x1, x2);
             float qm = 0.f;
 #pragma unroll
             for (int e = 0; e < kCH; ++e) qm = fmaxf(qm, fmaxf(fabsf(x1[e]), fabsf(x2[e])));
@@ -230,21 +275,21 @@ __global__ void __launch_bounds__(kQ8Threads) q8_quant_kernel(Q8Params a) {
             __builtin_amdgcn_raw_buffer_store_b64(pack_codes(x1, q_r), q8buf, o8 + rp.c1 * kCH, 0, 0);
             __builtin_amdgcn_raw_buffer_store_b64(pack_codes(x2, q_r), q8buf, o8 + rp.c2 * kCH, 0, 0);
             if (cp == 0) a.q_amax[((int64_t)b * a.N + n) * a.heads + head] = qm;
-            rotated_pair<E>(kbuf, n * row_bytes, rp, tab, a.T, a.H, q, x1, x2);
+            rotate_pair<E>(wk1[i], wk2[i], rp, tab, a.T, a.H, q, x1, x2);
             __builtin_amdgcn_raw_buffer_store_b64(pack_codes(x1, k_r), k8buf, o8 + rp.c1 * kCH, 0, 0);
             __builtin_amdgcn_raw_buffer_store_b64(pack_codes(x2, k_r), k8buf, o8 + rp.c2 * kCH, 0, 0);
         }
-        // v rows: rows tid / 16 + 16 i of the tile, channels 8 vc + [0, 8); zero past L
+        // v codes: rows tid / 16 + 16 i of the tile, channels 8 vc + [0, 8); zero past L
         {
             const f32x8 vam = *reinterpret_cast<const f32x8*>(a.v_amax + (int64_t)bh * kD + vc * kCH);
             float vr[kCH];
 #pragma unroll
             for (int e = 0; e < kCH; ++e) vr[e] = vam[e] > 0.f ? __fdiv_rn(448.f, vam[e]) : 0.f;
-            for (int rr = tid >> 4; rr < kQ8Tile; rr += kQ8Threads / 16) {
-                const int p = pt * kQ8Tile + rr;
-                const int n = p < L ? (int)scope_token(p, s, a.sparse_k, a.mode) : a.N;   // a.N reads 0
+#pragma unroll
+            for (int i = 0; i < kV; ++i) {
+                const int rr = (tid >> 4) + i * (kQ8Threads / 16);
                 float x[kCH];
-                load_chunk<E>(vbuf, n * row_bytes + vc * kCH * ES, x);
+                raw_to_f32(wv[i], x);
 #pragma unroll
                 for (int e = 0; e < kCH; e += 2) {
                     float y0, y1;
