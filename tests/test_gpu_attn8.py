@@ -177,12 +177,18 @@ def test_attn8_uniform_probe_is_exact():
     assert np.array_equal(got, want), np.abs(got - want).max()
 
 
-@pytest.mark.parametrize("w", [wl.OSP_SINGLE, wl.OSP_GROUP], ids=lambda w: w.name)
+FULL8 = [wl.OSP_SINGLE, wl.OSP_GROUP,
+         wl.OSP_SINGLE.with_mode(oracle.GROUP, sparse_k=2),
+         wl.OSP_SINGLE.with_mode(oracle.SINGLE, sparse_k=8)]
+
+
+@pytest.mark.parametrize("w", FULL8, ids=lambda w: f"{w.T}x{w.H}x{w.W}_h{w.heads}_k{w.sparse_k}_{'group' if w.mode else 'single'}")
 def test_attn8_full_size_sampled(w):
-    """The bench workload (24x22x40, 24 heads, k = 4) in the bench's launch configuration:
-    every operand bit-exact, and output rows of the first and last scope (first, middle and
-    last positions, two heads) against the 8-bit oracle."""
-    print(f"full size {w.name}", flush=True)
+    """The bench workload's grid (24x22x40, 24 heads) at k = 4 in both modes (the bench's
+    launch configuration) and at k = 2 and k = 8: every operand bit-exact, and output rows of
+    every scope against the 8-bit oracle: positions 0, 1, 255, 256, L/2, L-2, L-1 and three
+    drawn per scope from numpy default_rng(0), in heads 0, 12 and 23."""
+    print(f"full size {w.name} k{w.sparse_k} m{w.mode}", flush=True)
     q, kk, v = wl.make_inputs(w, seed=0, device="cpu")
     qz = sk.quant8(q.cuda(), kk.cuda(), v.cuda(), w.grid, w.sparse_k, w.mode)
     out = sk.attn8(qz, w.grid, w.sparse_k, w.mode)
@@ -192,9 +198,10 @@ def test_attn8_full_size_sampled(w):
     want_q = o8.quantize_8bit(qn, kn, vn, T, H, W, w.sparse_k, w.mode)
     _check_operands(qz, want_q, "operands")
     got_all = _np(out.float()).astype(np.float64)
-    positions = [0, 1, 255, 256, w.L // 2, w.L - 2, w.L - 1]
-    heads_idx = [0, w.heads - 1]
-    for s in (0, w.sparse_k - 1):
+    heads_idx = [0, w.heads // 2, w.heads - 1]
+    rng = np.random.default_rng(0)
+    for s in range(w.sparse_k):
+        positions = sorted({0, 1, 255, 256, w.L // 2, w.L - 2, w.L - 1} | set(rng.integers(0, w.L, size=3).tolist()))
         rows, want = o8.skiparse_attention_8bit_rows(want_q, T, H, W, w.sparse_k, w.mode, 0, s, positions, heads_idx)
         got = got_all[0][rows][:, heads_idx]
         _check_out(got, want, torch.bfloat16, f"scope {s}")
