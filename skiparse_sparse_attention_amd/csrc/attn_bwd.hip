@@ -101,8 +101,18 @@ __device__ __forceinline__ bf16x8 load8(__amdgpu_buffer_rsrc_t r, int off, float
 // each of those 4 rows.  Lanes 0-31 take rows {0-3, 8-11} and lanes 32-63 rows {4-7, 12-15}
 // of every 16-row step (the order in which a 32x32 accumulator holds its rows for the B
 // operand of the next product), columns 32 db + lane % 32.  Row 8 h8 + tr_row, granule
-// 4 db + tr_gran, byte tr_byte; every tile row sits at BwdLds::kPitch in natural granule
-// order (no swizzle).
+// 4 db + tr_gran, byte tr_byte; the tiles these reads serve hold their rows at BwdLds::kPitch
+// in natural granule order, each row at the LDS slot tile_slot gives it.
+// LDS slot of row r of a tile that is read both by 16-byte operand reads (one granule of 16
+// consecutive rows per 16 lanes) and by transpose reads (4 consecutive rows x 4 granules per 32
+// lanes), at the padded pitch BwdLds::kPitch (one pad granule per row): inside each block of 16
+// rows, row 4 a + b (a, b < 4) sits at slot 4 b + a.  With the rows in natural order the pad
+// put row r granule g on the banks of row r + 1 granule g - 1, so every transpose read took
+// 4 passes (head_dim 128; 2 at 64); with this order both kinds of read touch 64 distinct banks.
+// The map is its own inverse, keeps blocks of 16 in place and moves rows 0-7 of a block by 8
+// to slots 2 further on, so operand addresses keep constant offsets.
+__device__ __forceinline__ int tile_slot(int r) { return (r & ~15) | ((r & 3) << 2) | ((r >> 2) & 3); }
+
 struct TrLane {
     int row, gran, byte;
     __device__ __forceinline__ TrLane(int lane) {
@@ -355,7 +365,7 @@ attn_bwd_dq_kernel(AttnBwdParams a) {
     };
     auto store_kv = [&](int buf) __attribute__((always_inline)) {
         char* kd = ktile + buf * L::kKTile;
-        char* dst = kd + krow * L::kPitch;
+        char* dst = kd + tile_slot(krow) * L::kPitch;
         if constexpr (ROT) {
             // already rotated: the chunks move unchanged
             *reinterpret_cast<u32x4*>(dst + 2 * cp * CH * 2) = u32x4{kraw[0].w[0], kraw[0].w[1], kraw[0].w[2], kraw[0].w[3]};
@@ -377,7 +387,7 @@ attn_bwd_dq_kernel(AttnBwdParams a) {
         for (int i = 0; i < kVPer; ++i) {
             const int idx = tid + kDqThreads * i;
             const int r = idx / G;
-            *reinterpret_cast<u32x4*>(vd + r * L::kPitch + (idx % G) * 16) =
+            *reinterpret_cast<u32x4*>(vd + tile_slot(r) * L::kPitch + (idx % G) * 16) =
                 u32x4{vraw[i][0], vraw[i][1], vraw[i][2], vraw[i][3]};
         }
     };
@@ -395,7 +405,7 @@ attn_bwd_dq_kernel(AttnBwdParams a) {
 #pragma unroll
         for (int j = 0; j < 3; ++j) {
             const int gi = 64 * (j < 2 ? wave + 8 * j : 16) + lane;
-            const int row = gi / 17, slot = gi % 17;
+            const int row = tile_slot(gi / 17), slot = gi % 17;   // the tile row that LDS row gi / 17 holds
             const RopePair sp = rope_pair((slot >> 1) & 7);
             const int c = slot == 16 ? 0 : ((slot & 1) ? sp.c2 : sp.c1);
             kdo[j] = (int)scope_token(t * kBwdKN + row, s, k_, a.mode) * row_bytes + c * 16;
@@ -403,7 +413,7 @@ attn_bwd_dq_kernel(AttnBwdParams a) {
 #pragma unroll
         for (int j = 0; j < 3; ++j) {
             const int gi = 64 * (j < 2 ? wave + 8 * j : 16) + lane;
-            const int row = gi / 17, slot = gi % 17;
+            const int row = tile_slot(gi / 17), slot = gi % 17;
             vdo[j] = (int)scope_token(t * kBwdKN + row, s, k_, a.mode) * row_bytes + (slot == 16 ? 0 : slot) * 16;
         }
     };
@@ -475,7 +485,7 @@ attn_bwd_dq_kernel(AttnBwdParams a) {
                 dpacc[x] = 0.f;
             }
             {
-                const int r = kb * 32 + l32;
+                const int r = tile_slot(kb * 32 + l32);
                 auto kop = [&](int ks) __attribute__((always_inline)) {
                     return *reinterpret_cast<const bf16x8*>(kc + r * L::kPitch + (2 * ks + hf) * 16);
                 };
@@ -513,8 +523,8 @@ attn_bwd_dq_kernel(AttnBwdParams a) {
             {
                 constexpr int NST = 2 * DB;
                 auto top = [&](int st) __attribute__((always_inline)) {
-                    const char* base = kc + (32 * kb + 16 * (st / DB) + tr.row) * L::kPitch + (4 * (st % DB) + tr.gran) * 16 + tr.byte;
-                    return tr_operand(base, base + 8 * L::kPitch);
+                    const char* base = kc + tile_slot(32 * kb + 16 * (st / DB) + tr.row) * L::kPitch + (4 * (st % DB) + tr.gran) * 16 + tr.byte;
+                    return tr_operand(base, base + 2 * L::kPitch);   // rows 8 further on: slots 2 further on
                 };
                 bf16x8 ta[kR];
 #pragma unroll
@@ -674,7 +684,7 @@ attn_bwd_dkdv_kernel(AttnBwdParams a) {
         }
     };
     auto store_q = [&]() __attribute__((always_inline)) {
-        char* dst = qtile + qrow * L::kPitch;
+        char* dst = qtile + tile_slot(qrow) * L::kPitch;
         {
             float x1[CH], x2[CH];
             raw_to_f32(qraw[0], x1);
@@ -696,7 +706,7 @@ attn_bwd_dkdv_kernel(AttnBwdParams a) {
         for (int j = 0; j < kOPer; ++j) {
             const int idx = tid + kKvThreads * j;
             const int r = idx / G;
-            *reinterpret_cast<u32x4*>(otile + r * L::kPitch + (idx % G) * 16) =
+            *reinterpret_cast<u32x4*>(otile + tile_slot(r) * L::kPitch + (idx % G) * 16) =
                 u32x4{oraw[j][0], oraw[j][1], oraw[j][2], oraw[j][3]};
         }
         if (tid < 2 * kBwdQN) ldt[tid] = ldv;
@@ -741,7 +751,7 @@ attn_bwd_dkdv_kernel(AttnBwdParams a) {
         }
         // S = Q' K'^T and dP = dO V^T of the 32-query block, all four operands from LDS
         {
-            const int r = qb0 + l32;
+            const int r = tile_slot(qb0 + l32);
             auto qop = [&](int ks) __attribute__((always_inline)) {
                 return *reinterpret_cast<const bf16x8*>(qtile + r * L::kPitch + (2 * ks + hf) * 16);
             };
@@ -787,13 +797,13 @@ attn_bwd_dkdv_kernel(AttnBwdParams a) {
             constexpr int NST = 2 * DB;
             auto dop = [&](int st) __attribute__((always_inline)) {
                 const int kk = st / DB, db = st % DB;
-                const char* ob = otile + (qb0 + 16 * kk + tr.row) * L::kPitch + (4 * db + tr.gran) * 16 + tr.byte;
-                return tr_operand(ob, ob + 8 * L::kPitch);
+                const char* ob = otile + tile_slot(qb0 + 16 * kk + tr.row) * L::kPitch + (4 * db + tr.gran) * 16 + tr.byte;
+                return tr_operand(ob, ob + 2 * L::kPitch);
             };
             auto qtop = [&](int st) __attribute__((always_inline)) {
                 const int kk = st / DB, db = st % DB;
-                const char* qb = qtile + (qb0 + 16 * kk + tr.row) * L::kPitch + (4 * db + tr.gran) * 16 + tr.byte;
-                return tr_operand(qb, qb + 8 * L::kPitch);
+                const char* qb = qtile + tile_slot(qb0 + 16 * kk + tr.row) * L::kPitch + (4 * db + tr.gran) * 16 + tr.byte;
+                return tr_operand(qb, qb + 2 * L::kPitch);
             };
             bf16x8 da[kR], ka2[kR];
 #pragma unroll
@@ -953,7 +963,7 @@ attn_bwd_dkdv_rot_kernel(AttnBwdParams a) {
     };
     auto piece_off = [&](int i, int p, bool pair_slot) __attribute__((always_inline)) {
         const int gi = 64 * p + opaque_lane();
-        const int row = gi / 17, slot = gi % 17;
+        const int row = tile_slot(gi / 17), slot = gi % 17;   // the tile row that LDS row gi / 17 holds
         const RopePair sp = rope_pair((slot >> 1) & 7);
         const int c = slot == 16 ? 0 : (pair_slot ? ((slot & 1) ? sp.c2 : sp.c1) : slot);
         return (int)scope_token(i * kBwdQN + row, s, k_, a.mode) * row_bytes + c * 16;
@@ -1057,7 +1067,7 @@ attn_bwd_dkdv_rot_kernel(AttnBwdParams a) {
         }
         // S = Q' K'^T and dP = dO V^T of the 32-query block: A operands from LDS, B in registers
         {
-            const int r = qb0 + l32;
+            const int r = tile_slot(qb0 + l32);
             auto qop = [&](int ks) __attribute__((always_inline)) {
                 return *reinterpret_cast<const bf16x8*>(qtile + r * kPitch + (2 * ks + hf) * 16);
             };
@@ -1116,13 +1126,13 @@ attn_bwd_dkdv_rot_kernel(AttnBwdParams a) {
             constexpr int NST = 2 * DB;
             auto dop = [&](int st) __attribute__((always_inline)) {
                 const int kk = st / DB, db = st % DB;
-                const char* ob = otile + (qb0 + 16 * kk + tr.row) * kPitch + (4 * db + tr.gran) * 16 + tr.byte;
-                return tr_operand(ob, ob + 8 * kPitch);
+                const char* ob = otile + tile_slot(qb0 + 16 * kk + tr.row) * kPitch + (4 * db + tr.gran) * 16 + tr.byte;
+                return tr_operand(ob, ob + 2 * kPitch);
             };
             auto qtop = [&](int st) __attribute__((always_inline)) {
                 const int kk = st / DB, db = st % DB;
-                const char* qb = qtile + (qb0 + 16 * kk + tr.row) * kPitch + (4 * db + tr.gran) * 16 + tr.byte;
-                return tr_operand(qb, qb + 8 * kPitch);
+                const char* qb = qtile + tile_slot(qb0 + 16 * kk + tr.row) * kPitch + (4 * db + tr.gran) * 16 + tr.byte;
+                return tr_operand(qb, qb + 2 * kPitch);
             };
             bf16x8 da[kR], ka2[kR];
 #pragma unroll
