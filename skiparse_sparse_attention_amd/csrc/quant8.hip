@@ -41,7 +41,8 @@ constexpr int kQ8Threads = 256;        // 4 wavefronts
 constexpr int kQ8Tile = 64;            // scope positions per quantisation task
 constexpr int kStatTokens = 512;       // tokens per statistics workgroup
 constexpr int kQ8MaxGrid = 1024;       // quantisation workgroups (each builds the table once)
-constexpr int kVtPitch = kQ8Tile + 16; // bytes per transposed LDS row of the V codes
+constexpr int kVtQuad = 128 * 4 + 16;  // bytes per row quad of the V codes in LDS: a dword
+                                       // (4 rows) per channel, then a pad granule
 
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 
@@ -197,14 +198,19 @@ __global__ void __launch_bounds__(kQ8Threads) q8_stats_kernel(Q8Params a) {
 
 // Quantisation: task (batch, head, scope, tile of 64 scope positions).  q and k: 8 lanes per
 // row, one RoPE chunk pair each (the q row's amax across the 8 lanes), codes stored as two
-// 8-byte pieces straight to the token's row; v: 16 lanes per row, 8 channels each, codes
-// transposed through LDS and written as 64-byte rows of vt8.
+// 8-byte pieces straight to the token's row; v: lane l of a wave holds channels 2 l, 2 l + 1
+// of four consecutive rows (so each load instruction of a wave reads one whole V head row),
+// packs the codes of the four rows of each channel into one dword and writes both dwords
+// into LDS, laid out row quad by row quad ([quad][channel] dwords, the quads 528 bytes
+// apart); the vt8 rows are then gathered from there, four dwords per 16-byte piece.  Both LDS
+// passes touch 64 distinct banks per instruction (the byte-wise transpose this replaced spent
+// most of its LDS cycles in bank conflicts).
 template <typename E>
 __global__ void __launch_bounds__(kQ8Threads) q8_quant_kernel(Q8Params a) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     constexpr int ES = E::kBytes;
     char* tab = lds;
-    unsigned char* vt = reinterpret_cast<unsigned char*>(lds + (a.T + a.H + a.W) * 256);
+    char* vt = lds + (a.T + a.H + a.W) * 256;
     const int tid = threadIdx.x;
     const int row_bytes = a.heads * kD * ES;
     const int row8 = a.heads * kD;                              // bytes per token of q8 / k8
@@ -215,7 +221,7 @@ __global__ void __launch_bounds__(kQ8Threads) q8_quant_kernel(Q8Params a) {
     __syncthreads();
     const int cp = tid & 7;
     const RopePair rp = rope_pair(cp);
-    const int vc = tid & 15;
+    const int vch = 2 * (tid & 63);          // this lane's V channel pair
     for (int task = blockIdx.x; task < tasks; task += gridDim.x) {
         const int pt = task % tiles;
         const int s = (task / tiles) % a.sparse_k;
@@ -238,11 +244,12 @@ __global__ void __launch_bounds__(kQ8Threads) q8_quant_kernel(Q8Params a) {
         const float k_amax = a.k_amax[bh];
         const float k_r = k_amax > 0.f ? __fdiv_rn(127.f, k_amax) : 0.f;
         // Every load of the task is issued before any of its data is used: q and k rows
-        // tid / 8 + 32 i of the tile (one chunk pair each), v rows tid / 16 + 16 i (8 channels).
-        // Rows past L read as zeros (token a.N lies past the slice).
-        constexpr int kQK = kQ8Tile / (kQ8Threads / 8), kV = kQ8Tile / (kQ8Threads / 16);
+        // tid / 8 + 32 i of the tile (one chunk pair each), v rows 4 (tid / 64 + 4 j) + [0, 4)
+        // (channels vch, vch + 1).  Rows past L read as zeros (token a.N lies past the slice).
+        constexpr int kQK = kQ8Tile / (kQ8Threads / 8), kVQ = kQ8Tile / 4 / (kQ8Threads / 64);
         int nqk[kQK];
-        ChunkRaw<E, kCH> wq1[kQK], wq2[kQK], wk1[kQK], wk2[kQK], wv[kV];
+        ChunkRaw<E, kCH> wq1[kQK], wq2[kQK], wk1[kQK], wk2[kQK];
+        uint32_t wv[kVQ][4][ES / 2];
 #pragma unroll
         for (int i = 0; i < kQK; ++i) {
             const int p = pt * kQ8Tile + (tid >> 3) + i * (kQ8Threads / 8);
@@ -251,11 +258,19 @@ __global__ void __launch_bounds__(kQ8Threads) q8_quant_kernel(Q8Params a) {
             load_pair<E>(kbuf, nqk[i] * row_bytes, rp, wk1[i], wk2[i]);
         }
 #pragma unroll
-        for (int i = 0; i < kV; ++i) {
-            const int p = pt * kQ8Tile + (tid >> 4) + i * (kQ8Threads / 16);
-            const int n = p < L ? (int)scope_token(p, s, a.sparse_k, a.mode) : a.N;
-            buffer_load_dwords(vbuf, n * row_bytes + vc * kCH * ES, wv[i].w);
-        }
+        for (int j = 0; j < kVQ; ++j)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int p = pt * kQ8Tile + 4 * ((tid >> 6) + 4 * j) + r4;
+                const int n = p < L ? (int)scope_token(p, s, a.sparse_k, a.mode) : a.N;
+                if constexpr (ES == 2) {
+                    wv[j][r4][0] = __builtin_amdgcn_raw_buffer_load_b32(vbuf, n * row_bytes + vch * ES, 0, 0);
+                } else {
+                    const u32x2 w2 = __builtin_amdgcn_raw_buffer_load_b64(vbuf, n * row_bytes + vch * ES, 0, 0);
+                    wv[j][r4][0] = w2[0];
+                    wv[j][r4][1] = w2[1];
+                }
+            }
         // q and k codes
 #pragma unroll
         for (int i = 0; i < kQK; ++i) {
@@ -279,39 +294,56 @@ __global__ void __launch_bounds__(kQ8Threads) q8_quant_kernel(Q8Params a) {
             __builtin_amdgcn_raw_buffer_store_b64(pack_codes(x1, k_r), k8buf, o8 + rp.c1 * kCH, 0, 0);
             __builtin_amdgcn_raw_buffer_store_b64(pack_codes(x2, k_r), k8buf, o8 + rp.c2 * kCH, 0, 0);
         }
-        // v codes: rows tid / 16 + 16 i of the tile, channels 8 vc + [0, 8); zero past L
+        // v codes: channels vch, vch + 1 of the row quads tid / 64 + 4 j; zero past L.  Byte r
+        // of a channel's dword is row 4 q + r of the quad q (the order of the vt8 row).
         {
-            const f32x8 vam = *reinterpret_cast<const f32x8*>(a.v_amax + (int64_t)bh * kD + vc * kCH);
-            float vr[kCH];
+            float vr[2];
 #pragma unroll
-            for (int e = 0; e < kCH; ++e) vr[e] = vam[e] > 0.f ? __fdiv_rn(448.f, vam[e]) : 0.f;
+            for (int e = 0; e < 2; ++e) {
+                const float am = a.v_amax[(int64_t)bh * kD + vch + e];
+                vr[e] = am > 0.f ? __fdiv_rn(448.f, am) : 0.f;
+            }
 #pragma unroll
-            for (int i = 0; i < kV; ++i) {
-                const int rr = (tid >> 4) + i * (kQ8Threads / 16);
-                float x[kCH];
-                raw_to_f32(wv[i], x);
+            for (int j = 0; j < kVQ; ++j) {
+                float y[4][2];
 #pragma unroll
-                for (int e = 0; e < kCH; e += 2) {
-                    float y0, y1;
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    float x0, x1;
+                    if constexpr (ES == 2) {
+                        x0 = __uint_as_float(wv[j][r4][0] << 16);
+                        x1 = __uint_as_float(wv[j][r4][0] & 0xffff0000u);
+                    } else {
+                        x0 = __uint_as_float(wv[j][r4][0]);
+                        x1 = __uint_as_float(wv[j][r4][1]);
+                    }
                     {
 #pragma clang fp contract(off)
-                        y0 = x[e] * vr[e];
-                        y1 = x[e + 1] * vr[e + 1];
+                        y[r4][0] = x0 * vr[0];
+                        y[r4][1] = x1 * vr[1];
                     }
-                    const unsigned pk = (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
-                    vt[(vc * kCH + e) * kVtPitch + rr] = (unsigned char)(pk & 0xff);
-                    vt[(vc * kCH + e + 1) * kVtPitch + rr] = (unsigned char)((pk >> 8) & 0xff);
                 }
+                u32x2 codes;
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    int w = __builtin_amdgcn_cvt_pk_fp8_f32(y[0][e], y[1][e], 0, false);
+                    w = __builtin_amdgcn_cvt_pk_fp8_f32(y[2][e], y[3][e], w, true);
+                    codes[e] = (uint32_t)w;
+                }
+                *reinterpret_cast<u32x2*>(vt + ((tid >> 6) + 4 * j) * kVtQuad + vch * 4) = codes;
             }
         }
         __syncthreads();
-        // vt8 rows: kD channel rows of 64 bytes, one 16-byte piece per thread step
+        // vt8 rows: kD channel rows of 64 bytes, four 16-byte pieces each (piece g = row quads
+        // 4 g + [0, 4)); four consecutive threads write one row's 64 bytes
         unsigned char* dst = reinterpret_cast<unsigned char*>(a.vt8) + (((int64_t)bh * a.sparse_k + s) * kD) * a.Lp +
                              (int64_t)pt * kQ8Tile;
         for (int i = tid; i < kD * (kQ8Tile / 16); i += kQ8Threads) {
             const int c = i / (kQ8Tile / 16), g = i % (kQ8Tile / 16);
-            *reinterpret_cast<u32x4*>(dst + (int64_t)c * a.Lp + 16 * g) =
-                *reinterpret_cast<const u32x4*>(vt + c * kVtPitch + 16 * g);
+            u32x4 piece;
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq)
+                piece[qq] = *reinterpret_cast<const uint32_t*>(vt + (4 * g + qq) * kVtQuad + 4 * c);
+            *reinterpret_cast<u32x4*>(dst + (int64_t)c * a.Lp + 16 * g) = piece;
         }
         __syncthreads();
     }
@@ -331,7 +363,7 @@ hipError_t launch_q8_t(const Q8Params& a, hipStream_t stream) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int tasks = a.B * a.heads * a.sparse_k * (a.Lp / kQ8Tile);
-    const size_t lds_q = tab + (size_t)kD * kVtPitch;
+    const size_t lds_q = tab + (size_t)(kQ8Tile / 4) * kVtQuad;
     hipLaunchKernelGGL((q8_quant_kernel<E>), dim3(tasks < kQ8MaxGrid ? tasks : kQ8MaxGrid), dim3(kQ8Threads),
                        lds_q, stream, a);
     return hipGetLastError();
