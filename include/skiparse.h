@@ -81,15 +81,16 @@ enum skiparse_status {
 };
 
 /* Largest T + H + W for the calls whose kernels keep the whole 3D-RoPE cos/sin table,
- * one row per axis position, in LDS (the fused attention: 256 bytes per row beside its
- * K/V tile buffers): skiparse_attn, skiparse_attn_lse, skiparse_attn_schedule, both
+ * one row per axis position, in LDS (256 bytes per row beside each kernel's tile buffers;
+ * at 224 rows the rotated dk/dv kernel, the largest, fills 163,328 of its 163,840 bytes):
+ * skiparse_attn, skiparse_attn_lse, skiparse_attn_schedule, both
  * backward calls, skiparse_quant8, and skiparse_rope_remap / skiparse_rearrange with RoPE
  * at a dtype or head_dim other than bf16 / 128.  They return SKIPARSE_E_UNSUPPORTED for
  * larger grids.  skiparse_rope_qk, skiparse_attn_rotated(_lse),
  * skiparse_attn_schedule_rotated, skiparse_attn8, skiparse_reverse and the bf16 /
  * head_dim 128 remap evaluate each token's RoPE pairs themselves (or apply none) and take
  * any grid within the other size limits. */
-#define SKIPARSE_MAX_GRID_SUM 192
+#define SKIPARSE_MAX_GRID_SUM 224
 
 /*
  * skiparse_attn -- the fused Skiparse attention forward (steps 1-4 above).

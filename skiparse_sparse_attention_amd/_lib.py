@@ -34,7 +34,7 @@ E_WORKSPACE = 7
 STATIC_DELTA_MAX = 4194304
 
 # largest T + H + W of the calls that keep the whole RoPE table in LDS (include/skiparse.h)
-MAX_GRID_SUM = 192
+MAX_GRID_SUM = 224
 
 _lib = None
 

@@ -1192,6 +1192,8 @@ attn_bwd_dkdv_rot_kernel(AttnBwdParams a) {
 template <int D, typename E, bool KDQ, bool KKV, bool ROT>
 static hipError_t launch_bwd_k(const AttnBwdParams& a, hipStream_t stream) {
     typedef BwdLds<D> L;
+    static_assert(L::kDqTab + SKIPARSE_MAX_GRID_SUM * 256 <= kLdsBytes && L::kDkvTab + SKIPARSE_MAX_GRID_SUM * 256 <= kLdsBytes &&
+                  RotKvLds::kTab + SKIPARSE_MAX_GRID_SUM * 256 <= kLdsBytes, "the largest table fits LDS");
     const size_t table = (size_t)(a.T + a.H + a.W) * 256;
     const size_t lds_dq = (size_t)L::kDqTab + table, lds_kv = (size_t)L::kDkvTab + table;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bwd_dq_kernel<D, E, KDQ, ROT>),

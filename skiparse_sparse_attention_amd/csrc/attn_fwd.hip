@@ -511,6 +511,7 @@ attn_fwd_kernel(AttnParams a) {
 template <int D, typename E, bool KDIV, bool LSE>
 static hipError_t launch_attn_k(const AttnParams& a, hipStream_t stream) {
     typedef Lds<D> L;
+    static_assert(L::kTabOff + SKIPARSE_MAX_GRID_SUM * L::kTabRow <= kLdsBytes, "the largest table fits LDS");
     const size_t lds = (size_t)L::kTabOff + (size_t)(a.T + a.H + a.W) * L::kTabRow;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_kernel<D, E, KDIV, LSE>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

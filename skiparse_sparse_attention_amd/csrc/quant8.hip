@@ -358,12 +358,21 @@ hipError_t launch_q8_t(const Q8Params& a, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const size_t lds_stats = tab + (size_t)((kQ8Threads / 16) * kD + kQ8Threads / 64) * 4;
+    const size_t lds_q = tab + (size_t)(kQ8Tile / 4) * kVtQuad;
+    static_assert(SKIPARSE_MAX_GRID_SUM * 256 + ((kQ8Threads / 16) * kD + kQ8Threads / 64) * 4 <= kLdsBytes &&
+                  SKIPARSE_MAX_GRID_SUM * 256 + (kQ8Tile / 4) * kVtQuad <= kLdsBytes, "the largest table fits LDS");
+    // past 64 KiB of dynamic LDS (the largest grids) the kernels need the attribute
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&q8_stats_kernel<E>), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)lds_stats);
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&q8_quant_kernel<E>), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)lds_q);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL((q8_stats_kernel<E>), dim3((a.N + kStatTokens - 1) / kStatTokens, a.B * a.heads),
                        dim3(kQ8Threads), lds_stats, stream, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int tasks = a.B * a.heads * a.sparse_k * (a.Lp / kQ8Tile);
-    const size_t lds_q = tab + (size_t)(kQ8Tile / 4) * kVtQuad;
     hipLaunchKernelGGL((q8_quant_kernel<E>), dim3(tasks < kQ8MaxGrid ? tasks : kQ8MaxGrid), dim3(kQ8Threads),
                        lds_q, stream, a);
     return hipGetLastError();

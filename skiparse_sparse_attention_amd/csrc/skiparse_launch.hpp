@@ -9,6 +9,8 @@
 
 namespace skiparse {
 
+constexpr int kLdsBytes = 160 * 1024;   // LDS of one gfx950 compute unit, the most one workgroup can take
+
 struct RemapParams {
     const void* src[3];
     void* dst[3];

@@ -298,11 +298,11 @@ def test_rotated_schedule_rejects_before_any_device_call():
 
 
 def test_grid_limit_applies_only_to_the_table_kernels():
-    # T + H + W = 205 > SKIPARSE_MAX_GRID_SUM.  Every call below also has an output that
+    # T + H + W = 229 > SKIPARSE_MAX_GRID_SUM.  Every call below also has an output that
     # overlaps an input: a call that applies the grid limit returns E_UNSUPPORTED first, a call
     # that takes any grid reaches its alias check and returns E_ALIAS (no device call either way).
     L = sk.lib()
-    T, H, W = 2, 3, 200
+    T, H, W = 2, 3, 224
     assert T + H + W > sk.MAX_GRID_SUM
     dims = (1, T, H, W, 2, 128)
     # table kernels: the fused forward (and its validation) and the 8-bit quantisation pass

@@ -82,6 +82,7 @@ CASES = [
     (1, 1, 8, 8, 2, 64, oracle.SINGLE, torch.bfloat16, torch.bfloat16),     # L = 1 (one padded tile)
     (1, 1, 4, 16, 2, 32, oracle.SINGLE, torch.bfloat16, torch.float32),     # L = 2
     (1, 2, 4, 8, 2, 8, oracle.GROUP, torch.bfloat16, torch.bfloat16),       # L = 8, T and H > 1
+    (1, 2, 6, 216, 2, 4, oracle.GROUP, torch.bfloat16, torch.bfloat16),     # T + H + W = 224, the table limit
 ]
 
 

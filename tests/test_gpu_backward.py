@@ -81,6 +81,8 @@ CASES = [
     (1, 6, 10, 12, 2, 128, 4, oracle.SINGLE, torch.bfloat16),   # L = 180: several tiles, ragged
     (1, 8, 12, 16, 2, 128, 4, oracle.GROUP, torch.bfloat16),    # L = 384
     (1, 4, 10, 12, 2, 128, 8, oracle.SINGLE, torch.float32),
+    (1, 2, 6, 216, 2, 128, 4, oracle.GROUP, torch.bfloat16),    # T + H + W = 224, the table limit
+    (1, 2, 6, 216, 2, 64, 2, oracle.SINGLE, torch.float32),
 ]
 
 

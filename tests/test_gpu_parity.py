@@ -3,8 +3,10 @@
 Bars:
 * permutation / index work (rearrange, reverse, the value rows of the
   materialised pass): bit-exact;
-* 3D RoPE in the materialised pass: within one bf16 ulp of the fp64 value
-  (bf16), within 2e-6 absolute (fp32, |x| ~ N(0,1));
+* 3D RoPE in the materialised pass: within one bf16 ulp of the fp64 value, or (where
+  the rotation cancels to far below its operands) within 2^-21 of the largest |x| of the
+  row, the size of the float32 evaluation's own error (bf16); within 2e-6 absolute (fp32,
+  |x| ~ N(0,1));
 * attention: max |err| <= 2e-2 and mean |err| <= 2e-3 against the fp64 oracle
   (bf16 operands on the matrix cores, fp32 accumulation and softmax), plus
   an internal gate of relative RMS error <= 1e-2;
@@ -70,6 +72,7 @@ PERM_SHAPES = [
     (2, 4, 10, 12, 3, 128, 4, oracle.GROUP, torch.bfloat16),
     (1, 4, 10, 12, 3, 64, 8, oracle.SINGLE, torch.bfloat16),
     (1, 2, 8, 16, 2, 128, 8, oracle.GROUP, torch.float32),
+    (1, 2, 6, 216, 2, 64, 4, oracle.GROUP, torch.float32),     # T + H + W = 224, the table limit
 ]
 
 
@@ -114,6 +117,18 @@ def _bf16_ulps(got_bf16, exact64):
     return (a - b).abs()
 
 
+def _rope_misses(got_bf16, exact64, x64):
+    """Elements of a bf16 RoPE result neither within one bf16 ulp of the fp64 rotation nor
+    within 2^-21 of the row's largest operand |x|.  The kernels rotate in float32 with float32
+    (cos, sin): each of the two products and the sum rounds at 2^-24 of the operands' size, so
+    where x1 cos - x2 sin cancels to far below |x| (e.g. 4e-8 from O(1) operands) that error
+    spans many bf16 ulps of the tiny result while staying at the float32 scale."""
+    ulps = _bf16_ulps(got_bf16, exact64).numpy()
+    err = np.abs(got_bf16.detach().cpu().double().numpy() - exact64)
+    slack = 2.0 ** -21 * np.abs(x64).max(axis=-1, keepdims=True)
+    return int(((ulps > 1) & (err > slack)).sum())
+
+
 @pytest.mark.parametrize("B,T,H,W,heads,d,k,mode,dtype", PERM_SHAPES)
 def test_rope_remap_matches_oracle(B, T, H, W, heads, d, k, mode, dtype):
     q, kk, v = _inputs(B, T, H, W, heads, d, dtype, seed=3)
@@ -124,8 +139,8 @@ def test_rope_remap_matches_oracle(B, T, H, W, heads, d, k, mode, dtype):
     ek = oracle.rope_rearrange(_np64(kk), T, H, W, k, mode, True)
     ev = oracle.rope_rearrange(_np64(v), T, H, W, k, mode, False)
     if dtype == torch.bfloat16:
-        assert int(_bf16_ulps(rq, eq).max()) <= 1
-        assert int(_bf16_ulps(rk, ek).max()) <= 1
+        assert _rope_misses(rq, eq, oracle.rope_rearrange(_np64(q), T, H, W, k, mode, False)) == 0
+        assert _rope_misses(rk, ek, oracle.rope_rearrange(_np64(kk), T, H, W, k, mode, False)) == 0
     else:
         assert np.abs(_np64(rq) - eq).max() <= 2e-6
         assert np.abs(_np64(rk) - ek).max() <= 2e-6
@@ -160,6 +175,8 @@ SMALL = [
     (1, 3, 5, 7, 2, 128, 3, oracle.SINGLE, torch.bfloat16),   # k does not divide the key tile
     (1, 3, 6, 6, 2, 128, 3, oracle.GROUP, torch.bfloat16),
     (1, 9, 10, 12, 2, 128, 1, oracle.SINGLE, torch.bfloat16),  # L = 1080: 5 q tiles, 34 key tiles
+    (1, 2, 6, 216, 2, 128, 4, oracle.GROUP, torch.bfloat16),   # T + H + W = 224, the table limit
+    (1, 2, 6, 216, 2, 64, 2, oracle.SINGLE, torch.float32),
 ]
 
 
@@ -424,7 +441,7 @@ def test_full_size_config_sampled_rows(w):
 def test_full_size_rope_remap(mode):
     """The materialised RoPE + rearrange at the 24x22x40 / 24-head / k = 4 size the bench
     times: v moves bit-exactly (whole tensor), q and k are within one bf16 ulp of the fp64
-    RoPE on a row sample of every scope (positions 0, 1, L/2, L-1 and four drawn from
+    RoPE (or its float32 evaluation error, _rope_misses) on a row sample of every scope (positions 0, 1, L/2, L-1 and four drawn from
     numpy default_rng(1))."""
     w = wl.OSP_SINGLE.with_mode(mode)
     q, k, v = wl.make_inputs(w, seed=0, device="cpu")
@@ -442,15 +459,16 @@ def test_full_size_rope_remap(mode):
         for x, r in ((q, rq), (k, rk)):
             exact = oracle.rope_3d_at(x[0, toks].double().numpy(), t_all[toks], h_all[toks], w_all[toks])
             got = r[s * w.B, torch.from_numpy(pos).cuda()]
-            assert int(_bf16_ulps(got, exact).max()) <= 1, (s, pos)
+            assert _rope_misses(got, exact, x[0, toks].double().numpy()) == 0, (s, pos)
 
 
 @pytest.mark.parametrize("k,mode", [(4, oracle.GROUP), (2, oracle.SINGLE)], ids=["k4_group", "k2_single"])
 def test_grid_beyond_the_table_limit(k, mode):
-    """T + H + W = 205, above the limit of the calls that keep the whole RoPE table in LDS: the
-    RoPE pass + rotated attention match the oracle, the bf16 RoPE+remap is within one ulp (v
-    bit-exact), the reverse restores v, and the fused forward rejects the grid."""
-    T, H, W, heads, d = 2, 3, 200, 2, 128
+    """T + H + W = 229, above the limit of the calls that keep the whole RoPE table in LDS: the
+    RoPE pass + rotated attention match the oracle, the bf16 RoPE+remap is within one ulp or the
+    float32 evaluation error (v bit-exact), the reverse restores v, and the fused forward
+    rejects the grid."""
+    T, H, W, heads, d = 2, 3, 224, 2, 128
     assert T + H + W > sk.MAX_GRID_SUM
     print(f"case grid {T}x{H}x{W} k{k} m{mode}", flush=True)
     q, kk, v = _inputs(1, T, H, W, heads, d, torch.bfloat16, seed=5)
@@ -464,8 +482,8 @@ def test_grid_beyond_the_table_limit(k, mode):
     _assert_close(_np64(out), want, f"grid {T}x{H}x{W} k{k} m{mode}")
     eq = oracle.rope_rearrange(_np64(q), T, H, W, k, mode, True)
     ek = oracle.rope_rearrange(_np64(kk), T, H, W, k, mode, True)
-    assert int(_bf16_ulps(rq, eq).max()) <= 1
-    assert int(_bf16_ulps(rk, ek).max()) <= 1
+    assert _rope_misses(rq, eq, oracle.rope_rearrange(_np64(q), T, H, W, k, mode, False)) == 0
+    assert _rope_misses(rk, ek, oracle.rope_rearrange(_np64(kk), T, H, W, k, mode, False)) == 0
     assert np.array_equal(_np64(rv), oracle.rope_rearrange(_np64(v), T, H, W, k, mode, False))
     assert torch.equal(back.view(torch.int16), v.view(torch.int16))
     with pytest.raises(sk.SkiparseError) as e:

@@ -162,6 +162,7 @@ BWD_CASES = [
     (1, 4, 10, 16, 2, 8, oracle.SINGLE),     # L = 80
     (1, 4, 16, 16, 1, 8, oracle.GROUP),      # L = 128
     (2, 4, 8, 16, 3, 16, oracle.GROUP),      # k = 16, B = 2, L = 32
+    (1, 2, 6, 216, 2, 4, oracle.GROUP),      # T + H + W = 224, the table limit
 ]
 
 
